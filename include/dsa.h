@@ -1,0 +1,141 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD MI355X (gfx950).
+ *
+ * The path has three stages and one reuse scheme ("LLM architecture survey" page,
+ * section 2.2 DeepSeek-V3.2, and section 7.2 GLM-5.2 with Fig. 7-2):
+ *   1. lightning indexer: a score for every preceding token, s_t = sum_h w_h * ReLU(q_h . k_t),
+ *      Hi heads of dim 128 in FP8                                   -> dsa_index_score
+ *   2. token selector: the k (= 2048) highest-scoring tokens per query -> dsa_topk
+ *   3. MLA in MQA mode over only the selected latent rows (512 latent + 64 RoPE dims)
+ *                                                                     -> dsa_sparse_mla_fwd
+ *   4. IndexShare: one index set serves a group of consecutive layers, or all draft
+ *      positions of a speculative step ("GLM-5.2 inference deployment" page, MTP
+ *      draft + verify: indices computed at draft step 1 only)      -> dsa_forward_shared
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked (host). Every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL is the default stream) and launches no host sync.
+ *   - The caller owns every buffer. The library never allocates, frees, or keeps a pointer
+ *     after the call returns; scratch memory comes from the caller-provided workspace, sized
+ *     by dsa_workspace_size().
+ *   - Arguments are validated on the host before anything is launched; a failed check
+ *     returns a status and launches nothing. Device-side contents (seq_lens, q_pos, block
+ *     tables, indices) are trusted, not checked: 1 <= seq_lens[b] <= L_max,
+ *     0 <= q_pos < seq_lens[b], page ids inside the pool for every page below seq_lens[b].
+ *   - Results are bitwise reproducible run to run (fixed reduction orders, no float
+ *     atomics). The library holds no global mutable state and is thread-safe; calls that
+ *     share a workspace must not overlap in time.
+ *   - Dtypes: "e4m3" = OCP FP8 E4M3FN codes in uint8 (torch.float8_e4m3fn); "bf16" =
+ *     bfloat16 bits in uint16 (torch.bfloat16); float = IEEE binary32.
+ *   - Fixed dims: indexer head dim 128; latent row 576 (512 latent + 64 RoPE) bf16; value
+ *     = the first 512 dims of the row.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or stride            */
+  DSA_ERR_UNSUPPORTED = 2,  /* a shape outside what the kernels are built for          */
+  DSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than dsa_workspace_size()  */
+  DSA_ERR_HIP = 4           /* a HIP launch error; text in dsa_last_error()            */
+} dsa_status;
+
+/* A token-major cache of one kind of row (indexer keys: 128 e4m3 bytes per token;
+ * latent rows: 576 bf16 per token).
+ *   contiguous (block_table == NULL): base is [B][L_max][D]; token t of sequence b is row b*L_max + t.
+ *   paged: base is a pool [n_pages][page_size][D]; token t of sequence b is at
+ *          page block_table[b*max_pages + t/page_size], row t % page_size.
+ * The KV page / slot unit follows the GLM-5.2 inference page (HiSparse section: slot = KV page). */
+typedef struct {
+  const void* base;            /* device, 16-byte aligned                                   */
+  const int32_t* block_table;  /* device [B][max_pages] physical page ids, or NULL            */
+  int32_t max_pages;           /* row stride of block_table (>= ceil(L_max / page_size))      */
+  int32_t page_size;           /* tokens per page, a positive multiple of 16 (paged only)     */
+} dsa_cache_t;
+
+/* A batch of B sequences with Q query tokens each. Query token j of sequence b sits at
+ * position q_pos[b*Q + j], or at seq_lens[b] - Q + j when q_pos is NULL (the Q newest
+ * cache entries). Causality is inclusive: the query at position p sees tokens 0..p. */
+typedef struct {
+  int32_t B, Q, L_max;         /* (host) sizes; L_max is the row stride of scores and caches  */
+  const int32_t* seq_lens;     /* device [B]                                                  */
+  const int32_t* q_pos;        /* device [B][Q] or NULL                                       */
+} dsa_batch_t;
+
+/* Lightning indexer ("LLM architecture survey", section 2.2: 64 heads x 128, FP8, a scalar
+ * relevance score for every preceding token; section 7.2: GLM-5.2 uses 32 heads).
+ *   q       [B][Q][Hi][128] e4m3      w [B][Q][Hi] float (per query token, per head)
+ *   keys    cache of 128-byte e4m3 rows
+ *   scores  [B][Q][L_max] float, written in full: s_t for t <= p, -inf for t > p.
+ * Hi must be 32 or 64. The dot products run on FP8 matrix cores with fp32 accumulation;
+ * the head sum is fp32. Needs no workspace. */
+dsa_status dsa_index_score(const dsa_batch_t* batch, const uint8_t* q, const float* w, int Hi,
+                           const dsa_cache_t* keys, float* scores, void* stream);
+
+/* Token selector ("LLM architecture survey", section 2.2: each query keeps the k = 2048
+ * highest-scoring history tokens).
+ *   scores  [B][Q][L_max] float; only entries 0..p of each row are read.
+ *   idx     [B][Q][k] int32: the positions of the min(k, p+1) highest scores, ascending,
+ *           then -1 up to k. Equal scores go to the lower position; -0 equals +0; NaN is
+ *           not allowed in scores 0..p.
+ * 1 <= k <= 2048. ws: dsa_workspace_size(DSA_OP_TOPK, ...) bytes, 256-byte aligned. */
+dsa_status dsa_topk(const dsa_batch_t* batch, const float* scores, int k, int32_t* idx,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse MLA in MQA mode ("LLM architecture survey", section 2.1: the latent row is kv rank
+ * 512 plus a 64-dim RoPE part; section 2.2: DSA runs on MLA's MQA mode and only the selected
+ * tokens take the full attention path).
+ * For query token (b, j) and head h over the selected rows c_i (entries -1 are skipped):
+ *   z_i = softmax_scale * (q_h . c_i) over all 576 dims, o_h = sum_i softmax(z)_i c_i[0:512],
+ *   lse_h = log(sum_i exp z_i) (natural log).
+ *   q       [B][Q][H][576] bf16          latent  cache of 576-bf16 rows
+ *   idx     row (b, j) at idx + b*(idx_q_stride ? Q*k : k) + j*idx_q_stride; idx_q_stride is
+ *           k (one set per query token) or 0 (one set per sequence, shared by its Q tokens)
+ *   out     [B][Q][H][512] float         lse [B][Q][H] float, or NULL
+ * A query whose set has no valid entry gets out = 0 and lse = -inf.
+ * H must be 64 or 128; 1 <= k <= 2048. QK and PV run on bf16 matrix cores with fp32
+ * accumulation; softmax weights are rounded to bf16 for PV.
+ * ws: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes (split partials), 256-byte aligned. */
+dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H,
+                              const dsa_cache_t* latent, const int32_t* idx, int k, int idx_q_stride,
+                              float softmax_scale, float* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* IndexShare group ("LLM architecture survey", section 7.2 and Fig. 7-2: every 4 sparse
+ * layers share one indexer whose top-k indices the following layers reuse; "GLM-5.2
+ * inference deployment", MTP draft + verify: draft steps reuse the step-1 indices).
+ * Runs dsa_index_score + dsa_topk once, then dsa_sparse_mla_fwd for each of n_layers layers
+ * with that layer's query and latent cache and the same indices.
+ *   share_first_query = 0: one index set per query token, idx_out [B][Q][k];
+ *   share_first_query = 1: the set of query token 0 of each sequence serves all its Q
+ *                          tokens, idx_out [B][1][k] (scores computed for token 0 only).
+ *   q_bf16, latents, out, lse: (host) arrays of n_layers device pointers / caches; lse may be
+ *   NULL or hold NULL entries. Shapes per layer as in dsa_sparse_mla_fwd.
+ * ws: dsa_workspace_size(DSA_OP_FORWARD_SHARED, ...) bytes; it holds the scores, so the
+ * scores are not returned. */
+dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                              const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                              const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                              float softmax_scale, float* const* out, float* const* lse,
+                              int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace sizes, from host fields of `batch` only (B, Q, L_max). */
+enum { DSA_OP_INDEX_SCORE = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD_SHARED = 3 };
+size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int Hi, int H, int k, int n_layers);
+
+const char* dsa_status_str(dsa_status s);
+/* Thread-local text of the last failure on this thread; valid until the next call. */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

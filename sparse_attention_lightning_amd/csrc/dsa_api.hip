@@ -1,0 +1,229 @@
+// C ABI of the DSA hot path: host-side validation, workspace sizing and launch order.
+// Every check runs before any HIP call, so a rejected call touches neither the GPU nor
+// the HIP runtime (this is what the CPU-only tests exercise).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kMaxTopK = 2048;
+
+dsa_status check_batch(const dsa_batch_t* bt, const char* who) {
+  if (!bt) return fail(DSA_ERR_INVALID_ARG, "%s: batch is NULL", who);
+  if (bt->B < 1 || bt->Q < 1 || bt->L_max < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: B=%d Q=%d L_max=%d must be >= 1", who, bt->B, bt->Q, bt->L_max);
+  if (bt->Q > bt->L_max) return fail(DSA_ERR_INVALID_ARG, "%s: Q=%d exceeds L_max=%d", who, bt->Q, bt->L_max);
+  if (!bt->seq_lens || !aligned(bt->seq_lens, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: seq_lens is NULL or misaligned", who);
+  if (bt->q_pos && !aligned(bt->q_pos, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: q_pos misaligned", who);
+  if ((int64_t)bt->B * bt->Q > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*Q=%lld too large", who, (long long)bt->B * bt->Q);
+  if (bt->L_max > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "%s: L_max=%d above 16M tokens", who, bt->L_max);
+  return DSA_OK;
+}
+
+dsa_status check_cache(const dsa_cache_t* c, int L_max, const char* who, const char* name) {
+  if (!c) return fail(DSA_ERR_INVALID_ARG, "%s: %s cache is NULL", who, name);
+  if (!c->base || !aligned(c->base, 16)) return fail(DSA_ERR_INVALID_ARG, "%s: %s base is NULL or not 16-byte aligned", who, name);
+  if (c->block_table) {
+    if (!aligned(c->block_table, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: %s block_table misaligned", who, name);
+    if (c->page_size < 16 || c->page_size % 16)
+      return fail(DSA_ERR_UNSUPPORTED, "%s: %s page_size=%d must be a positive multiple of 16", who, name, c->page_size);
+    const int64_t need = ((int64_t)L_max + c->page_size - 1) / c->page_size;
+    if (c->max_pages < need)
+      return fail(DSA_ERR_INVALID_ARG, "%s: %s max_pages=%d < ceil(L_max/page_size)=%lld", who, name, c->max_pages, (long long)need);
+  }
+  return DSA_OK;
+}
+
+dsa_status check_ptr(const void* p, size_t a, const char* who, const char* name) {
+  if (!p || !aligned(p, a)) return fail(DSA_ERR_INVALID_ARG, "%s: %s is NULL or not %zu-byte aligned", who, name, a);
+  return DSA_OK;
+}
+
+dsa_status check_ws(void* ws, size_t have, size_t need, const char* who) {
+  if (need == 0) return DSA_OK;
+  if (!ws || !aligned(ws, 256)) return fail(DSA_ERR_WORKSPACE, "%s: workspace is NULL or not 256-byte aligned", who);
+  if (have < need) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", who, have, need);
+  return DSA_OK;
+}
+
+dsa::HostBatch host_batch(const dsa_batch_t* bt) {
+  return dsa::HostBatch{bt->B, bt->Q, bt->L_max, bt->seq_lens, bt->q_pos, bt->Q};
+}
+dsa::HostCache host_cache(const dsa_cache_t* c) {
+  return dsa::HostCache{c->base, c->block_table, c->block_table ? c->max_pages : 0,
+                        c->block_table ? c->page_size : 0};
+}
+
+dsa_status launched(hipError_t e, const char* who) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    dsa_status _st = (x);           \
+    if (_st != DSA_OK) return _st;  \
+  } while (0)
+
+size_t scores_bytes(int rows, int L_max) { return align256((size_t)rows * L_max * sizeof(float)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_UNKNOWN_STATUS";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+size_t dsa_workspace_size(int op, const dsa_batch_t* bt, int Hi, int H, int k, int n_layers) {
+  (void)Hi;
+  (void)n_layers;
+  if (!bt || bt->B < 1 || bt->Q < 1 || bt->L_max < 1 || k < 1) return 0;
+  const int rows = bt->B * bt->Q;
+  switch (op) {
+    case DSA_OP_INDEX_SCORE: return 0;
+    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(rows, bt->L_max);
+    case DSA_OP_SPARSE_MLA: return (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k) : 0;
+    case DSA_OP_FORWARD_SHARED: {
+      // scores + top-k state for every query token (the largest case), then the MLA partials
+      size_t a = scores_bytes(rows, bt->L_max) + align256(dsa::topk_workspace_bytes(rows, bt->L_max));
+      size_t m = (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k) : 0;
+      return a + align256(m);
+    }
+  }
+  return 0;
+}
+
+dsa_status dsa_index_score(const dsa_batch_t* batch, const uint8_t* q, const float* w, int Hi,
+                           const dsa_cache_t* keys, float* scores, void* stream) {
+  const char* who = "dsa_index_score";
+  TRY(check_batch(batch, who));
+  if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
+  TRY(check_ptr(q, 16, who, "q"));
+  TRY(check_ptr(w, 4, who, "w"));
+  TRY(check_ptr(scores, 4, who, "scores"));
+  TRY(check_cache(keys, batch->L_max, who, "keys"));
+  g_last_error.clear();
+  return launched(dsa::launch_index_score(host_batch(batch), q, w, Hi, host_cache(keys), scores, (hipStream_t)stream), who);
+}
+
+dsa_status dsa_topk(const dsa_batch_t* batch, const float* scores, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                    void* stream) {
+  const char* who = "dsa_topk";
+  TRY(check_batch(batch, who));
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
+  TRY(check_ptr(scores, 4, who, "scores"));
+  TRY(check_ptr(idx, 4, who, "idx"));
+  TRY(check_ws(ws, ws_bytes, dsa::topk_workspace_bytes(batch->B * batch->Q, batch->L_max), who));
+  g_last_error.clear();
+  return launched(dsa::launch_topk(host_batch(batch), scores, k, idx, ws, (hipStream_t)stream), who);
+}
+
+dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H, const dsa_cache_t* latent,
+                              const int32_t* idx, int k, int idx_q_stride, float softmax_scale, float* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "dsa_sparse_mla_fwd";
+  TRY(check_batch(batch, who));
+  if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
+  if (idx_q_stride != 0 && idx_q_stride != k)
+    return fail(DSA_ERR_INVALID_ARG, "%s: idx_q_stride=%d must be 0 or k=%d", who, idx_q_stride, k);
+  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  TRY(check_ptr(q, 16, who, "q"));
+  TRY(check_ptr(idx, 4, who, "idx"));
+  TRY(check_ptr(out, 16, who, "out"));
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse misaligned", who);
+  TRY(check_cache(latent, batch->L_max, who, "latent"));
+  TRY(check_ws(ws, ws_bytes, dsa::sparse_mla_workspace_bytes(batch->B * batch->Q, H, k), who));
+  g_last_error.clear();
+  return launched(dsa::launch_sparse_mla(host_batch(batch), q, H, host_cache(latent), idx, k, idx_q_stride,
+                                         softmax_scale, out, lse, ws, (hipStream_t)stream),
+                  who);
+}
+
+dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                              const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                              const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,
+                              float* const* out, float* const* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* who = "dsa_forward_shared";
+  TRY(check_batch(batch, who));
+  if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
+  if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
+  if (share_first_query != 0 && share_first_query != 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: share_first_query=%d must be 0 or 1", who, share_first_query);
+  if (n_layers < 1 || n_layers > 64) return fail(DSA_ERR_INVALID_ARG, "%s: n_layers=%d outside [1, 64]", who, n_layers);
+  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  TRY(check_ptr(q_e4m3, 16, who, "q_e4m3"));
+  TRY(check_ptr(w, 4, who, "w"));
+  TRY(check_ptr(idx_out, 4, who, "idx_out"));
+  TRY(check_cache(keys, batch->L_max, who, "keys"));
+  if (!q_bf16 || !latents || !out) return fail(DSA_ERR_INVALID_ARG, "%s: per-layer arrays must not be NULL", who);
+  for (int l = 0; l < n_layers; ++l) {
+    TRY(check_ptr(q_bf16[l], 16, who, "q_bf16[layer]"));
+    TRY(check_ptr(out[l], 16, who, "out[layer]"));
+    TRY(check_cache(&latents[l], batch->L_max, who, "latent"));
+    if (lse && lse[l] && !aligned(lse[l], 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse[%d] misaligned", who, l);
+  }
+  const size_t need = dsa_workspace_size(DSA_OP_FORWARD_SHARED, batch, Hi, H, k, n_layers);
+  TRY(check_ws(ws, ws_bytes, need, who));
+  g_last_error.clear();
+
+  const hipStream_t s = (hipStream_t)stream;
+  const int rows_all = batch->B * batch->Q;
+  dsa::HostBatch sel = host_batch(batch);          // the query tokens that get scores + top-k
+  if (share_first_query) sel.Q = 1;                // token 0 of each sequence; inputs keep stride Q
+  const int rows_sel = batch->B * sel.Q;
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += scores_bytes(rows_all, batch->L_max);
+  void* topk_ws = p;
+  p += align256(dsa::topk_workspace_bytes(rows_all, batch->L_max));
+  void* mla_ws = p;
+  (void)rows_sel;
+
+  TRY(launched(dsa::launch_index_score(sel, q_e4m3, w, Hi, host_cache(keys), scores, s), who));
+  TRY(launched(dsa::launch_topk(sel, scores, k, idx_out, topk_ws, s), who));
+  const int stride = share_first_query ? 0 : k;
+  for (int l = 0; l < n_layers; ++l) {
+    TRY(launched(dsa::launch_sparse_mla(host_batch(batch), q_bf16[l], H, host_cache(&latents[l]), idx_out, k, stride,
+                                        softmax_scale, out[l], lse ? lse[l] : nullptr, mla_ws, s),
+                 who));
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Device-side helpers shared by the DSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kDi = 128;     // indexer head dim (bytes per e4m3 key row)
+constexpr int kDqk = 576;    // latent row: 512 latent + 64 RoPE
+constexpr int kDv = 512;     // value = first 512 dims of the latent row
+constexpr int kMaxK = 2048;
+
+// Row address of token t of sequence b in a token-major cache (contiguous or paged).
+struct CacheView {
+  const uint8_t* base;
+  const int32_t* table;
+  int max_pages, page_size;
+  int64_t row_bytes;
+  int L_max;
+  __device__ __forceinline__ const uint8_t* row(int b, int t) const {
+    if (table == nullptr) return base + ((int64_t)b * L_max + t) * row_bytes;
+    int page = table[(int64_t)b * max_pages + t / page_size];
+    return base + ((int64_t)page * page_size + (t % page_size)) * row_bytes;
+  }
+};
+
+// Position of query token j of sequence b; in_Q = query tokens per sequence in the inputs.
+__device__ __forceinline__ int query_pos(const int32_t* seq_lens, const int32_t* q_pos, int in_Q, int b, int j) {
+  return q_pos ? q_pos[b * in_Q + j] : seq_lens[b] - in_Q + j;
+}
+
+// 16x16x128 FP8(E4M3) x FP8(E4M3) -> fp32 matrix-core product, accumulating into c.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, 32 bytes each; the two
+// operands must use the same byte order along K. c[r] = C[4*(l/16) + r][l % 16].
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16x16x32 bf16 matrix-core product: lane l supplies 8 bf16 of row (l % 16) of A and of
+// column (l % 16) of B with one shared K order; c[r] = C[4*(l/16) + r][l % 16].
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Order-preserving map of an IEEE float to uint32 (larger float -> larger key); -0 -> +0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

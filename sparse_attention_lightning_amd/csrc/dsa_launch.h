@@ -1,0 +1,37 @@
+// Internal launchers of the DSA kernels (host side). Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct HostCache {
+  const void* base;
+  const int32_t* table;
+  int max_pages, page_size;
+};
+
+struct HostBatch {
+  int B, Q, L_max;
+  const int32_t* seq_lens;
+  const int32_t* q_pos;
+  int in_Q;   // query tokens per sequence in the inputs (q, w, q_pos rows); Q <= in_Q
+};
+
+// Lightning-indexer scores [B][Q][L_max].
+hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float* w, int Hi,
+                              const HostCache& keys, float* scores, hipStream_t s);
+
+// Top-k selection. Workspace layout and size are owned by topk.hip.
+size_t topk_workspace_bytes(int rows, int L_max);
+hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s);
+
+// Sparse MLA (MQA mode). Workspace holds split partials.
+int sparse_mla_splits(int rows, int H, int k);
+size_t sparse_mla_workspace_bytes(int rows, int H, int k);
+hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
+                             const int32_t* idx, int k, int idx_q_stride, float scale, float* out,
+                             float* lse, void* ws, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,142 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments on the host with the documented status before touching HIP."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_attention_lightning_amd as dsa
+from sparse_attention_lightning_amd._binding import BatchT, CacheT
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+A = 1 << 20          # a fake, well-aligned "device address": never dereferenced by these calls
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(dsa.EXPORTS)
+    lib = dsa.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = dsa.lib()
+    assert [lib.dsa_status_str(i).decode() for i in range(5)] == [
+        "DSA_OK", "DSA_ERR_INVALID_ARG", "DSA_ERR_UNSUPPORTED", "DSA_ERR_WORKSPACE", "DSA_ERR_HIP"]
+
+
+def batch(B=2, Q=1, L=4096, seq=A, q_pos=None):
+    return BatchT(B, Q, L, seq, q_pos)
+
+
+def cache(base=A, table=None, max_pages=0, page=0):
+    return CacheT(base, table, max_pages, page)
+
+
+def call_index(bt, q=A, w=A, Hi=64, kc=None, scores=A):
+    kc = kc or cache()
+    lib = dsa.lib()
+    return lib.dsa_index_score(C.byref(bt) if bt is not None else None, q, w, Hi, C.byref(kc), scores, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(bt=None), INVALID),
+    (dict(bt=batch(B=0)), INVALID),
+    (dict(bt=batch(Q=0)), INVALID),
+    (dict(bt=batch(L=0)), INVALID),
+    (dict(bt=batch(Q=5000, L=4096)), INVALID),
+    (dict(bt=batch(seq=None)), INVALID),
+    (dict(bt=batch(seq=A + 2)), INVALID),
+    (dict(bt=batch(), Hi=48), UNSUPPORTED),
+    (dict(bt=batch(), Hi=128), UNSUPPORTED),
+    (dict(bt=batch(), q=None), INVALID),
+    (dict(bt=batch(), q=A + 8), INVALID),
+    (dict(bt=batch(), w=A + 2), INVALID),
+    (dict(bt=batch(), scores=None), INVALID),
+    (dict(bt=batch(), kc=cache(base=None)), INVALID),
+    (dict(bt=batch(), kc=cache(base=A + 4)), INVALID),
+    (dict(bt=batch(), kc=cache(table=A, max_pages=64, page=24)), UNSUPPORTED),
+    (dict(bt=batch(), kc=cache(table=A, max_pages=64, page=0)), UNSUPPORTED),
+    (dict(bt=batch(L=4096), kc=cache(table=A, max_pages=63, page=64)), INVALID),
+])
+def test_index_score_rejects(case, expect):
+    assert call_index(**case) == expect
+    assert dsa.lib().dsa_last_error().decode().startswith("dsa_index_score")
+
+
+def test_topk_rejects():
+    lib = dsa.lib()
+    bt = batch()
+    need = dsa.workspace_size(dsa.OP_TOPK, 2, 1, 4096, k=2048)
+    assert need > 0
+    for k in (0, -1, 2049, 4096):
+        assert lib.dsa_topk(C.byref(bt), A, k, A, A, need, None) == UNSUPPORTED
+    assert lib.dsa_topk(C.byref(bt), A, 2048, A, None, need, None) == WORKSPACE
+    assert lib.dsa_topk(C.byref(bt), A, 2048, A, A + 128, need, None) == WORKSPACE
+    assert lib.dsa_topk(C.byref(bt), A, 2048, A, A, need - 1, None) == WORKSPACE
+    assert lib.dsa_topk(C.byref(bt), A + 1, 2048, A, A, need, None) == INVALID
+    assert lib.dsa_topk(C.byref(bt), A, 2048, None, A, need, None) == INVALID
+
+
+def test_sparse_mla_rejects():
+    lib = dsa.lib()
+    bt = batch(B=1, L=8192)
+    kc = cache()
+    need = dsa.workspace_size(dsa.OP_SPARSE_MLA, 1, 1, 8192, H=128, k=2048)
+    ok = dict(q=A, H=128, k=2048, stride=2048, scale=0.04, out=A, lse=A, ws=A, n=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.dsa_sparse_mla_fwd(C.byref(bt), a["q"], a["H"], C.byref(kc), A, a["k"], a["stride"], a["scale"],
+                                      a["out"], a["lse"], a["ws"], a["n"], None)
+    assert call(H=96) == UNSUPPORTED
+    assert call(H=256) == UNSUPPORTED
+    assert call(k=0) == UNSUPPORTED
+    assert call(stride=5) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(q=A + 4) == INVALID
+    assert call(out=A + 4) == INVALID
+    assert call(lse=A + 2) == INVALID
+    if need:
+        assert call(ws=None) == WORKSPACE
+        assert call(n=need - 1) == WORKSPACE
+
+
+def test_forward_shared_rejects():
+    lib = dsa.lib()
+    bt = batch(B=1, L=8192)
+    kc = cache()
+    lat = (CacheT * 4)(*[cache() for _ in range(4)])
+    ptrs = (C.c_void_p * 4)(A, A, A, A)
+    need = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 1, 1, 8192, k=2048, n_layers=4)
+
+    def call(share=0, nl=4, qs=ptrs, lats=lat, outs=ptrs, ws=A, n=need, Hi=64, H=128):
+        return lib.dsa_forward_shared(C.byref(bt), A, A, Hi, C.byref(kc), 2048, share, nl, qs, H, lats, 0.04, outs,
+                                      None, A, ws, n, None)
+    assert call(share=2) == INVALID
+    assert call(nl=0) == INVALID
+    assert call(qs=None) == INVALID
+    assert call(outs=(C.c_void_p * 4)(A, A, None, A)) == INVALID
+    assert call(Hi=16) == UNSUPPORTED
+    assert call(H=32) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(n=need - 1) == WORKSPACE
+
+
+def test_workspace_sizes_scale_with_batch():
+    small = dsa.workspace_size(dsa.OP_TOPK, 1, 1, 8192)
+    big = dsa.workspace_size(dsa.OP_TOPK, 32, 1, 131072)
+    assert 0 < small < big
+    assert dsa.workspace_size(dsa.OP_INDEX_SCORE, 32, 1, 131072) == 0
+    shared = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 32, 1, 131072)
+    assert shared >= 32 * 131072 * 4 + big

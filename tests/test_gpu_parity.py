@@ -1,0 +1,255 @@
+"""GPU parity of the DSA hot path against the CPU oracle, through the C ABI.
+
+Small cases run the oracle on every output; they span several key chunks, split tiles and
+a ragged tail. Tolerances and their derivations are in tests/helpers.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import (bits, check_mla, check_scores, check_topk_sets, dsa_cache, integer_e4m3, key_cache,
+                     latent_cache, np_, positions, score_tolerance)
+
+pytestmark = pytest.mark.gpu
+
+dsa = pytest.importorskip("sparse_attention_lightning_amd")
+DEV = "cuda"
+
+
+def gpu_batch(wl, seed=0, layers=None, with_mla=True):
+    """Draw on the CPU, copy to the GPU (small cases)."""
+    cpu = synth.generate(wl, seed=seed, device="cpu", layers=layers, with_mla=with_mla)
+    return cpu, cpu.to(DEV)
+
+
+def keys_arg(g):
+    return dsa_cache(g.keys, g.key_table, g.wl.page_size)
+
+
+def lat_arg(g, layer=0):
+    return dsa_cache(g.latent[layer], g.latent_table[layer], g.wl.page_size)
+
+
+# ----------------------------------------------------------------------------- indexer
+@pytest.mark.parametrize("Hi", [64, 32])
+@pytest.mark.parametrize("page_size", [0, 64, 16])
+def test_index_score_integer_inputs_exact(Hi, page_size):
+    wl = synth.Workload("int", B=3, Q=2, L=5000, Hi=Hi, page_size=page_size, L_max=5056,
+                        seq_lens=(5000, 4099, 1500))
+    cpu, g = gpu_batch(wl, with_mla=False)
+    gen = torch.Generator().manual_seed(11)
+    cpu.q_idx = integer_e4m3(tuple(cpu.q_idx.shape), gen)
+    cpu.keys = integer_e4m3(tuple(cpu.keys.shape), gen)
+    g.q_idx, g.keys = cpu.q_idx.to(DEV), cpu.keys.to(DEV)
+    scores = np_(dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax))
+    torch.cuda.synchronize()
+    kc = key_cache(cpu)
+    pos = positions(wl)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            p = pos[b][j]
+            exact = oracle.index_scores(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc, b, p, wl.lmax)
+            tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)),
+                                  integer_inputs=True)
+            check_scores(scores[b, j], exact, tol, p)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_tiny_8k", {}),                                                   # the 8K tiny decode workload as is
+    ("decode_b32_128k_paged", dict(B=2, L=9000, L_max=9024, planted=4, seq_lens=(9000, 7777))),
+    ("verify_b64_q8_32k", dict(B=2, L=4200, L_max=4224)),
+])
+def test_index_score_normal_inputs(name, kw):
+    wl = synth.small(name, **kw)
+    cpu, g = gpu_batch(wl, with_mla=False)
+    scores = np_(dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax))
+    kc = key_cache(cpu)
+    pos = positions(wl)
+    worst = 0.0
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            p = pos[b][j]
+            exact = oracle.index_scores(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc, b, p, wl.lmax)
+            tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)))
+            worst = max(worst, check_scores(scores[b, j], exact, tol, p))
+    print(f"{name}: max |score error| {worst:.3g}")
+
+
+def test_index_score_explicit_positions_and_determinism():
+    wl = synth.small("verify_b64_q8_32k", B=2, Q=3, L=3000, L_max=3000, page_size=0)
+    cpu, g = gpu_batch(wl, with_mla=False)
+    q_pos = torch.tensor([[5, 1000, 2999], [0, 17, 2048]], dtype=torch.int32)
+    s1 = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax, q_pos=q_pos.to(DEV))
+    s2 = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax, q_pos=q_pos.to(DEV))
+    assert torch.equal(s1, s2)
+    scores = np_(s1)
+    kc = key_cache(cpu)
+    for b in range(2):
+        for j in range(3):
+            p = int(q_pos[b, j])
+            exact = oracle.index_scores(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc, b, p, wl.lmax)
+            tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)))
+            check_scores(scores[b, j], exact, tol, p)
+
+
+# ----------------------------------------------------------------------------- top-k
+def run_topk(scores32, seq_lens, k, q_pos=None):
+    t = torch.from_numpy(np.ascontiguousarray(scores32)).to(DEV)
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int32, device=DEV)
+    return np_(dsa.topk(t, sl, k, q_pos=qp))
+
+
+def oracle_topk(scores32, seq_lens, k, q_pos=None):
+    return oracle.topk_batch(scores32, seq_lens, k, q_pos=q_pos)
+
+
+@pytest.mark.parametrize("k", [2048, 1, 7, 300])
+def test_topk_exact_on_oracle_scores(k):
+    wl = synth.small("verify_b64_q8_32k", B=3, Q=2, L=20000, L_max=20480, page_size=0, seq_lens=(20000, 9000, 2100))
+    cpu = synth.generate(wl, seed=3, with_mla=False)
+    s = oracle.index_scores_batch(np_(cpu.q_idx), np_(cpu.w), key_cache(cpu), wl.lens, wl.lmax)
+    s32 = s.astype(np.float32)
+    got = run_topk(s32, wl.lens, k)
+    assert np.array_equal(got, oracle_topk(s32, wl.lens, k))
+
+
+def test_topk_exact_ties_and_degenerate_rows():
+    rng = np.random.default_rng(7)
+    L = 13000
+    rows = [
+        rng.integers(0, 50, L).astype(np.float32),                 # heavy ties at the threshold
+        np.full(L, 3.5, np.float32),                                # all equal: the first k positions
+        np.where(rng.random(L) < 0.5, -0.0, 0.0).astype(np.float32),  # -0 and +0 tie
+        rng.normal(size=L).astype(np.float32),
+        np.concatenate([np.full(L - 5000, -np.inf, np.float32), rng.normal(size=5000).astype(np.float32)]),
+        (rng.integers(-3, 3, L) * 1e-30).astype(np.float32),        # denormal-scale values
+    ]
+    s = np.stack(rows)[:, None, :]
+    lens = [L, L, L, 12345, L, 4097]
+    for k in (2048, 1000, 1):
+        got = run_topk(s, lens, k)
+        assert np.array_equal(got, oracle_topk(s, lens, k)), k
+
+
+def test_topk_rows_shorter_than_k_and_positions():
+    rng = np.random.default_rng(8)
+    L = 6000
+    s = rng.normal(size=(2, 4, L)).astype(np.float32)
+    lens = [L, 1500]
+    q_pos = [[0, 2047, 2048, 5999], [10, 1499, 700, 2047]]
+    got = run_topk(s, lens, 2048, q_pos=q_pos)
+    assert np.array_equal(got, oracle_topk(s, lens, 2048, q_pos=np.array(q_pos)))
+    assert got[0, 0, 0] == 0 and np.all(got[0, 0, 1:] == -1)
+
+
+def test_topk_deterministic():
+    rng = np.random.default_rng(9)
+    s = rng.integers(0, 1000, size=(4, 1, 70000)).astype(np.float32)
+    a = run_topk(s, [70000] * 4, 2048)
+    b = run_topk(s, [70000] * 4, 2048)
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, oracle_topk(s, [70000] * 4, 2048))
+
+
+# ----------------------------------------------------------------------------- sparse MLA
+def oracle_idx(cpu, wl, share_first=False):
+    Q = 1 if share_first else wl.Q
+    pos = np.array(positions(wl))[:, :Q]
+    s = oracle.index_scores_batch(np_(cpu.q_idx)[:, :Q], np_(cpu.w)[:, :Q], key_cache(cpu), wl.lens, wl.lmax, q_pos=pos)
+    return oracle.topk_batch(s.astype(np.float32), wl.lens, wl.k, q_pos=pos), s
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_tiny_8k", dict(B=2, L=5000, seq_lens=(5000, 3333))),                                 # split path
+    ("decode_b32_128k_paged", dict(B=2, L=2600, L_max=2624, planted=0, H=64, seq_lens=(2600, 1000))),  # p+1 < k rows
+    ("verify_b64_q8_32k", dict(B=2, L=3000, L_max=3008, k=100)),                                  # k not a multiple of 32
+    ("prefill_4096_at_128k", dict(Q=130, L=3000, k=256)),                                          # many rows, no split
+])
+def test_sparse_mla_on_oracle_indices(name, kw):
+    wl = synth.small(name, **kw)
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl)
+    idx_g = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), idx, wl.scale)
+    worst = (0.0, 0.0)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            m = check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
+            worst = (max(worst[0], m[0]), max(worst[1], m[1]))
+    print(f"{name}: max abs {worst[0]:.3g} rel L2 {worst[1]:.3g}")
+
+
+def test_sparse_mla_shared_index_row_and_empty_sets():
+    wl = synth.small("verify_b64_q8_32k", B=2, Q=4, L=2500, L_max=2560, k=512)
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl, share_first=True)       # [B, 1, k]
+    idx[1, 0, :] = -1                                    # sequence 1: empty set -> out 0, lse -inf
+    idx_g = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), idx, wl.scale, idx_q_stride_is_k=False)
+    for j in range(wl.Q):
+        check_mla(out[0, j], lse[0, j], ref_o[0, j], ref_l[0, j])
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_sparse_mla_deterministic_and_paged_equals_contiguous():
+    wl = synth.small("decode_b32_128k_paged", B=3, L=4000, L_max=4032, planted=0, seq_lens=(4000, 3000, 2222))
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl)
+    idx_g = torch.from_numpy(idx).to(DEV)
+    o1, l1 = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    o2, l2 = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    tab = g.latent_table[0].long()
+    contig = g.latent[0][tab].reshape(wl.B, wl.lmax, 576).contiguous()
+    o3, l3 = dsa.sparse_mla_fwd(g.q_mla[0], dsa_cache(contig, None, 0), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+# ----------------------------------------------------------------------------- whole path
+def test_decode_tiny_end_to_end():
+    """The 8K tiny decode workload exactly: B=1, Q=1, L=8192 contiguous, seed 0."""
+    wl = synth.WORKLOADS["decode_tiny_8k"]
+    cpu, g = gpu_batch(wl)
+    scores = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax)
+    idx = dsa.topk(scores, g.seq_lens, wl.k)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    o_idx, exact = oracle_idx(cpu, wl)
+    p = wl.L - 1
+    tol = score_tolerance(np_(cpu.q_idx[0, 0]), np_(cpu.w[0, 0]), np_(cpu.keys[0]))
+    check_scores(np_(scores)[0, 0], exact[0, 0], tol, p)
+    swaps = check_topk_sets(np_(idx)[0, 0], o_idx[0, 0], exact[0, 0], wl.k)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), o_idx, wl.scale)
+    check_mla(np_(out)[0, 0], np_(lse)[0, 0], ref_o[0, 0], ref_l[0, 0])
+    print(f"decode_tiny_8k: {swaps} near-threshold swaps")
+
+
+@pytest.mark.parametrize("share_first", [False, True])
+def test_forward_shared_small(share_first):
+    if share_first:
+        wl = synth.small("verify_b64_q8_32k_draftshare", B=3, L=3000, L_max=3008, seq_lens=(3000, 2900, 2100))
+    else:
+        wl = synth.small("indexshare_b8_1m_4layers", B=2, L=6000, L_max=6016, seq_lens=(6000, 4444))
+    cpu, g = gpu_batch(wl)
+    idx, res = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla, [lat_arg(g, l) for l in range(wl.n_layers)],
+                                  wl.scale, g.seq_lens, wl.lmax, share_first_query=share_first)
+    o_idx, exact = oracle_idx(cpu, wl, share_first=share_first)
+    idx = np_(idx)
+    for b in range(wl.B):
+        for j in range(o_idx.shape[1]):
+            check_topk_sets(idx[b, j], o_idx[b, j], exact[b, j], wl.k)
+    for layer in range(wl.n_layers):
+        ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[layer]), latent_cache(cpu, layer), o_idx, wl.scale,
+                                               idx_q_stride_is_k=not share_first)
+        out, lse = np_(res[layer][0]), np_(res[layer][1])
+        for b in range(wl.B):
+            for j in range(wl.Q):
+                check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
