@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: lightning-indexer scores for every
+query token, top-k selection, sparse MLA (MQA mode) with its split combine; for an
+IndexShare workload, the attention runs once per layer of the group with the same indices.
+Inputs are synthetic (seeded), resident in HBM before timing starts, and rotate over
+several independent batches so that no step re-reads rows a previous step left in cache.
+
+Prints ONE JSON line. Default workload: decode, batch 32, 128K-token paged caches.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "sparse-attn decode tokens/s and HBM GB/s at 128K ctx; prefill indexer TFLOPS"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_b32_128k_paged")
+    ap.add_argument("--rotate", type=int, default=3, help="independent input batches cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def index_work(wl):
+    """Algorithmic bytes and FLOPs of one index-score launch (every key read once per sequence)."""
+    B, Q, Hi = wl.B, wl.Q, wl.Hi
+    rows = 1 if wl.share_first_query else Q
+    keys = sum(wl.lens) * 128
+    scores = B * rows * wl.lmax * 4
+    qw = B * rows * Hi * (128 + 4)
+    table = B * wl.max_pages * 4 if wl.page_size else 0
+    flops = 0
+    for n in wl.lens:
+        for j in range(rows):
+            flops += (n - Q + j + 1) * Hi * 128 * 2
+    return keys + scores + qw + table, flops
+
+
+def mla_work(wl):
+    """Algorithmic bytes and FLOPs of one sparse-MLA launch (rows gathered once per query token)."""
+    rows = wl.B * wl.Q
+    sel = sum(min(wl.k, n - wl.Q + j + 1) for n in wl.lens for j in range(wl.Q))
+    byts = sel * 1152 + rows * wl.H * (576 * 2 + 512 * 4 + 4) + rows * wl.k * 4
+    flops = sel * wl.H * 2 * (576 + 512)
+    return byts, flops
+
+
+def traffic_from_profile(wl_name):
+    """HBM bytes per index-score launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (matched by hash); else None."""
+    path = os.path.join(ROOT, "profiles", f"index_score_{wl_name}_counters.json")
+    src = os.path.join(ROOT, "sparse_attention_lightning_amd", "csrc", "index_score.hip")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if rec.get("source_sha256_16") != h:
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(batches, wl, budget_s):
+    """The oracle as it stands, timed on a bounded sample of the same workload on host cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    g = batches[0]
+    done_tokens, elapsed, seqs = 0, 0.0, 0
+    rows_per_seq = 1 if wl.share_first_query else wl.Q
+    for b in range(wl.B):
+        # inputs of sequence b in logical token order (input preparation, not timed)
+        def seq_rows(data, table):
+            if data.dtype == torch.bfloat16:
+                data = data.view(torch.int16)
+            if table is None:
+                return data[b:b + 1].cpu().numpy()
+            return data[table[b].long()].reshape(1, -1, data.shape[-1]).cpu().numpy()
+        keys = oracle.Cache(seq_rows(g.keys, g.key_table))
+        lats = [oracle.Cache(seq_rows(g.latent[l], g.latent_table[l]).view(np.uint16)) for l in range(len(g.latent))]
+        q_idx = g.q_idx[b].cpu().numpy()
+        w = g.w[b].cpu().numpy()
+        q_mla = [t[b].view(torch.int16).cpu().numpy().view(np.uint16) for t in g.q_mla]
+        n = wl.lens[b]
+        t0 = time.perf_counter()
+        for j in range(rows_per_seq):
+            p = n - wl.Q + j
+            s = oracle.index_scores(q_idx[j], w[j], keys, 0, p, wl.lmax)
+            idx = oracle.select_topk(s.astype(np.float32), p, wl.k)
+            users = range(wl.Q) if wl.share_first_query else [j]
+            for layer in range(len(lats)):
+                for u in users:
+                    oracle.sparse_mla_one(q_mla[layer][u], lats[layer], 0, idx, wl.scale)
+        elapsed += time.perf_counter() - t0
+        done_tokens += wl.Q if wl.share_first_query else rows_per_seq
+        seqs += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": threads if threads > 1 else cores,
+            "kind": "oracle",
+            "sample": f"{seqs} of {wl.B} sequences of {wl.name} (all {rows_per_seq * seqs} query tokens of the "
+                      f"sample: index scores over every visible key, top-{wl.k}, sparse MLA over {wl.H} heads x "
+                      f"{len(lats)} layer(s)); {elapsed:.1f} s of oracle time; numpy float64, host threads={threads}, "
+                      f"affinity cores={cores}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the DSA path on one GPU; runs on more than one GPU are not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import sparse_attention_lightning_amd as dsa
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batches = [synth.generate(wl, seed=s, device=dev) for s in range(args.rotate)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    rows_sel = wl.B * (1 if wl.share_first_query else wl.Q)
+    scores = torch.empty((wl.B, 1 if wl.share_first_query else wl.Q, wl.lmax), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.B, scores.shape[1], wl.k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((wl.B, wl.Q, wl.H, 512), dtype=torch.float32, device=dev) for _ in range(wl.n_layers)]
+    lses = [torch.empty((wl.B, wl.Q, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.n_layers)]
+    ws_topk = torch.empty(dsa.workspace_size(dsa.OP_TOPK, wl.B, scores.shape[1], wl.lmax, k=wl.k), dtype=torch.uint8,
+                          device=dev)
+    n_mla = dsa.workspace_size(dsa.OP_SPARSE_MLA, wl.B, wl.Q, wl.lmax, H=wl.H, k=wl.k)
+    ws_mla = torch.empty(max(n_mla, 1), dtype=torch.uint8, device=dev)
+    q_pos = None
+    if wl.share_first_query:   # scores + top-k for query token 0 of each sequence only
+        q_pos = torch.tensor([[n - wl.Q] for n in wl.lens], dtype=torch.int32, device=dev)
+    ev = {k: [] for k in ("index", "topk", "mla")}
+
+    def step(i, record):
+        g = batches[i % len(batches)]
+        keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        qi = g.q_idx[:, :1].contiguous() if wl.share_first_query else g.q_idx
+        wi = g.w[:, :1].contiguous() if wl.share_first_query else g.w
+        dsa.index_score(qi, wi, keys, g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores, stream=stream)
+        if record:
+            e[1].record(stream)
+        dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
+        if record:
+            e[2].record(stream)
+        for layer in range(wl.n_layers):
+            dsa.sparse_mla_fwd(g.q_mla[layer], dsa.Cache(g.latent[layer], g.latent_table[layer], wl.page_size), idx,
+                               wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0 if wl.share_first_query else wl.k,
+                               out=outs[layer], lse=lses[layer], ws=ws_mla if n_mla else None, stream=stream)
+        if record:
+            e[3].record(stream)
+            ev["index"].append((e[0], e[1]))
+            ev["topk"].append((e[1], e[2]))
+            ev["mla"].append((e[2], e[3]))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items()}   # microseconds
+
+    tokens = wl.B * wl.Q
+    value = tokens / (ms_per_step / 1e3)
+    ibytes, iflops = index_work(wl)
+    mbytes, mflops = mla_work(wl)
+    index_s = avg["index"] * 1e-6
+    if args.workload.startswith("prefill"):
+        roof = {"bound": "mfma", "achieved": iflops / index_s / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": ibytes / index_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profile(args.workload)
+    roof["kernel"] = "index_score (lightning indexer scan)"
+    step_bytes = ibytes + mbytes * wl.n_layers
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "L": wl.L, "page_size": wl.page_size, "k": wl.k,
+                   "Hi": wl.Hi, "H": wl.H, "n_layers": wl.n_layers, "share_first_query": wl.share_first_query,
+                   "planted": wl.planted},
+        "roofline": roof,
+        "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"]},
+        "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "index_tflops": iflops / index_s / 1e12,
+        "mla_tflops": mflops * wl.n_layers / (avg["mla"] * 1e-6) / 1e12,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(batches, wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

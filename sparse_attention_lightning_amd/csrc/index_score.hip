@@ -13,8 +13,15 @@
 
 namespace dsa {
 
-constexpr int kScoreChunk = 2048;          // keys per workgroup (4 waves x 512)
+#ifndef DSA_SCORE_CHUNK
+#define DSA_SCORE_CHUNK 1024
+#endif
+#ifndef DSA_SCORE_PIPE
+#define DSA_SCORE_PIPE 0
+#endif
+constexpr int kScoreChunk = DSA_SCORE_CHUNK;   // keys per workgroup (4 waves)
 constexpr int kScoreWaveKeys = kScoreChunk / 4;
+static_assert(kScoreWaveKeys / 16 + 1 <= 64, "a wave's pages fit in one register across lanes");
 
 // XCD-aware work index: consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
 // remap so that each XCD walks a contiguous range of work items (items sharing keys share L2).
@@ -54,11 +61,18 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
     return;
   }
 
-  // query operand: A rows = heads 16m + (l % 16), bytes [32g, 32g + 32) of the 128-byte head
+  // Byte order along K shared by both operands: lane group g holds bytes [16g, 16g+16) and
+  // [64+16g, 64+16g+16) of a 128-byte row, so each 16-byte load instruction of a wave covers
+  // 16 whole 64-byte segments.
+  // query operand: A rows = heads 16m + (l % 16)
   v8i qa[MT];
   const uint8_t* qrow = q + (int64_t)bqi * HI * kDi;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) qa[m] = *(const v8i*)(qrow + (16 * m + c16) * kDi + 32 * g);
+  for (int m = 0; m < MT; ++m) {
+    const uint8_t* hp = qrow + (16 * m + c16) * kDi;
+    const v4i lo4 = *(const v4i*)(hp + 16 * g), hi4 = *(const v4i*)(hp + 64 + 16 * g);
+    qa[m] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  }
   // weights of the heads this lane's accumulators hold: head 16m + 4g + r
   float wr[MT][4];
   const float* wrow = w + (int64_t)bqi * HI;
@@ -67,34 +81,52 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) wr[m][r] = wrow[16 * m + 4 * g + r];
 
+  // Page ids of this wave's key range, one per lane, resolved once: the key loads then never
+  // wait on a block-table load. Group t's page is read back with a wave-uniform readlane.
+  const bool paged = keys.table != nullptr;
+  int page0 = 0, my_page = 0;
+  if (paged) {
+    page0 = t_begin / keys.page_size;
+    const int pg = page0 + lane;
+    const int last = min(t_end - 1, p) / keys.page_size;
+    if (pg <= last) my_page = keys.table[(int64_t)b * keys.max_pages + pg];
+  }
+  auto group_row = [&](int t16) -> const uint8_t* {   // row of key t16 (a multiple of 16)
+    if (!paged) return keys.base + ((int64_t)b * L_max + t16) * kDi;
+    const int page = __builtin_amdgcn_readlane(my_page, t16 / keys.page_size - page0);
+    return keys.base + ((int64_t)page * keys.page_size + (t16 % keys.page_size)) * kDi;
+  };
+  // keys t .. t+63 as four B operands (16 keys each); keys after p are not read
+  auto load_keys = [&](int t, v4i (&kb)[4][2]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int tk = t + 16 * c + c16;     // this lane's key (B column)
+      if (t + 16 * c <= p && t + 16 * c < t_end) {
+        const uint8_t* rowp = group_row(t + 16 * c) + (int64_t)c16 * kDi;  // 16 keys share a page
+        kb[c][0] = tk <= p ? *(const v4i*)(rowp + 16 * g) : (v4i){0, 0, 0, 0};
+        kb[c][1] = tk <= p ? *(const v4i*)(rowp + 64 + 16 * g) : (v4i){0, 0, 0, 0};
+      } else {
+        kb[c][0] = (v4i){0, 0, 0, 0};
+        kb[c][1] = (v4i){0, 0, 0, 0};
+      }
+    }
+  };
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  for (int t = t_begin; t < t_end; t += 64) {
+  auto score_keys = [&](int t, const v4i (&kb)[4][2]) {
+    if (t >= t_end) return;
     float part[4];
-    if (t <= p) {
-      v8i kb[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int tk = t + 16 * c + c16;     // this lane's key (B column)
-        if (tk <= p) {
-          const uint8_t* rowp = keys.row(b, t + 16 * c) + (int64_t)c16 * kDi;  // 16 keys share a page
-          kb[c] = *(const v8i*)(rowp + 32 * g);
-        } else {
-          kb[c] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-        }
+    for (int c = 0; c < 4; ++c) {
+      const v8i bk = {kb[c][0][0], kb[c][0][1], kb[c][0][2], kb[c][0][3],
+                      kb[c][1][0], kb[c][1][1], kb[c][1][2], kb[c][1][3]};
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const v4f acc = mfma_fp8(qa[m], bk, zero);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += wr[m][r] * fmaxf(acc[r], 0.f);
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          v4f acc = mfma_fp8(qa[m], kb[c], zero);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s += wr[m][r] * fmaxf(acc[r], 0.f);
-        }
-        part[c] = s;
-      }
-    } else {
-      part[0] = part[1] = part[2] = part[3] = 0.f;
+      part[c] = s;
     }
     // reduce-scatter over the 4 lane groups: group g ends with the full score of key group c = g
     const bool lo = g < 2;
@@ -107,7 +139,25 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
     const float v = (odd ? x1 : x0) + r2;
     const int tk = t + lane;
     if (tk < t_end) srow[tk] = (tk <= p) ? v : -INFINITY;
+  };
+
+#if DSA_SCORE_PIPE
+  // two-stage pipeline: the next 64 keys are in flight while the current 64 are scored
+  v4i ka[4][2], kb2[4][2];
+  load_keys(t_begin, ka);
+  for (int t = t_begin; t < t_end; t += 128) {
+    load_keys(t + 64, kb2);
+    score_keys(t, ka);
+    load_keys(t + 128, ka);
+    score_keys(t + 64, kb2);
   }
+#else
+  for (int t = t_begin; t < t_end; t += 64) {
+    v4i ka[4][2];
+    load_keys(t, ka);
+    score_keys(t, ka);
+  }
+#endif
 }
 
 hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float* w, int Hi,

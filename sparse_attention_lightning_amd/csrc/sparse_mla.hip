@@ -33,11 +33,18 @@ static_assert(kStepChunks % kMlaThreads == 0, "even gather split");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+#ifndef DSA_MLA_TARGET_WGS
+#define DSA_MLA_TARGET_WGS 256
+#endif
+#ifndef DSA_MLA_MIN_SPLIT
+#define DSA_MLA_MIN_SPLIT 128
+#endif
+
 int sparse_mla_splits(int rows, int H, int k) {
   const int wgs = rows * (H / kHeadsPerWg);
   int s = 1;
-  // aim for ~512 workgroups while each split keeps >= 128 tokens
-  while (wgs * s < 512 && (k + 2 * s - 1) / (2 * s) >= 128 && s < 16) s *= 2;
+  // aim for enough workgroups to fill the chip while each split keeps a minimum of tokens
+  while (wgs * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < 16) s *= 2;
   return s;
 }
 
@@ -63,6 +70,7 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
     float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTok * kPitch];
   __shared__ int vflag[kTok];
+  __shared__ int rowid[kMaxK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -90,45 +98,63 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
   float m_run = -INFINITY;   // running max (log2 domain) of head c16
   float l_run = 0.f;         // this lane's share of the softmax denominator
 
-  // gather of one step into registers: thread handles chunks tid + 256 i
-  v4i stage[kChunksPerThread];
-  int my_pos = -1;           // threads 0..31: index of row tid of the staged step
-  auto gather = [&](int tok0) {
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kMlaThreads * i;
-      const int row = c / kRowChunks, col = c - row * kRowChunks;
-      const int t = tok0 + row;
-      const int pos = (t < tok_end) ? irow[t] : -1;
-      if (pos >= 0) stage[i] = *(const v4i*)(lat.row(b, pos) + 16 * col);
-      else stage[i] = (v4i){0, 0, 0, 0};
-    }
-    if (tid < kTok) my_pos = (tok0 + tid < tok_end) ? irow[tok0 + tid] : -1;
+  // Row index (into the cache's rows) of every token of this split, resolved once through the
+  // index list and the block table; -1 for masked tokens (index -1 or past k).
+  for (int i = tid; i < tok_end - tok_begin; i += kMlaThreads) {
+    const int pos = irow[tok_begin + i];
+    int r = -1;
+    if (pos >= 0)
+      r = lat.table ? lat.table[(int64_t)b * lat.max_pages + pos / lat.page_size] * lat.page_size + pos % lat.page_size
+                    : b * lat.L_max + pos;
+    rowid[i] = r;
+  }
+  __syncthreads();
+  // Gather: 8 threads per row (32 rows per step), thread (row tid/8, part) loads the 16-byte
+  // chunks part + 8i, i < 9, of its row; rows are loaded one step before they are used.
+  // Masked rows read a valid dummy row and are zeroed in LDS.
+  const int grow = tid >> 3, gpart = tid & 7;
+  auto row_of = [&](int tok0) -> int {
+    const int i = tok0 - tok_begin + grow;
+    return (tok0 + grow < tok_end) ? rowid[i] : -1;
   };
-
-  if (tok_begin < tok_end) gather(tok_begin);
+  v4i stage[kChunksPerThread];
+  auto load_rows = [&](int r) {
+    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0);
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) stage[i] = *(const v4i*)(src + 16 * (gpart + 8 * i));
+  };
+  int r_cur = row_of(tok_begin);
+  load_rows(r_cur);
   for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTok) {
     __syncthreads();                           // previous step done with the tile
+    const bool row_ok = r_cur >= 0;
+    uint8_t* dst = tile + grow * kPitch + 16 * gpart;
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kMlaThreads * i;
-      const int row = c / kRowChunks, col = c - row * kRowChunks;
-      *(v4i*)(tile + row * kPitch + 16 * col) = stage[i];
-    }
-    if (tid < kTok) vflag[tid] = my_pos >= 0;
+    for (int i = 0; i < kChunksPerThread; ++i)
+      *(v4i*)(dst + 128 * i) = row_ok ? stage[i] : (v4i){0, 0, 0, 0};
+    if (gpart == 0) vflag[grow] = row_ok;
     __syncthreads();
-    if (tok0 + kTok < tok_end) gather(tok0 + kTok);   // prefetch the next step
+    if (tok0 + kTok < tok_end) {               // block-uniform
+      r_cur = row_of(tok0 + kTok);
+      load_rows(r_cur);
+    }
 
     // ---- S^T = K_tile . Q^T : two 16-token tiles
-    v4f sacc[2];
+    // four independent accumulator chains (2 token tiles x 2 halves of K) keep the matrix
+    // pipe busy with one wave per SIMD
+    v4f sacc[2], sacc2[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* arow = tile + (16 * mt + c16) * kPitch + 16 * g;
+    for (int mt = 0; mt < 2; ++mt) sacc[mt] = sacc2[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kDqk / 32; ++s) acc = mfma_bf16(load_v8bf(arow + 64 * s), qb[s], acc);
-      sacc[mt] = acc;
-    }
+    for (int s = 0; s < kDqk / 64; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint8_t* arow = tile + (16 * mt + c16) * kPitch + 16 * g;
+        sacc[mt] = mfma_bf16(load_v8bf(arow + 64 * s), qb[s], sacc[mt]);
+        sacc2[mt] = mfma_bf16(load_v8bf(arow + 64 * (s + kDqk / 64)), qb[s + kDqk / 64], sacc2[mt]);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sacc[mt] += sacc2[mt];
     // ---- online softmax for head c16 over tokens 16mt + 4g + r
     float z[2][4];
     float tmax = -INFINITY;
@@ -158,13 +184,15 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // ---- rescale O: this lane's accumulators hold heads 4g + r
-    float al[4];
+    if (__ballot(alpha != 1.f) != 0ull) {      // wave-uniform: skip when no head's max moved
+      float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
 #pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt)
+      for (int nt = 0; nt < kDv / 16; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
+        for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
+    }
     // ---- O += P . V, V^T fragments by transpose reads: tokens 4g+e (e<4), 16+4g+(e-4) (e>=4)
     const uint8_t* v0 = tile + (4 * g + (c16 >> 2)) * kPitch + 8 * (c16 & 3);
     const uint8_t* v1 = v0 + 16 * kPitch;
