@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="independent input batches cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -193,6 +195,13 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items()}   # microseconds
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     tokens = wl.B * wl.Q
     value = tokens / (ms_per_step / 1e3)

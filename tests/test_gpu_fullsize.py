@@ -1,0 +1,155 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark times.
+
+Inputs are drawn on the GPU. The oracle checks sampled sequences / query tokens one by one;
+properties that hold at any size are checked on every row (set sizes, ascending order,
+causality, planted tokens, run-to-run determinism).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import check_mla, check_scores, check_topk_sets, score_tolerance
+
+pytestmark = pytest.mark.gpu
+dsa = pytest.importorskip("sparse_attention_lightning_amd")
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def seq_cache(data, table, b):
+    """Sequence b of a cache, in logical token order, on the host (input relayout only)."""
+    if data.dtype == torch.bfloat16:
+        data = data.view(torch.int16)
+    if table is None:
+        x = data[b:b + 1]
+    else:
+        x = data[table[b].long()].reshape(1, -1, data.shape[-1])
+    arr = x.cpu().numpy()
+    return oracle.Cache(arr.view(np.uint16) if arr.dtype == np.int16 else arr)
+
+
+def q_bits(t, b):
+    return t[b].view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_rows_wellformed(idx, wl, share_first=False):
+    """Every row: min(k, p+1) ascending positions <= p, then -1."""
+    idx = idx.cpu().numpy()
+    Qs = 1 if share_first else wl.Q
+    for b in range(wl.B):
+        for j in range(Qs):
+            p = wl.lens[b] - wl.Q + j
+            m = min(wl.k, p + 1)
+            row = idx[b, j]
+            assert np.all(row[m:] == -1)
+            assert np.all(np.diff(row[:m]) > 0) and row[0] >= 0 and row[m - 1] <= p
+
+
+def oracle_check_query(g, wl, b, j, scores_gpu, idx_gpu, outs, lses, share_first=False, layers=None):
+    """Oracle for one query token (b, j) of a full-size batch."""
+    layers = range(wl.n_layers) if layers is None else layers
+    p = wl.lens[b] - wl.Q + j
+    keys = seq_cache(g.keys, g.key_table, b)
+    qi = g.q_idx[b, j].cpu().numpy()
+    w = g.w[b, j].cpu().numpy()
+    exact = oracle.index_scores(qi, w, keys, 0, p, wl.lmax)
+    if scores_gpu is not None:
+        tol = score_tolerance(qi, w, keys.rows(0, np.arange(wl.lmax)))
+        check_scores(scores_gpu[b, j].cpu().numpy(), exact, tol, p)
+    o_idx = oracle.select_topk(exact.astype(np.float32), p, wl.k)
+    swaps = check_topk_sets(idx_gpu[b, 0 if share_first else j].cpu().numpy(), o_idx, exact, wl.k)
+    users = range(wl.Q) if share_first else [j]
+    worst = (0.0, 0.0)
+    for layer in layers:
+        lat = seq_cache(g.latent[layer], g.latent_table[layer], b)
+        qm = q_bits(g.q_mla[layer], b)
+        for u in users:
+            ref_o, ref_l = oracle.sparse_mla_one(qm[u], lat, 0, o_idx, wl.scale)
+            e = check_mla(outs[layer][b, u].cpu().numpy(), lses[layer][b, u].cpu().numpy(), ref_o, ref_l)
+            worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    print(f"  {wl.name} b={b} j={j}: {swaps} near-threshold swaps, out max abs {worst[0]:.3g} rel L2 {worst[1]:.3g}")
+    return swaps
+
+
+def run_path(g, wl, share_first=False):
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    q_pos = None
+    qi, wi = g.q_idx, g.w
+    if share_first:
+        q_pos = torch.tensor([[n - wl.Q] for n in wl.lens], dtype=torch.int32, device=DEV)
+        qi, wi = g.q_idx[:, :1].contiguous(), g.w[:, :1].contiguous()
+    scores = dsa.index_score(qi, wi, keys, g.seq_lens, wl.lmax, q_pos=q_pos)
+    idx = dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos)
+    outs, lses = [], []
+    for layer in range(wl.n_layers):
+        lat = dsa.Cache(g.latent[layer], g.latent_table[layer], wl.page_size)
+        o, l = dsa.sparse_mla_fwd(g.q_mla[layer], lat, idx, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                  idx_q_stride=0 if share_first else wl.k)
+        outs.append(o)
+        lses.append(l)
+    torch.cuda.synchronize()
+    return scores, idx, outs, lses
+
+
+def test_decode_b32_128k_paged():
+    wl = synth.WORKLOADS["decode_b32_128k_paged"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    scores, idx, outs, lses = run_path(g, wl)
+    check_rows_wellformed(idx, wl)
+    sets = idx.cpu().numpy()
+    for b in range(wl.B):                                   # planted tokens are selected in every sequence
+        assert set(g.planted_pos[b].tolist()) <= set(sets[b, 0].tolist())
+    s2, i2, o2, l2 = run_path(g, wl)                        # bitwise reproducible
+    assert torch.equal(scores, s2) and torch.equal(idx, i2) and torch.equal(outs[0], o2[0])
+    for b in (0, 17, 31):
+        oracle_check_query(g, wl, b, 0, scores, idx, outs, lses)
+
+
+def test_prefill_4096_at_128k():
+    wl = synth.WORKLOADS["prefill_4096_at_128k"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    scores, idx, outs, lses = run_path(g, wl)
+    check_rows_wellformed(idx, wl)
+    for j in (0, 1234, 4095):
+        oracle_check_query(g, wl, 0, j, scores, idx, outs, lses)
+
+
+def test_indexshare_b8_1m_4layers():
+    wl = synth.WORKLOADS["indexshare_b8_1m_4layers"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    lats = [dsa.Cache(g.latent[l], g.latent_table[l], wl.page_size) for l in range(4)]
+    idx, res = dsa.forward_shared(g.q_idx, g.w, keys, wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax)
+    torch.cuda.synchronize()
+    check_rows_wellformed(idx, wl)
+    # the group forward equals separate calls with one index set
+    scores, idx2, outs, lses = run_path(g, wl)
+    assert torch.equal(idx, idx2)
+    for layer in range(4):
+        assert torch.equal(res[layer][0], outs[layer]) and torch.equal(res[layer][1], lses[layer])
+    del res
+    oracle_check_query(g, wl, 3, 0, scores, idx, outs, lses)
+
+
+@pytest.mark.parametrize("name", ["verify_b64_q8_32k", "verify_b64_q8_32k_draftshare"])
+def test_verify_b64_q8_32k(name):
+    wl = synth.WORKLOADS[name]
+    share = bool(wl.share_first_query)
+    g = synth.generate(wl, seed=0, device=DEV)
+    scores, idx, outs, lses = run_path(g, wl, share_first=share)
+    check_rows_wellformed(idx, wl, share_first=share)
+    if share:
+        oracle_check_query(g, wl, 5, 0, scores, idx, outs, lses, share_first=True)
+    else:
+        for j in (0, 3, 7):
+            oracle_check_query(g, wl, 5, j, scores, idx, outs, lses)
