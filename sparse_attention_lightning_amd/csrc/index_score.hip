@@ -160,9 +160,197 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 #endif
 }
 
+// ------------------------------------------------------------------------------------------
+// Multi-query form (prefill chunks, speculative verify): the query tokens of one sequence share
+// every key, so a workgroup of NW waves x 2 query tokens stages each tile of 256 keys once in
+// LDS (direct-to-LDS loads into a 3-stage ring, rows XOR-swizzled by 16-byte chunk so the
+// 16 rows of one MFMA operand fetch hit distinct banks). Every B fragment read from LDS then
+// feeds 2 queries x Hi/16 FP8 matrix-core products, and the ReLU / weighted head sum runs in
+// registers as in the decode form. Keys after the last query's position are neither loaded
+// nor scored; scores after each query's own position are -inf.
+constexpr int kMqTile = 256;                         // keys per LDS tile
+constexpr int kMqStages = 3;
+constexpr int kMqTilesPerChunk = 16;                 // 4096 keys per workgroup
+constexpr int kMqChunk = kMqTile * kMqTilesPerChunk;
+constexpr int kMqDma = kMqTile / 8;                  // 1 KB direct-to-LDS loads per tile
+
+__device__ __forceinline__ int mq_off(int row, int chunk16) {   // chunk16 in 0..7 of a 128 B row
+  return row * 128 + 16 * (chunk16 ^ ((row >> 1) & 7));
+}
+
+template <int VM>
+__device__ __forceinline__ void mq_wait() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void mq_wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+template <int HI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ w, CacheView keys,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int n_qgroups, int n_chunks, float* __restrict__ scores) {
+  constexpr int MT = HI / 16;
+  constexpr int QG = 2 * NW;                          // query tokens per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kMqStages][kMqTile * kDi];
+  __shared__ int pmax_lds;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  // work item = (b, chunk, query group), query group fastest: groups sharing keys run together
+  const int item = blockIdx.x;
+  const int qg = item % n_qgroups;
+  const int rest = item / n_qgroups;
+  const int chunk = rest % n_chunks;
+  const int b = rest / n_chunks;
+  const int L_max = keys.L_max;
+  const int t0 = chunk * kMqChunk;
+  const int t1 = min(t0 + kMqChunk, L_max);
+
+  // this wave's two query tokens
+  int jq[2], pq[2];
+  bool live[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    jq[qi] = qg * QG + 2 * wave + qi;
+    live[qi] = jq[qi] < Q;
+    pq[qi] = live[qi] ? min(query_pos(seq_lens, q_pos, in_Q, b, jq[qi]), L_max - 1) : -1;
+  }
+  if (threadIdx.x == 0) pmax_lds = -1;
+  __syncthreads();
+  if (lane == 0) atomicMax(&pmax_lds, max(pq[0], pq[1]));
+  __syncthreads();
+  const int pmax = pmax_lds;                           // keys after it are never loaded
+  const int t_load_end = min(t1, pmax + 1);
+  const int n_tiles = t_load_end > t0 ? (t_load_end - t0 + kMqTile - 1) / kMqTile : 0;
+  const int my_dma = (kMqDma - wave + NW - 1) / NW;
+
+  // Direct-to-LDS load of tile tt: load d covers rows 8d..8d+7; lane l lands row 8d + l/8,
+  // slot l%8, fetching the 16-byte chunk that the swizzle puts there. Rows past the last
+  // visible key read a valid dummy row; their scores are masked.
+  auto issue_tile = [&](int tt) {
+    uint8_t* base = ring[tt % kMqStages];
+    for (int d = wave; d < kMqDma; d += NW) {
+      const int row = 8 * d + (lane >> 3);
+      const int t = t0 + tt * kMqTile + row;
+      const uint8_t* src = keys.base;
+      if (t <= pmax) src = keys.row(b, t);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c),
+                                       (__attribute__((address_space(3))) void*)(base + d * 1024), 16, 0, 0);
+    }
+  };
+
+  // query operands (A rows = heads 16m + c16) and weights of heads 16m + 4g + r
+  v8i qa[2][MT];
+  float wr[2][MT][4];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int jj = live[qi] ? jq[qi] : 0;
+    const uint8_t* qrow = q + ((int64_t)b * in_Q + jj) * HI * kDi;
+    const float* wrow = w + ((int64_t)b * in_Q + jj) * HI;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint8_t* hp = qrow + (16 * m + c16) * kDi;
+      const v4i lo4 = *(const v4i*)(hp + 16 * g), hi4 = *(const v4i*)(hp + 64 + 16 * g);
+      qa[qi][m] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wr[qi][m][r] = wrow[16 * m + 4 * g + r];
+    }
+  }
+  float* srow[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) srow[qi] = scores + ((int64_t)b * Q + (live[qi] ? jq[qi] : 0)) * L_max;
+
+  // scores of keys in this chunk that no tile covers (after pmax): -inf
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi)
+    if (live[qi])
+      for (int t = max(t0, t_load_end) + lane; t < t1; t += kWave) srow[qi][t] = -INFINITY;
+
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const int b_lo = mq_off(c16, g), b_hi = mq_off(c16, g + 4);   // per-lane fragment offsets in a 16-row group
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    if (tt + 1 < n_tiles) {
+      switch (my_dma) {
+        case 4: mq_wait<4>(); break;
+        case 8: mq_wait<8>(); break;
+        default: mq_wait<0>(); break;
+      }
+    } else {
+      mq_wait<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (tt + 2 < n_tiles) issue_tile(tt + 2);         // its slot was last read in tile tt - 1
+    const uint8_t* tile = ring[tt % kMqStages];
+    const int tb = t0 + tt * kMqTile;
+    // 4 blocks of 64 keys; each block: 4 groups of 16 keys, reduce-scatter, one store per query
+#pragma unroll 1
+    for (int blk = 0; blk < kMqTile / 64; ++blk) {
+      const int tk0 = tb + 64 * blk;
+      if (tk0 > pmax) break;                          // block-uniform
+      float part[2][4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint8_t* gp = tile + (64 * blk + 16 * c) * 128;   // 16-row group: the swizzle repeats every 16 rows
+        const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
+        const v8i bk = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          float sum = 0.f;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const v4f acc = mfma_fp8(qa[qi][m], bk, zero);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sum += wr[qi][m][r] * fmaxf(acc[r], 0.f);
+          }
+          part[qi][c] = sum;
+        }
+      }
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        const bool lo = g < 2;
+        const float r0 = shfl_xor(lo ? part[qi][2] : part[qi][0], 32);
+        const float r1 = shfl_xor(lo ? part[qi][3] : part[qi][1], 32);
+        const float x0 = (lo ? part[qi][0] : part[qi][2]) + r0;
+        const float x1 = (lo ? part[qi][1] : part[qi][3]) + r1;
+        const bool odd = g & 1;
+        const float r2 = shfl_xor(odd ? x0 : x1, 16);
+        const float v = (odd ? x1 : x0) + r2;
+        const int tk = tk0 + lane;
+        if (live[qi] && tk < t1) srow[qi][tk] = (tk <= pq[qi]) ? v : -INFINITY;
+      }
+    }
+    // keys of this tile after pmax (the loop broke early): -inf
+    for (int qi = 0; qi < 2; ++qi)
+      if (live[qi])
+        for (int t = max(tb, pmax + 1) + lane; t < min(tb + kMqTile, t1); t += kWave) srow[qi][t] = -INFINITY;
+  }
+}
+
+template <int HI, int NW>
+static void launch_multi(const HostBatch& bt, const uint8_t* q, const float* w, const CacheView& kv, float* scores,
+                         hipStream_t s) {
+  const int qgroups = (bt.Q + 2 * NW - 1) / (2 * NW);
+  const int n_chunks = (bt.L_max + kMqChunk - 1) / kMqChunk;
+  const dim3 grid((unsigned)bt.B * n_chunks * qgroups), block(NW * 64);
+  hipLaunchKernelGGL((index_score_multi_kernel<HI, NW>), grid, block, 0, s, q, w, kv, bt.seq_lens, bt.q_pos, bt.Q,
+                     bt.in_Q, qgroups, n_chunks, scores);
+}
+
 hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float* w, int Hi,
                               const HostCache& keys, float* scores, hipStream_t s) {
   CacheView kv{(const uint8_t*)keys.base, keys.table, keys.max_pages, keys.page_size, kDi, bt.L_max};
+  if (bt.Q >= 2) {
+    if (Hi == 64) {
+      if (bt.Q > 8) launch_multi<64, 8>(bt, q, w, kv, scores, s);
+      else launch_multi<64, 4>(bt, q, w, kv, scores, s);
+    } else {
+      if (bt.Q > 8) launch_multi<32, 8>(bt, q, w, kv, scores, s);
+      else launch_multi<32, 4>(bt, q, w, kv, scores, s);
+    }
+    return hipGetLastError();
+  }
   const int n_chunks = (bt.L_max + kScoreChunk - 1) / kScoreChunk;
   const int n_items = bt.B * bt.Q * n_chunks;
   dim3 grid(n_items), block(256);

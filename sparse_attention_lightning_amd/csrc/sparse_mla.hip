@@ -21,17 +21,14 @@
 
 namespace dsa {
 
-constexpr int kMlaThreads = 256;
-constexpr int kHeadsPerWg = 64;
-constexpr int kTok = 32;                       // tokens per step
-constexpr int kRowBytes = kDqk * 2;            // 1152
-constexpr int kPitch = kRowBytes + 16;         // padded LDS row: 16 consecutive rows hit distinct banks
-constexpr int kRowChunks = kRowBytes / 16;     // 72 16-byte chunks per row
-constexpr int kStepChunks = kTok * kRowChunks; // 2304
-constexpr int kChunksPerThread = kStepChunks / kMlaThreads;  // 9
-static_assert(kStepChunks % kMlaThreads == 0, "even gather split");
+constexpr int kTok = 32;                        // tokens per step
+constexpr int kRowBytes = kDqk * 2;             // 1152
+constexpr int kSegs = kRowBytes / 128;          // 9 segments of 128 B per row
+constexpr int kTileBytes = kTok * kRowBytes;    // 36 KB per step
+constexpr int kStages = 3;                      // LDS ring depth: rows land two steps ahead
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.f;             // rescale O only when a head's max grows by > 2^8
 
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
@@ -41,10 +38,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 #endif
 
 int sparse_mla_splits(int rows, int H, int k) {
-  const int wgs = rows * (H / kHeadsPerWg);
+  (void)H;
   int s = 1;
-  // aim for enough workgroups to fill the chip while each split keeps a minimum of tokens
-  while (wgs * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < 16) s *= 2;
+  // enough workgroups to fill the chip while each split keeps a minimum of tokens
+  while (rows * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < 16) s *= 2;
   return s;
 }
 
@@ -56,52 +53,67 @@ size_t sparse_mla_workspace_bytes(int rows, int H, int k) {
   return align256((size_t)rows * s * H * kDv * sizeof(float)) + align256((size_t)rows * s * H * sizeof(float));
 }
 
-__device__ __forceinline__ v8bf load_v8bf(const void* p) { return *(const v8bf*)p; }
+__device__ __forceinline__ v8bf lds_v8bf(const uint8_t* p) { return *(const v8bf*)p; }
 
 __device__ __forceinline__ v4bf lds_tr_read(const uint8_t* lds_byte_ptr) {
   typedef __attribute__((address_space(3))) v4bf lds_v4bf;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(lds_byte_ptr));
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
+// LDS tile layout of one step: 9 segments of [32 rows][128 B]; inside a row segment the eight
+// 16-byte chunks are XOR-swizzled by ((row >> 1) & 7), so the 16 rows read by one MFMA
+// operand fetch land on 16 distinct bank groups.
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return (chunk >> 3) * (kTok * 128) + row * 128 + 16 * ((chunk & 7) ^ ((row >> 1) & 7));
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt
+// [11:8]): wait until at most VM vector memory operations and LGKM LDS/scalar operations of
+// this wave are outstanding. VM = 63 / LGKM = 15 mean "no wait" on that counter.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Wait until this wave's direct-to-LDS loads of one step have landed while `pending` loads
+// (the next step's) may still be in flight.
+__device__ __forceinline__ void wait_step(int pending) {
+  switch (pending) {
+    case 0: wait_counts<0, 15>(); break;
+    case 4: wait_counts<4, 15>(); break;
+    case 5: wait_counts<5, 15>(); break;
+    case 9: wait_counts<9, 15>(); break;
+    default: wait_counts<0, 15>(); break;
+  }
+}
+
+template <int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, CacheView lat, const int32_t* __restrict__ idx, int k, int idx_q_stride,
     int Q, int H, int splits, int split_len, float scale_log2,
     float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTok * kPitch];
-  __shared__ int vflag[kTok];
+  constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kTileBytes];
   __shared__ int rowid[kMaxK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int hgroups = H / kHeadsPerWg;
-  int item = blockIdx.x;
-  const int split = item % splits; item /= splits;
-  const int hg = item % hgroups;
-  const int bq = item / hgroups;
+  const int split = blockIdx.x % splits;
+  const int bq = blockIdx.x / splits;
   const int b = bq / Q, j = bq - b * Q;
-  const int h0 = hg * kHeadsPerWg + wave * 16;          // this wave's first head
+  const int h0 = wave * 16;                            // this wave's 16 heads
+  const int my_dma = (kDmaPerStep - wave + NW - 1) / NW;   // loads this wave issues per step
 
   const int32_t* irow = idx + (int64_t)b * (idx_q_stride ? (int64_t)Q * k : k) + (int64_t)j * idx_q_stride;
   const int tok_begin = split * split_len;
   const int tok_end = min(k, tok_begin + split_len);
+  const int n_steps = tok_end > tok_begin ? (tok_end - tok_begin + kTok - 1) / kTok : 0;
 
-  // query heads h0 + (l % 16) as the B operand of S^T = K . Q^T: 8 dims per lane per K step
-  v8bf qb[kDqk / 32];
-  const uint16_t* qrow = q + ((int64_t)bq * H + h0 + c16) * kDqk;
-#pragma unroll
-  for (int s = 0; s < kDqk / 32; ++s) qb[s] = load_v8bf(qrow + 32 * s + 8 * g);
-
-  v4f o[kDv / 16];
-#pragma unroll
-  for (int nt = 0; nt < kDv / 16; ++nt) o[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max (log2 domain) of head c16
-  float l_run = 0.f;         // this lane's share of the softmax denominator
-
-  // Row index (into the cache's rows) of every token of this split, resolved once through the
-  // index list and the block table; -1 for masked tokens (index -1 or past k).
-  for (int i = tid; i < tok_end - tok_begin; i += kMlaThreads) {
-    const int pos = irow[tok_begin + i];
+  // row index (into the cache's rows) of every token of the split, -1 for masked tokens
+  for (int i = tid; i < n_steps * kTok; i += NW * 64) {
+    const int t = tok_begin + i;
+    const int pos = t < tok_end ? irow[t] : -1;
     int r = -1;
     if (pos >= 0)
       r = lat.table ? lat.table[(int64_t)b * lat.max_pages + pos / lat.page_size] * lat.page_size + pos % lat.page_size
@@ -109,68 +121,92 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
     rowid[i] = r;
   }
   __syncthreads();
-  // Gather: 8 threads per row (32 rows per step), thread (row tid/8, part) loads the 16-byte
-  // chunks part + 8i, i < 9, of its row; rows are loaded one step before they are used.
-  // Masked rows read a valid dummy row and are zeroed in LDS.
-  const int grow = tid >> 3, gpart = tid & 7;
-  auto row_of = [&](int tok0) -> int {
-    const int i = tok0 - tok_begin + grow;
-    return (tok0 + grow < tok_end) ? rowid[i] : -1;
-  };
-  v4i stage[kChunksPerThread];
-  auto load_rows = [&](int r) {
-    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0);
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) stage[i] = *(const v4i*)(src + 16 * (gpart + 8 * i));
-  };
-  int r_cur = row_of(tok_begin);
-  load_rows(r_cur);
-  for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTok) {
-    __syncthreads();                           // previous step done with the tile
-    const bool row_ok = r_cur >= 0;
-    uint8_t* dst = tile + grow * kPitch + 16 * gpart;
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i)
-      *(v4i*)(dst + 128 * i) = row_ok ? stage[i] : (v4i){0, 0, 0, 0};
-    if (gpart == 0) vflag[grow] = row_ok;
-    __syncthreads();
-    if (tok0 + kTok < tok_end) {               // block-uniform
-      r_cur = row_of(tok0 + kTok);
-      load_rows(r_cur);
-    }
 
-    // ---- S^T = K_tile . Q^T : two 16-token tiles
-    // four independent accumulator chains (2 token tiles x 2 halves of K) keep the matrix
-    // pipe busy with one wave per SIMD
-    v4f sacc[2], sacc2[2];
+  // Direct-to-LDS gather of step st: load d = (row group rg = d % 4, segment d / 4) lands rows
+  // 8rg + l/8, slot l%8 of the segment, fetching the chunk that the swizzle puts there.
+  // Loads are dealt round-robin over the waves.
+  auto issue_step = [&](int st) {
+    uint8_t* base = ring[st % kStages];
+    for (int d = wave; d < kDmaPerStep; d += NW) {
+      const int rg = d & 3, sg = d >> 2;
+      const int row = 8 * rg + (lane >> 3);
+      const int r = rowid[st * kTok + row];
+      const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0);
+      const int chunk = 8 * sg + ((lane & 7) ^ ((row >> 1) & 7));
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * chunk),
+                                       (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128) + rg * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // masked rows this wave landed: overwrite the dummy bytes with zeros
+  auto zero_masked = [&](int st) {
+    uint8_t* base = ring[st % kStages];
+    for (int d = wave; d < kDmaPerStep; d += NW) {
+      const int rg = d & 3, sg = d >> 2;
+      const int row = 8 * rg + (lane >> 3);
+      if (rowid[st * kTok + row] < 0) *(v4i*)(base + sg * (kTok * 128) + rg * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
+    }
+  };
+
+  // query heads h0 + (l % 16) as the B operand of S^T = K . Q^T: 8 dims per lane per K step
+  v8bf qb[kDqk / 32];
+  const uint16_t* qrow = q + ((int64_t)bq * H + h0 + c16) * kDqk;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sacc[mt] = sacc2[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kDqk / 32; ++s) qb[s] = *(const v8bf*)(qrow + 32 * s + 8 * g);
+  v4f o[kDv / 16];
 #pragma unroll
-    for (int s = 0; s < kDqk / 64; ++s)
+  for (int nt = 0; nt < kDv / 16; ++nt) o[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // reference max (log2 domain) of head h0 + c16
+  float l_run = 0.f;         // this lane's share of its softmax denominator
+
+  // Per-lane LDS offsets inside a tile. Chunk c of row r sits at segment c/8, slot
+  // (c & 7) ^ ((r >> 1) & 7); for the fragments below the slot varies only in bits the XOR
+  // immediates flip, so one base per row serves all of them:
+  //   QK (token 16mt + c16, chunk 4s + g):   (qk_base[mt] ^ 64 (s & 1)) + (s / 2) * 4096
+  //   PV (token row vrow_hf, dims 16nt..):   (pv_base[hf] ^ 32 (nt & 3)) + (nt / 4) * 4096
+  int qk_base[2], pv_base[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const uint8_t* arow = tile + (16 * mt + c16) * kPitch + 16 * g;
-        sacc[mt] = mfma_bf16(load_v8bf(arow + 64 * s), qb[s], sacc[mt]);
-        sacc2[mt] = mfma_bf16(load_v8bf(arow + 64 * (s + kDqk / 64)), qb[s + kDqk / 64], sacc2[mt]);
-      }
+  for (int mt = 0; mt < 2; ++mt) qk_base[mt] = tile_off(16 * mt + c16, g);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sacc[mt] += sacc2[mt];
-    // ---- online softmax for head c16 over tokens 16mt + 4g + r
+  for (int hf = 0; hf < 2; ++hf)
+    pv_base[hf] = tile_off(4 * g + (c16 >> 2) + 16 * hf, (c16 & 3) >> 1) + 8 * (c16 & 1);
+
+  if (n_steps > 0) issue_step(0);
+  if (n_steps > 1) issue_step(1);
+  for (int st = 0; st < n_steps; ++st) {
+    wait_step(st + 1 < n_steps ? my_dma : 0);       // this step's rows have landed
+    zero_masked(st);
+    wait_counts<63, 0>();                            // LDS writes done before the barrier
+    __builtin_amdgcn_s_barrier();
+    if (st + 2 < n_steps) issue_step(st + 2);        // its slot was last read in step st - 1
+    const uint8_t* tile = ring[st % kStages];
+
+    // ---- S^T = K_tile . Q^T over K = 576
+    v4f sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sacc[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = mfma_bf16(lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s & 1))) + (s >> 1) * (kTok * 128))), qb[s], sacc[mt]);
+    // ---- online softmax of head h0 + c16 over tokens 16mt + 4g + r
     float z[2][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = vflag[16 * mt + 4 * g + r];
+        const bool ok = rowid[st * kTok + 16 * mt + 4 * g + r] >= 0;
         z[mt][r] = ok ? sacc[mt][r] * scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, z[mt][r]);
       }
     tmax = fmaxf(tmax, shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // lazy reference max: exp2(z - m_ref) stays <= 2^8, exact enough in fp32 / bf16
+    const float m_ref = (tmax > m_run + kLazyRescale) ? tmax : m_run;
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    const float alpha = (m_run == -INFINITY) ? 1.f : exp2f(m_run - m_use);   // O is still 0 at -inf
     float psum = 0.f;
     v8bf pa;
 #pragma unroll
@@ -182,9 +218,8 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
         pa[4 * mt + r] = (__bf16)pv;
       }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // ---- rescale O: this lane's accumulators hold heads 4g + r
-    if (__ballot(alpha != 1.f) != 0ull) {      // wave-uniform: skip when no head's max moved
+    m_run = m_ref;
+    if (__ballot(alpha != 1.f) != 0ull) {       // wave-uniform and rare: a head's max jumped by > 2^8
       float al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
@@ -193,19 +228,17 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
     }
-    // ---- O += P . V, V^T fragments by transpose reads: tokens 4g+e (e<4), 16+4g+(e-4) (e>=4)
-    const uint8_t* v0 = tile + (4 * g + (c16 >> 2)) * kPitch + 8 * (c16 & 3);
-    const uint8_t* v1 = v0 + 16 * kPitch;
+    // ---- O += P . V; V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4)
 #pragma unroll
     for (int nt = 0; nt < kDv / 16; ++nt) {
-      const v4bf lo = lds_tr_read(v0 + 32 * nt);
-      const v4bf hi = lds_tr_read(v1 + 32 * nt);
+      const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
+      const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
       const v8bf vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[nt] = mfma_bf16(pa, vb, o[nt]);
     }
   }
 
-  // ---- finish: denominator of head c16, then per accumulator head 4g + r
+  // ---- finish: denominator of head h0 + c16, then per accumulator head h0 + 4g + r
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
   const float lse_h = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -255,6 +288,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   if (t == 0 && lse_out) lse_out[(int64_t)bq * H + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(den);
 }
 
+template <int NW>
+static void launch_mla(int splits, dim3 grid, hipStream_t s, const uint16_t* q, CacheView lv, const int32_t* idx,
+                       int k, int idx_q_stride, int Q, int H, int split_len, float sl2, float* out, float* lse,
+                       float* part_o, float* part_lse) {
+  const dim3 block(NW * 64);
+  if (splits == 1)
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, false>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, 1,
+                       split_len, sl2, out, lse, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, true>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, splits,
+                       split_len, sl2, nullptr, nullptr, part_o, part_lse);
+}
+
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out, float* lse,
                              void* ws, hipStream_t s) {
@@ -263,19 +309,21 @@ hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, cons
   const int splits = sparse_mla_splits(rows, H, k);
   int split_len = (k + splits - 1) / splits;
   split_len = (split_len + kTok - 1) / kTok * kTok;
-  const dim3 grid((unsigned)rows * (H / kHeadsPerWg) * splits), block(kMlaThreads);
+  const dim3 grid((unsigned)rows * splits);
   const float sl2 = scale * kLog2e;
-  if (splits == 1) {
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, block, 0, s, q, lv, idx, k, idx_q_stride, bt.Q, H, 1,
-                       split_len, sl2, out, lse, nullptr, nullptr);
-    return hipGetLastError();
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (splits > 1) {
+    part_o = (float*)ws;
+    part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(float)));
   }
-  float* part_o = (float*)ws;
-  float* part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(float)));
-  hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, block, 0, s, q, lv, idx, k, idx_q_stride, bt.Q, H, splits,
-                     split_len, sl2, nullptr, nullptr, part_o, part_lse);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2)), dim3(256), 0, s, part_o, part_lse, H,
-                     splits, out, lse);
+  if (H == 128)
+    launch_mla<8>(splits, grid, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o, part_lse);
+  else
+    launch_mla<4>(splits, grid, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o, part_lse);
+  if (splits > 1)
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2)), dim3(256), 0, s, part_o, part_lse, H,
+                       splits, out, lse);
   return hipGetLastError();
 }
 
