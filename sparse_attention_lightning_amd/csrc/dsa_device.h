@@ -52,6 +52,11 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// max(x, 0) as one integer max on the bit pattern: every negative float (sign bit set) is a
+// negative int32 and maps to +0; non-negative floats are unchanged. Unlike fmaxf it needs no
+// NaN-quieting instruction in front.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Order-preserving map of an IEEE float to uint32 (larger float -> larger key); -0 -> +0.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
       for (int m = 0; m < MT; ++m) {
         const v4f acc = mfma_fp8(qa[m], bk, zero);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s += wr[m][r] * fmaxf(acc[r], 0.f);
+        for (int r = 0; r < 4; ++r) s += wr[m][r] * relu(acc[r]);
       }
       part[c] = s;
     }
@@ -168,10 +168,16 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 // feeds 2 queries x Hi/16 FP8 matrix-core products, and the ReLU / weighted head sum runs in
 // registers as in the decode form. Keys after the last query's position are neither loaded
 // nor scored; scores after each query's own position are -inf.
-constexpr int kMqTile = 256;                         // keys per LDS tile
-constexpr int kMqStages = 3;
-constexpr int kMqTilesPerChunk = 16;                 // 4096 keys per workgroup
-constexpr int kMqChunk = kMqTile * kMqTilesPerChunk;
+#ifndef DSA_MQ_TILE
+#define DSA_MQ_TILE 256
+#endif
+#ifndef DSA_MQ_STAGES
+#define DSA_MQ_STAGES 2
+#endif
+constexpr int kMqTile = DSA_MQ_TILE;                 // keys per LDS tile
+constexpr int kMqStages = DSA_MQ_STAGES;
+constexpr int kMqChunk = 4096;                       // keys per workgroup
+constexpr int kMqTilesPerChunk = kMqChunk / kMqTile;
 constexpr int kMqDma = kMqTile / 8;                  // 1 KB direct-to-LDS loads per tile
 
 __device__ __forceinline__ int mq_off(int row, int chunk16) {   // chunk16 in 0..7 of a 128 B row
@@ -184,13 +190,20 @@ __device__ __forceinline__ void mq_wait() {
 }
 __device__ __forceinline__ void mq_wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-template <int HI, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
+#ifndef DSA_MQ_QPW
+#define DSA_MQ_QPW 1
+#endif
+#ifndef DSA_MQ_WAVES
+#define DSA_MQ_WAVES 8
+#endif
+
+template <int HI, int NW, int QPW>
+__global__ __launch_bounds__(NW * 64) void index_score_multi_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, CacheView keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int n_qgroups, int n_chunks, float* __restrict__ scores) {
   constexpr int MT = HI / 16;
-  constexpr int QG = 2 * NW;                          // query tokens per workgroup
+  constexpr int QG = QPW * NW;                        // query tokens per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kMqStages][kMqTile * kDi];
   __shared__ int pmax_lds;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -205,18 +218,21 @@ __global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
   const int t0 = chunk * kMqChunk;
   const int t1 = min(t0 + kMqChunk, L_max);
 
-  // this wave's two query tokens
-  int jq[2], pq[2];
-  bool live[2];
+  // this wave's query tokens
+  int jq[QPW], pq[QPW];
+  bool live[QPW];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    jq[qi] = qg * QG + 2 * wave + qi;
+  for (int qi = 0; qi < QPW; ++qi) {
+    jq[qi] = qg * QG + QPW * wave + qi;
     live[qi] = jq[qi] < Q;
     pq[qi] = live[qi] ? min(query_pos(seq_lens, q_pos, in_Q, b, jq[qi]), L_max - 1) : -1;
   }
   if (threadIdx.x == 0) pmax_lds = -1;
   __syncthreads();
-  if (lane == 0) atomicMax(&pmax_lds, max(pq[0], pq[1]));
+  int pw = -1;
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) pw = max(pw, pq[qi]);
+  if (lane == 0) atomicMax(&pmax_lds, pw);
   __syncthreads();
   const int pmax = pmax_lds;                           // keys after it are never loaded
   const int t_load_end = min(t1, pmax + 1);
@@ -240,10 +256,10 @@ __global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
   };
 
   // query operands (A rows = heads 16m + c16) and weights of heads 16m + 4g + r
-  v8i qa[2][MT];
-  float wr[2][MT][4];
+  v8i qa[QPW][MT];
+  float wr[QPW][MT][4];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < QPW; ++qi) {
     const int jj = live[qi] ? jq[qi] : 0;
     const uint8_t* qrow = q + ((int64_t)b * in_Q + jj) * HI * kDi;
     const float* wrow = w + ((int64_t)b * in_Q + jj) * HI;
@@ -256,32 +272,37 @@ __global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
       for (int r = 0; r < 4; ++r) wr[qi][m][r] = wrow[16 * m + 4 * g + r];
     }
   }
-  float* srow[2];
+  float* srow[QPW];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) srow[qi] = scores + ((int64_t)b * Q + (live[qi] ? jq[qi] : 0)) * L_max;
+  for (int qi = 0; qi < QPW; ++qi) srow[qi] = scores + ((int64_t)b * Q + (live[qi] ? jq[qi] : 0)) * L_max;
 
   // scores of keys in this chunk that no tile covers (after pmax): -inf
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi)
+  for (int qi = 0; qi < QPW; ++qi)
     if (live[qi])
       for (int t = max(t0, t_load_end) + lane; t < t1; t += kWave) srow[qi][t] = -INFINITY;
 
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  // prefetch distance: kMqStages - 1 tiles are in flight while one is computed
+  constexpr int kAhead = kMqStages - 1;
+  static_assert(kAhead >= 1, "at least two stages");
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a)
+    if (a < n_tiles) issue_tile(a);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const int b_lo = mq_off(c16, g), b_hi = mq_off(c16, g + 4);   // per-lane fragment offsets in a 16-row group
   for (int tt = 0; tt < n_tiles; ++tt) {
-    if (tt + 1 < n_tiles) {
-      switch (my_dma) {
-        case 4: mq_wait<4>(); break;
-        case 8: mq_wait<8>(); break;
-        default: mq_wait<0>(); break;
-      }
-    } else {
-      mq_wait<0>();
+    // tile tt has landed once only the later tiles' loads (at most kAhead - 1 tiles) are in flight
+    const int later = min(kAhead - 1, n_tiles - 1 - tt) * my_dma;
+    switch (later) {
+      case 2: mq_wait<2>(); break;
+      case 4: mq_wait<4>(); break;
+      case 8: mq_wait<8>(); break;
+      case 16: mq_wait<16>(); break;
+      default: mq_wait<0>(); break;
     }
     __builtin_amdgcn_s_barrier();
-    if (tt + 2 < n_tiles) issue_tile(tt + 2);         // its slot was last read in tile tt - 1
+    // the slot of tile tt + kAhead was last read in tile tt - 1, which every wave has finished
+    if (tt + kAhead < n_tiles) issue_tile(tt + kAhead);
     const uint8_t* tile = ring[tt % kMqStages];
     const int tb = t0 + tt * kMqTile;
     // 4 blocks of 64 keys; each block: 4 groups of 16 keys, reduce-scatter, one store per query
@@ -289,26 +310,35 @@ __global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
     for (int blk = 0; blk < kMqTile / 64; ++blk) {
       const int tk0 = tb + 64 * blk;
       if (tk0 > pmax) break;                          // block-uniform
-      float part[2][4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      // matrix-core products of group c+1 are issued before the epilogue of group c consumes
+      // its results, so the FP8 pipe and the ReLU / FMA epilogue overlap within the wave
+      float part[QPW][4];
+      v4f acc[2][QPW][MT];
+      auto products = [&](int c, v4f (&a)[QPW][MT]) {
         const uint8_t* gp = tile + (64 * blk + 16 * c) * 128;   // 16-row group: the swizzle repeats every 16 rows
         const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
         const v8i bk = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
-        for (int qi = 0; qi < 2; ++qi) {
+        for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) a[qi][m] = mfma_fp8(qa[qi][m], bk, zero);
+      };
+      products(0, acc[0]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c + 1 < 4) products(c + 1, acc[(c + 1) & 1]);
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) {
           float sum = 0.f;
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const v4f acc = mfma_fp8(qa[qi][m], bk, zero);
+          for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sum += wr[qi][m][r] * fmaxf(acc[r], 0.f);
-          }
+            for (int r = 0; r < 4; ++r) sum += wr[qi][m][r] * relu(acc[c & 1][qi][m][r]);
           part[qi][c] = sum;
         }
       }
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
+      for (int qi = 0; qi < QPW; ++qi) {
         const bool lo = g < 2;
         const float r0 = shfl_xor(lo ? part[qi][2] : part[qi][0], 32);
         const float r1 = shfl_xor(lo ? part[qi][3] : part[qi][1], 32);
@@ -322,32 +352,33 @@ __global__ __launch_bounds__(NW * 64, 1) void index_score_multi_kernel(
       }
     }
     // keys of this tile after pmax (the loop broke early): -inf
-    for (int qi = 0; qi < 2; ++qi)
+    for (int qi = 0; qi < QPW; ++qi)
       if (live[qi])
         for (int t = max(tb, pmax + 1) + lane; t < min(tb + kMqTile, t1); t += kWave) srow[qi][t] = -INFINITY;
   }
 }
 
-template <int HI, int NW>
+template <int HI, int NW, int QPW>
 static void launch_multi(const HostBatch& bt, const uint8_t* q, const float* w, const CacheView& kv, float* scores,
                          hipStream_t s) {
-  const int qgroups = (bt.Q + 2 * NW - 1) / (2 * NW);
+  const int qgroups = (bt.Q + QPW * NW - 1) / (QPW * NW);
   const int n_chunks = (bt.L_max + kMqChunk - 1) / kMqChunk;
   const dim3 grid((unsigned)bt.B * n_chunks * qgroups), block(NW * 64);
-  hipLaunchKernelGGL((index_score_multi_kernel<HI, NW>), grid, block, 0, s, q, w, kv, bt.seq_lens, bt.q_pos, bt.Q,
-                     bt.in_Q, qgroups, n_chunks, scores);
+  hipLaunchKernelGGL((index_score_multi_kernel<HI, NW, QPW>), grid, block, 0, s, q, w, kv, bt.seq_lens, bt.q_pos,
+                     bt.Q, bt.in_Q, qgroups, n_chunks, scores);
 }
 
 hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float* w, int Hi,
                               const HostCache& keys, float* scores, hipStream_t s) {
   CacheView kv{(const uint8_t*)keys.base, keys.table, keys.max_pages, keys.page_size, kDi, bt.L_max};
   if (bt.Q >= 2) {
+    // up to 8 query tokens: one per wave of an 8-wave workgroup; more: DSA_MQ_QPW per wave
     if (Hi == 64) {
-      if (bt.Q > 8) launch_multi<64, 8>(bt, q, w, kv, scores, s);
-      else launch_multi<64, 4>(bt, q, w, kv, scores, s);
+      if (bt.Q > 8) launch_multi<64, DSA_MQ_WAVES, DSA_MQ_QPW>(bt, q, w, kv, scores, s);
+      else launch_multi<64, 8, 1>(bt, q, w, kv, scores, s);
     } else {
-      if (bt.Q > 8) launch_multi<32, 8>(bt, q, w, kv, scores, s);
-      else launch_multi<32, 4>(bt, q, w, kv, scores, s);
+      if (bt.Q > 8) launch_multi<32, DSA_MQ_WAVES, DSA_MQ_QPW>(bt, q, w, kv, scores, s);
+      else launch_multi<32, 8, 1>(bt, q, w, kv, scores, s);
     }
     return hipGetLastError();
   }
