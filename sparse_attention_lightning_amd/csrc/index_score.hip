@@ -14,10 +14,13 @@
 namespace dsa {
 
 #ifndef DSA_SCORE_CHUNK
-#define DSA_SCORE_CHUNK 1024
+#define DSA_SCORE_CHUNK 2048
 #endif
 #ifndef DSA_SCORE_PIPE
 #define DSA_SCORE_PIPE 0
+#endif
+#ifndef DSA_SCORE_NT
+#define DSA_SCORE_NT 0
 #endif
 constexpr int kScoreChunk = DSA_SCORE_CHUNK;   // keys per workgroup (4 waves)
 constexpr int kScoreWaveKeys = kScoreChunk / 4;
@@ -103,8 +106,13 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
       const int tk = t + 16 * c + c16;     // this lane's key (B column)
       if (t + 16 * c <= p && t + 16 * c < t_end) {
         const uint8_t* rowp = group_row(t + 16 * c) + (int64_t)c16 * kDi;  // 16 keys share a page
+#if DSA_SCORE_NT
+        kb[c][0] = tk <= p ? __builtin_nontemporal_load((const v4i*)(rowp + 16 * g)) : (v4i){0, 0, 0, 0};
+        kb[c][1] = tk <= p ? __builtin_nontemporal_load((const v4i*)(rowp + 64 + 16 * g)) : (v4i){0, 0, 0, 0};
+#else
         kb[c][0] = tk <= p ? *(const v4i*)(rowp + 16 * g) : (v4i){0, 0, 0, 0};
         kb[c][1] = tk <= p ? *(const v4i*)(rowp + 64 + 16 * g) : (v4i){0, 0, 0, 0};
+#endif
       } else {
         kb[c][0] = (v4i){0, 0, 0, 0};
         kb[c][1] = (v4i){0, 0, 0, 0};

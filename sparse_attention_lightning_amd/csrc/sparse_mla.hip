@@ -185,11 +185,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     v4f sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) sacc[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+    {
+      // fragment i = (s = i / 2, mt = i % 2); the next fragment is read before the current product
+      auto kfrag = [&](int i) {
+        const int s2 = i >> 1, mt = i & 1;
+        return lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s2 & 1))) + (s2 >> 1) * (kTok * 128)));
+      };
+      v8bf cur = kfrag(0);
 #pragma unroll
-    for (int s = 0; s < kDqk / 32; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = mfma_bf16(lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s & 1))) + (s >> 1) * (kTok * 128))), qb[s], sacc[mt]);
+      for (int i = 0; i < 2 * (kDqk / 32); ++i) {
+        v8bf nxt;
+        if (i + 1 < 2 * (kDqk / 32)) nxt = kfrag(i + 1);
+        sacc[i & 1] = mfma_bf16(cur, qb[i >> 1], sacc[i & 1]);
+        cur = nxt;
+      }
+    }
     // ---- online softmax of head h0 + c16 over tokens 16mt + 4g + r
     float z[2][4];
     float tmax = -INFINITY;
@@ -206,14 +216,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     // lazy reference max: exp2(z - m_ref) stays <= 2^8, exact enough in fp32 / bf16
     const float m_ref = (tmax > m_run + kLazyRescale) ? tmax : m_run;
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    const float alpha = (m_run == -INFINITY) ? 1.f : exp2f(m_run - m_use);   // O is still 0 at -inf
+    // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless for softmax weights
+    const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);   // O is 0 at -inf
     float psum = 0.f;
     v8bf pa;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = exp2f(z[mt][r] - m_use);
+        const float pv = __builtin_amdgcn_exp2f(z[mt][r] - m_use);
         psum += pv;
         pa[4 * mt + r] = (__bf16)pv;
       }
@@ -229,12 +240,20 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
     }
     // ---- O += P . V; V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4)
+    {
+      auto vfrag = [&](int nt) {
+        const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
+        const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
+        return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      v8bf cur = vfrag(0);
 #pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt) {
-      const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-      const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-      const v8bf vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[nt] = mfma_bf16(pa, vb, o[nt]);
+      for (int nt = 0; nt < kDv / 16; ++nt) {
+        v8bf nxt;
+        if (nt + 1 < kDv / 16) nxt = vfrag(nt + 1);
+        o[nt] = mfma_bf16(pa, cur, o[nt]);
+        cur = nxt;
+      }
     }
   }
 
