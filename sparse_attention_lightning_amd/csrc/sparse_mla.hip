@@ -30,6 +30,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.f;             // rescale O only when a head's max grows by > 2^8
 
+#ifndef DSA_MLA_PART_BF16
+#define DSA_MLA_PART_BF16 1
+#endif
+// Split partials: normalised outputs o_s (|o_s| <= the largest value entry, a convex
+// combination) stored as bf16 to halve their traffic, plus fp32 lse_s.
+#if DSA_MLA_PART_BF16
+typedef __bf16 part_t;
+#else
+typedef float part_t;
+#endif
+
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
 #endif
@@ -50,7 +61,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t sparse_mla_workspace_bytes(int rows, int H, int k) {
   const int s = sparse_mla_splits(rows, H, k);
   if (s == 1) return 0;
-  return align256((size_t)rows * s * H * kDv * sizeof(float)) + align256((size_t)rows * s * H * sizeof(float));
+  return align256((size_t)rows * s * H * kDv * sizeof(part_t)) + align256((size_t)rows * s * H * sizeof(float));
 }
 
 __device__ __forceinline__ v8bf lds_v8bf(const uint8_t* p) { return *(const v8bf*)p; }
@@ -92,7 +103,7 @@ template <int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, CacheView lat, const int32_t* __restrict__ idx, int k, int idx_q_stride,
     int Q, int H, int splits, int split_len, float scale_log2,
-    float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ out, float* __restrict__ lse_out, part_t* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kTileBytes];
   __shared__ int rowid[kMaxK];
@@ -267,23 +278,26 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const float lr = __shfl(l_tot, 4 * g + r, 64);
     inv[r] = lr > 0.f ? 1.f / lr : 0.f;
   }
-  float* obase;
   if (SPLIT) {
     const int64_t ps = (int64_t)bq * splits + split;
-    obase = part_o + (ps * H + h0) * kDv;
+    part_t* pbase = part_o + (ps * H + h0) * kDv;
     if (g == 0) part_lse[ps * H + h0 + c16] = lse_h;
+#pragma unroll
+    for (int nt = 0; nt < kDv / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pbase[(4 * g + r) * kDv + 16 * nt + c16] = (part_t)(o[nt][r] * inv[r]);
   } else {
-    obase = out + ((int64_t)bq * H + h0) * kDv;
+    float* obase = out + ((int64_t)bq * H + h0) * kDv;
     if (g == 0 && lse_out) lse_out[(int64_t)bq * H + h0 + c16] = lse_h;
+#pragma unroll
+    for (int nt = 0; nt < kDv / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) obase[(4 * g + r) * kDv + 16 * nt + c16] = o[nt][r] * inv[r];
   }
-#pragma unroll
-  for (int nt = 0; nt < kDv / 16; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) obase[(4 * g + r) * kDv + 16 * nt + c16] = o[nt][r] * inv[r];
 }
 
 // Merge split partials: one workgroup per (query token, 2 heads), 128 threads x 4 dims per head.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void mla_combine_kernel(const part_t* __restrict__ part_o,
                                                           const float* __restrict__ part_lse, int H, int splits,
                                                           float* __restrict__ out, float* __restrict__ lse_out) {
   const int hl = threadIdx.x >> 7, t = threadIdx.x & 127;
@@ -298,8 +312,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
       const int64_t ps = (int64_t)bq * splits + s;
       const float wgt = expf(part_lse[ps * H + h] - mx);
       den += wgt;
-      const v4f v = *(const v4f*)(part_o + (ps * H + h) * kDv + 4 * t);
-      acc += wgt * v;
+      const part_t* src = part_o + (ps * H + h) * kDv + 4 * t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += wgt * (float)src[e];
     }
     acc *= 1.f / den;
   }
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 template <int NW>
 static void launch_mla(int splits, dim3 grid, hipStream_t s, const uint16_t* q, CacheView lv, const int32_t* idx,
                        int k, int idx_q_stride, int Q, int H, int split_len, float sl2, float* out, float* lse,
-                       float* part_o, float* part_lse) {
+                       part_t* part_o, float* part_lse) {
   const dim3 block(NW * 64);
   if (splits == 1)
     hipLaunchKernelGGL((sparse_mla_kernel<NW, false>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, 1,
@@ -330,11 +345,11 @@ hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, cons
   split_len = (split_len + kTok - 1) / kTok * kTok;
   const dim3 grid((unsigned)rows * splits);
   const float sl2 = scale * kLog2e;
-  float* part_o = nullptr;
+  part_t* part_o = nullptr;
   float* part_lse = nullptr;
   if (splits > 1) {
-    part_o = (float*)ws;
-    part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(float)));
+    part_o = (part_t*)ws;
+    part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(part_t)));
   }
   if (H == 128)
     launch_mla<8>(splits, grid, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o, part_lse);

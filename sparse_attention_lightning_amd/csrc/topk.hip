@@ -22,9 +22,14 @@
 
 namespace dsa {
 
+#ifndef DSA_TOPK_VPT
+#define DSA_TOPK_VPT 4
+#endif
 constexpr int kTopkThreads = 256;
 constexpr int kTopkVec = 4;                                   // floats per load
-constexpr int kTopkChunk = kTopkThreads * kTopkVec * 4;       // 4096 scores per workgroup
+constexpr int kTopkVpt = DSA_TOPK_VPT;                        // vector loads per thread
+constexpr int kTopkPer = kTopkVec * kTopkVpt;                 // scores per thread
+constexpr int kTopkChunk = kTopkThreads * kTopkPer;           // scores per workgroup
 constexpr int kNB1 = 2048, kNB2 = 2048, kNB3 = 1024;
 
 struct TopkRow {
@@ -137,14 +142,14 @@ __device__ __forceinline__ void find_bin(const uint32_t* __restrict__ gh, int ne
   __syncthreads();
 }
 
-// This thread's 16 scores of the chunk as keys: vectors of 4 at lo + 4*tid + 1024*v, v < 4
+// This thread's scores of the chunk as keys: vectors of 4 at lo + 4*tid + 1024*v, v < kTopkVpt
 // (each vector load of a wave covers 1 KB contiguous). Bit e of `valid`: element e in [lo, hi).
 template <bool VEC>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int lo, int hi, uint32_t (&u)[16],
-                                           uint32_t& valid) {
+__device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int lo, int hi, uint32_t (&u)[kTopkPer],
+                                           uint64_t& valid) {
   valid = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < kTopkVpt; ++v) {
     const int i0 = lo + kTopkVec * (int)threadIdx.x + kTopkThreads * kTopkVec * v;
     float f[4];
     if (VEC && i0 + 3 < hi) {
@@ -157,7 +162,7 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int l
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       u[4 * v + e] = float_key(f[e]);
-      valid |= (uint32_t)(i0 + e < hi) << (4 * v + e);
+      valid |= (uint64_t)(i0 + e < hi) << (4 * v + e);
     }
   }
 }
@@ -180,7 +185,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
   TopkRow* st = ws.rows + ri.row;
   const float* srow = scores + (int64_t)ri.row * L_max;
 
-  uint32_t u[16], valid = 0;
+  uint32_t u[kTopkPer];
+  uint64_t valid = 0;
   if (ri.lo < ri.hi) load_chunk<VEC>(srow, ri.lo, ri.hi, u, valid);
 
   uint32_t prefix = 0;
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
   for (int i = threadIdx.x; i < NB; i += kTopkThreads) hist[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < kTopkPer; ++e) {
     if (!((valid >> e) & 1)) continue;
     const uint32_t x = u[e];
     if (LEVEL == 0) atomicAdd(&hist[x >> 21], 1u);
@@ -228,7 +234,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(
   if (ri.m == ri.n) return;
   TopkRow* st = ws.rows + ri.row;
   const float* srow = scores + (int64_t)ri.row * L_max;
-  uint32_t u[16], valid = 0;
+  uint32_t u[kTopkPer];
+  uint64_t valid = 0;
   if (ri.lo < ri.hi) load_chunk<VEC>(srow, ri.lo, ri.hi, u, valid);
   uint32_t b3;
   int rem3;
@@ -237,13 +244,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(
   if (ri.chunk == 0 && threadIdx.x == 0) { st->bin[2] = b3; st->rem[2] = rem3; }
   uint32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < kTopkPer; ++e) {
     const bool ok = (valid >> e) & 1;
     gt += ok && u[e] > T;
     eq += ok && u[e] == T;
   }
   uint32_t dummy;
-  const uint32_t packed = block_exclusive_scan(gt | (eq << 16), &dummy, lds4);   // <= 4096 each
+  static_assert(kTopkChunk < 65536, "per-chunk counts fit 16 bits");
+  const uint32_t packed = block_exclusive_scan(gt | (eq << 16), &dummy, lds4);
   if (threadIdx.x == 0) {
     const int64_t c = (int64_t)ri.row * n_chunks + ri.chunk;
     ws.gt[c] = (int32_t)(packed & 0xFFFF);
@@ -269,7 +277,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_compact_kernel(
   const TopkRow* st = ws.rows + ri.row;
   const uint32_t T = (st->bin[0] << 21) | (st->bin[1] << 10) | st->bin[2];
   const int rem = st->rem[2];
-  uint32_t u[16], valid;
+  uint32_t u[kTopkPer];
+  uint64_t valid;
   load_chunk<VEC>(scores + (int64_t)ri.row * L_max, ri.lo, ri.hi, u, valid);
 
   // keys kept by earlier chunks of the row, and ties seen before this chunk
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_compact_kernel(
 
   int gt_carry = 0, eq_carry = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < kTopkVpt; ++v) {
     const int i0 = ri.lo + kTopkVec * (int)threadIdx.x + kTopkThreads * kTopkVec * v;
     uint32_t fgt = 0, feq = 0;
 #pragma unroll
