@@ -1,87 +1,87 @@
 // Token selector ("LLM architecture survey", section 2.2: each query keeps the k = 2048
-// highest-scoring tokens). Exact top-k by radix select on the order-preserving uint32 image
-// of the fp32 scores, ties to the lower position, output ascending.
+// highest-scoring tokens). Exact top-k on the order-preserving uint32 image of the fp32
+// scores; equal scores go to the lower position; output ascending, -1 padded.
 //
-// A row (one query token) is cut into chunks of kTopkChunk scores, one workgroup per chunk,
-// so long rows (128K, 1M) spread over the whole chip. Passes, one launch each:
-//   hist0       histogram of key bits [31:21] (LDS, then global atomics into the row's bins)
-//   hist1       every workgroup first finds the level-0 threshold bin b1 (a block scan of the
-//               finished level-0 histogram), then bins bits [20:10] of the keys inside b1
-//   hist2       finds b2 the same way, then bins bits [9:0] of the keys whose top 22 bits match
-//   count       finds b3: T = (b1, b2, b3) is the k-th largest key and `rem` the number of ties
-//               at T to keep; counts keys > T and keys == T in its chunk
-//   compact     the chunk's output offset is the number of keys kept by earlier chunks (ties are
-//               taken in position order); ordered scan-based compaction of the kept positions;
-//               chunk 0 writes the -1 padding
-// Workgroups never wait on each other: a pass only reads what earlier launches finished, and
-// kernel boundaries make it visible. The chunk-0 workgroup of each pass stores the bin it
-// found so that later passes scan only the newest histogram.
-// Rows with p + 1 <= k keep every visible token and skip the histogram passes.
+// Two implementations with identical results. For small calls (decode, long-context share
+// groups) the chunked radix form (topk_radix.hip) keeps the chip busy; for large ones (prefill,
+// multi-token verification) the sampled form below reads the scores about once instead of five
+// times. Three launches:
+//   sample   one workgroup per row reads a block-strided sample (whole 64-byte lines, one
+//            16-score block in `stride`, stride <= k / 64 so that about 128 sampled scores are
+//            expected above the threshold) and radix-selects in LDS the key tau that about 2k
+//            of the row's scores are expected to reach.
+//   gather   chunk workgroups over the whole row append (key, position) of every score >= tau
+//            to the row's candidate list (wave-aggregated atomics; order is irrelevant).
+//   finish   one workgroup per row. If the list holds between k and kTkCap candidates it
+//            contains the exact top-k (all scores >= tau, and tau is at most the k-th
+//            largest); the workgroup radix-selects the k-th largest key T among them, breaks
+//            ties at T toward lower positions with a second radix select on the complemented
+//            position, and emits the k kept positions in order through LDS bitmaps of windows
+//            of positions. Otherwise (a sample that missed,
+//            or a flood of equal scores) it falls back to an exact scan of the whole row:
+//            three histogram passes for T, then an ordered block-scan compaction.
+// Rows with p + 1 <= k keep every visible token. Results are deterministic: the kept set is
+// defined by score and position alone, never by the order of the appends.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
 namespace dsa {
 
-#ifndef DSA_TOPK_VPT
-#define DSA_TOPK_VPT 4
+namespace radix {
+size_t workspace_bytes(int rows, int L_max);
+hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s);
+}  // namespace radix
+
+namespace sampled {
+
+constexpr int kTkThreads = 256;
+constexpr int kTkCap = 8192;               // candidates kept per row (4 x the largest k)
+#ifndef DSA_TK_SAMPLE_BLOCKS
+#define DSA_TK_SAMPLE_BLOCKS 1024
 #endif
-constexpr int kTopkThreads = 256;
-constexpr int kTopkVec = 4;                                   // floats per load
-constexpr int kTopkVpt = DSA_TOPK_VPT;                        // vector loads per thread
-constexpr int kTopkPer = kTopkVec * kTopkVpt;                 // scores per thread
-constexpr int kTopkChunk = kTopkThreads * kTopkPer;           // scores per workgroup
-constexpr int kNB1 = 2048, kNB2 = 2048, kNB3 = 1024;
+constexpr int kTkSampleBlocks = DSA_TK_SAMPLE_BLOCKS;   // sampled 16-score blocks per row
+constexpr int kTkChunk = 4096;             // scores per gather workgroup (16 per thread)
+constexpr int kTkWindow = 1 << 18;         // positions per bitmap window in the finish step (32 KB)
+static_assert(kTkCap >= 2 * kMaxK, "room for about 2k candidates plus spread");
 
-struct TopkRow {
-  uint32_t hist1[kNB1];
-  uint32_t hist2[kNB2];
-  uint32_t hist3[kNB3];
-  uint32_t bin[3];       // threshold bin found at each level (written by chunk 0)
-  int32_t rem[3];        // keys still needed from that bin
-  uint32_t pad[58];
+struct TkRow {
+  uint32_t count;   // candidates appended (may exceed kTkCap: the excess was not stored)
+  uint32_t tau;     // candidate threshold key
+  uint32_t pad[62];
 };
-static_assert(sizeof(TopkRow) % 256 == 0, "row state is 256-byte aligned");
-constexpr int kZeroWords = kNB1 + kNB2 + kNB3;
-
-struct TopkWs {
-  TopkRow* rows;
-  int32_t* gt;       // [rows][n_chunks] keys > T per chunk
-  int32_t* eq;       // [rows][n_chunks] keys == T per chunk
-};
+static_assert(sizeof(TkRow) == 256, "row state is 256 bytes");
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t topk_workspace_bytes(int rows, int L_max) {
-  const size_t n_chunks = (L_max + kTopkChunk - 1) / kTopkChunk;
-  return align256(sizeof(TopkRow) * (size_t)rows) + 2 * align256(sizeof(int32_t) * rows * n_chunks);
+static size_t workspace_bytes(int rows) {
+  return align256(sizeof(TkRow) * (size_t)rows) + align256((size_t)rows * kTkCap * sizeof(uint2));
 }
 
-static TopkWs carve(void* ws, int rows, int n_chunks) {
-  char* p = (char*)ws;
-  TopkWs t;
-  t.rows = (TopkRow*)p;
-  p += align256(sizeof(TopkRow) * (size_t)rows);
-  const size_t a = align256(sizeof(int32_t) * (size_t)rows * n_chunks);
-  t.gt = (int32_t*)p;
-  t.eq = (int32_t*)(p + a);
+struct TkWs {
+  TkRow* rows;
+  uint2* cand;      // [rows][kTkCap] (key, position)
+};
+
+static TkWs carve(void* ws, int rows) {
+  TkWs t;
+  t.rows = (TkRow*)ws;
+  t.cand = (uint2*)((char*)ws + align256(sizeof(TkRow) * (size_t)rows));
   return t;
 }
 
-struct RowInfo {
-  int row, chunk, n, m, lo, hi;
+struct TkRowInfo {
+  int n, m;
 };
 
-__device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32_t* q_pos, int Q, int in_Q,
-                                            int L_max, int k, int n_chunks) {
-  RowInfo ri;
-  ri.row = blockIdx.x / n_chunks;
-  ri.chunk = blockIdx.x - ri.row * n_chunks;
-  const int b = ri.row / Q, j = ri.row - b * Q;
+__device__ __forceinline__ TkRowInfo tk_row(const int32_t* seq_lens, const int32_t* q_pos, int Q, int in_Q, int L_max,
+                                            int k, int row) {
+  const int b = row / Q, j = row - b * Q;
   const int p = query_pos(seq_lens, q_pos, in_Q, b, j);
+  TkRowInfo ri;
   ri.n = max(0, min(p + 1, L_max));
   ri.m = min(k, ri.n);
-  ri.lo = ri.chunk * kTopkChunk;
-  ri.hi = min(ri.lo + kTopkChunk, ri.n);
   return ri;
 }
 
@@ -108,49 +108,192 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* e
   return total;
 }
 
-// The bin of a finished histogram that holds the need-th largest key, and how many keys are
-// still needed from it. Bins are scanned from the top; thread 0 owns the highest bins.
-// Every thread of the block must call it.
+// Radix-select scratch shared by the helpers below (LDS).
+struct TkLds {
+  uint32_t hist[4096];
+  uint32_t lds4[4];
+  uint32_t res[2];
+};
+
+// The bin of hist[0..NB) holding the need-th largest element and how many are still needed
+// from it. Every thread of the block must call it.
 template <int NB>
-__device__ __forceinline__ void find_bin(const uint32_t* __restrict__ gh, int need, uint32_t* lds4,
-                                         uint32_t* out_bin, int* out_rem) {
-  constexpr int PER = NB / kTopkThreads;
-  __shared__ uint32_t res[2];
-  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
+__device__ __forceinline__ void find_bin(TkLds& L, int need, uint32_t& bin, int& rem) {
+  constexpr int PER = NB / kTkThreads;
+  if (threadIdx.x == 0) { L.res[0] = 0; L.res[1] = 0; }
   const int top = NB - PER * (int)threadIdx.x;
   uint32_t h[PER];
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    h[e] = gh[top - 1 - e];
+    h[e] = L.hist[top - 1 - e];
     mine += h[e];
   }
   uint32_t above;
-  block_exclusive_scan(mine, &above, lds4);
+  block_exclusive_scan(mine, &above, L.lds4);
   uint32_t cum = above;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     if (cum < (uint32_t)need && (uint32_t)need <= cum + h[e]) {
-      res[0] = (uint32_t)(top - 1 - e);
-      res[1] = (uint32_t)(need - (int)cum);
+      L.res[0] = (uint32_t)(top - 1 - e);
+      L.res[1] = (uint32_t)(need - (int)cum);
     }
     cum += h[e];
   }
   __syncthreads();
-  *out_bin = res[0];
-  *out_rem = (int)res[1];
+  bin = L.res[0];
+  rem = (int)L.res[1];
   __syncthreads();
 }
 
-// This thread's scores of the chunk as keys: vectors of 4 at lo + 4*tid + 1024*v, v < kTopkVpt
-// (each vector load of a wave covers 1 KB contiguous). Bit e of `valid`: element e in [lo, hi).
-template <bool VEC>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int lo, int hi, uint32_t (&u)[kTopkPer],
-                                           uint64_t& valid) {
-  valid = 0;
+__device__ __forceinline__ void zero_hist(TkLds& L, int nb) {
+  for (int i = threadIdx.x; i < nb; i += kTkThreads) L.hist[i] = 0u;
+  __syncthreads();
+}
+
+// Block-wide min and max of one uint32 per thread.
+__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TkLds& L, uint32_t& out_lo, uint32_t& out_hi) {
 #pragma unroll
-  for (int v = 0; v < kTopkVpt; ++v) {
-    const int i0 = lo + kTopkVec * (int)threadIdx.x + kTopkThreads * kTopkVec * v;
+  for (int d = 32; d >= 1; d >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+  }
+  const int wave = threadIdx.x >> 6;
+  __shared__ uint32_t mm[8];
+  if ((threadIdx.x & 63) == 0) { mm[wave] = lo; mm[4 + wave] = hi; }
+  __syncthreads();
+  out_lo = min(min(mm[0], mm[1]), min(mm[2], mm[3]));
+  out_hi = max(max(mm[4], mm[5]), max(mm[6], mm[7]));
+  __syncthreads();
+}
+
+// The need-th largest 32-bit key among key(i), i < n, and how many keys equal to it must be
+// taken. The radix digits are taken from key - min over only the significant bits of the
+// observed range (up to 11 bits per level), so even tightly clustered keys spread over the
+// histogram instead of piling onto one or two LDS counters; equal keys need no level at all.
+template <typename KeyFn>
+__device__ void select_key(TkLds& L, int n, int need, KeyFn key, uint32_t& T, int& rem) {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = threadIdx.x; i < n; i += kTkThreads) {
+    const uint32_t u = key(i);
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+  block_minmax(lo, hi, L, lo, hi);
+  const uint32_t span = hi - lo;
+  int bits = span ? 32 - __clz((int)span) : 0;
+  uint32_t prefix = 0;                    // offset bits resolved so far (those above `bits`)
+  int nd = need;
+  while (bits > 0) {                      // block-uniform
+    const int w = min(11, bits), shift = bits - w;
+    zero_hist(L, 2048);
+    for (int i = threadIdx.x; i < n; i += kTkThreads) {
+      const uint32_t off = key(i) - lo;
+      if ((uint32_t)((uint64_t)off >> bits) == prefix) atomicAdd(&L.hist[(off >> shift) & ((1u << w) - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t b;
+    int r;
+    find_bin<2048>(L, nd, b, r);
+    prefix = (prefix << w) | b;
+    nd = r;
+    bits = shift;
+  }
+  T = lo + prefix;
+  rem = nd;
+}
+
+// The need-th largest 24-bit value v(i) among the i with use(i): two 12-bit levels.
+template <typename ValFn, typename UseFn>
+__device__ uint32_t select_24(TkLds& L, int n, int need, ValFn v, UseFn use) {
+  uint32_t b1, b2;
+  int r1, r2;
+  zero_hist(L, 4096);
+  for (int i = threadIdx.x; i < n; i += kTkThreads)
+    if (use(i)) atomicAdd(&L.hist[v(i) >> 12], 1u);
+  __syncthreads();
+  find_bin<4096>(L, need, b1, r1);
+  zero_hist(L, 4096);
+  for (int i = threadIdx.x; i < n; i += kTkThreads)
+    if (use(i) && (v(i) >> 12) == b1) atomicAdd(&L.hist[v(i) & 0xFFF], 1u);
+  __syncthreads();
+  find_bin<4096>(L, r1, b2, r2);
+  return (b1 << 12) | b2;
+}
+
+// ------------------------------------------------------------------------------------------ sample
+template <bool VEC>
+__global__ __launch_bounds__(kTkThreads) void topk_sample_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, TkWs ws) {
+  __shared__ uint32_t skey[kTkSampleBlocks * 16];
+  __shared__ TkLds L;
+  const int row = blockIdx.x;
+  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  TkRow* st = ws.rows + row;
+  if (ri.m == ri.n) {
+    if (threadIdx.x == 0) { st->count = 0; st->tau = 0; }
+    return;
+  }
+  if (ri.n <= kTkCap) {                                // the whole row fits the candidate list
+    if (threadIdx.x == 0) { st->tau = 0u; st->count = 0; }
+    return;
+  }
+  const float* srow = scores + (int64_t)row * L_max;
+  const int n_blocks = (ri.n + 15) / 16;
+  const int stride = max(max(1, k / 64), (n_blocks + kTkSampleBlocks - 1) / kTkSampleBlocks);
+  const int s_blocks = (n_blocks + stride - 1) / stride;
+  constexpr int kPer = kTkSampleBlocks * 4 / kTkThreads;                   // float4 slots per thread
+  float f[kPer][4];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {                                         // all loads in flight at once
+    const int v = (int)threadIdx.x + e * kTkThreads;
+    const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
+    if (VEC && v < s_blocks * 4 && i0 + 3 < ri.n) {
+      const float4 x = *(const float4*)(srow + i0);
+      f[e][0] = x.x; f[e][1] = x.y; f[e][2] = x.z; f[e][3] = x.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f[e][c] = (v < s_blocks * 4 && i0 + c < ri.n) ? srow[i0 + c] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = (int)threadIdx.x + e * kTkThreads;
+    const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (v < s_blocks * 4) skey[4 * v + c] = (i0 + c < ri.n) ? float_key(f[e][c]) : 0u;   // 0: below every score
+  }
+  __syncthreads();
+  const int s = s_blocks * 16;
+  const int r = max(1, min((2 * k + stride - 1) / stride, s));   // ~2k scores of the row should reach tau
+  uint32_t T;
+  int rem;
+  select_key(L, s, r, [&](int i) { return skey[i]; }, T, rem);
+  if (threadIdx.x == 0) { st->tau = T; st->count = 0; }
+}
+
+// ------------------------------------------------------------------------------------------ gather
+template <bool VEC>
+__global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, int n_chunks, TkWs ws) {
+  const int row = blockIdx.x / n_chunks, chunk = blockIdx.x - row * n_chunks;
+  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  if (ri.m == ri.n) return;
+  const int lo = chunk * kTkChunk, hi = min(lo + kTkChunk, ri.n);
+  if (lo >= hi) return;
+  TkRow* st = ws.rows + row;
+  const uint32_t tau = st->tau;
+  const float* srow = scores + (int64_t)row * L_max;
+  const int lane = threadIdx.x & 63;
+  uint32_t u[16];
+  int pos[16];
+  int mine = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i0 = lo + 4 * (int)threadIdx.x + 1024 * v;
     float f[4];
     if (VEC && i0 + 3 < hi) {
       const float4 x = *(const float4*)(srow + i0);
@@ -161,160 +304,61 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int l
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      u[4 * v + e] = float_key(f[e]);
-      valid |= (uint64_t)(i0 + e < hi) << (4 * v + e);
+      const uint32_t key = float_key(f[e]);
+      if (i0 + e < hi && key >= tau) {
+        u[mine] = key;
+        pos[mine] = i0 + e;
+        ++mine;
+      }
     }
   }
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_zero_kernel(TopkRow* rows) {
-  uint32_t* base = (uint32_t*)(rows + blockIdx.x);
-  for (int i = threadIdx.x; i < kZeroWords; i += kTopkThreads) base[i] = 0u;
-}
-
-// Radix level LEVEL over key bits [31:21], [20:10] or [9:0].
-template <int LEVEL, bool VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, int n_chunks, TopkWs ws) {
-  constexpr int NB = LEVEL == 2 ? kNB3 : kNB1;
-  __shared__ uint32_t hist[NB];
-  __shared__ uint32_t lds4[4];
-  const RowInfo ri = row_info(seq_lens, q_pos, Q, in_Q, L_max, k, n_chunks);
-  if (ri.m == ri.n) return;                       // every visible token is kept
-  TopkRow* st = ws.rows + ri.row;
-  const float* srow = scores + (int64_t)ri.row * L_max;
-
-  uint32_t u[kTopkPer];
-  uint64_t valid = 0;
-  if (ri.lo < ri.hi) load_chunk<VEC>(srow, ri.lo, ri.hi, u, valid);
-
-  uint32_t prefix = 0;
-  if (LEVEL == 1) {
-    uint32_t b1;
-    int rem1;
-    find_bin<kNB1>(st->hist1, ri.m, lds4, &b1, &rem1);
-    if (ri.chunk == 0 && threadIdx.x == 0) { st->bin[0] = b1; st->rem[0] = rem1; }
-    prefix = b1;
-  } else if (LEVEL == 2) {
-    uint32_t b2;
-    int rem2;
-    const uint32_t b1 = st->bin[0];
-    find_bin<kNB2>(st->hist2, st->rem[0], lds4, &b2, &rem2);
-    if (ri.chunk == 0 && threadIdx.x == 0) { st->bin[1] = b2; st->rem[1] = rem2; }
-    prefix = (b1 << 11) | b2;
-  }
-  if (ri.lo >= ri.hi) return;                     // block-uniform; after the find's barriers
-
-  for (int i = threadIdx.x; i < NB; i += kTopkThreads) hist[i] = 0u;
-  __syncthreads();
+  // one atomic per wave reserves room for the wave's candidates
+  int incl = mine;
 #pragma unroll
-  for (int e = 0; e < kTopkPer; ++e) {
-    if (!((valid >> e) & 1)) continue;
-    const uint32_t x = u[e];
-    if (LEVEL == 0) atomicAdd(&hist[x >> 21], 1u);
-    else if (LEVEL == 1) { if ((x >> 21) == prefix) atomicAdd(&hist[(x >> 10) & 0x7FF], 1u); }
-    else { if ((x >> 10) == prefix) atomicAdd(&hist[x & 0x3FF], 1u); }
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
-  __syncthreads();
-  uint32_t* gh = LEVEL == 0 ? st->hist1 : (LEVEL == 1 ? st->hist2 : st->hist3);
-  for (int i = threadIdx.x; i < NB; i += kTopkThreads) {
-    const uint32_t c = hist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
+  const int total = __shfl(incl, 63, 64);
+  if (total == 0) return;
+  uint32_t base = 0;
+  if (lane == 63) base = atomicAdd(&st->count, (uint32_t)total);
+  base = __shfl(base, 63, 64) + (uint32_t)(incl - mine);
+  uint2* cand = ws.cand + (int64_t)row * kTkCap;
+  for (int c = 0; c < mine; ++c)
+    if (base + c < (uint32_t)kTkCap) cand[base + c] = make_uint2(u[c], (uint32_t)pos[c]);
 }
 
-// Finds T and the tie quota, then counts keys > T and == T in the chunk.
-template <bool VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, int n_chunks, TopkWs ws) {
-  __shared__ uint32_t lds4[4];
-  const RowInfo ri = row_info(seq_lens, q_pos, Q, in_Q, L_max, k, n_chunks);
-  if (ri.m == ri.n) return;
-  TopkRow* st = ws.rows + ri.row;
-  const float* srow = scores + (int64_t)ri.row * L_max;
-  uint32_t u[kTopkPer];
-  uint64_t valid = 0;
-  if (ri.lo < ri.hi) load_chunk<VEC>(srow, ri.lo, ri.hi, u, valid);
-  uint32_t b3;
-  int rem3;
-  find_bin<kNB3>(st->hist3, st->rem[1], lds4, &b3, &rem3);
-  const uint32_t T = (st->bin[0] << 21) | (st->bin[1] << 10) | b3;
-  if (ri.chunk == 0 && threadIdx.x == 0) { st->bin[2] = b3; st->rem[2] = rem3; }
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < kTopkPer; ++e) {
-    const bool ok = (valid >> e) & 1;
-    gt += ok && u[e] > T;
-    eq += ok && u[e] == T;
-  }
-  uint32_t dummy;
-  static_assert(kTopkChunk < 65536, "per-chunk counts fit 16 bits");
-  const uint32_t packed = block_exclusive_scan(gt | (eq << 16), &dummy, lds4);
-  if (threadIdx.x == 0) {
-    const int64_t c = (int64_t)ri.row * n_chunks + ri.chunk;
-    ws.gt[c] = (int32_t)(packed & 0xFFFF);
-    ws.eq[c] = (int32_t)(packed >> 16);
-  }
-}
-
-// Ordered compaction of each chunk's kept positions into idx.
-template <bool VEC>
-__global__ __launch_bounds__(kTopkThreads) void topk_compact_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, int n_chunks, TopkWs ws, int32_t* __restrict__ idx) {
-  __shared__ uint32_t lds4[4];
-  const RowInfo ri = row_info(seq_lens, q_pos, Q, in_Q, L_max, k, n_chunks);
-  int32_t* out = idx + (int64_t)ri.row * k;
-  if (ri.chunk == 0)
-    for (int i = ri.m + (int)threadIdx.x; i < k; i += kTopkThreads) out[i] = -1;
-  if (ri.lo >= ri.hi) return;
-  if (ri.m == ri.n) {                      // keep all visible: position i goes to slot i
-    for (int i = ri.lo + (int)threadIdx.x; i < ri.hi; i += kTopkThreads) out[i] = i;
-    return;
-  }
-  const TopkRow* st = ws.rows + ri.row;
-  const uint32_t T = (st->bin[0] << 21) | (st->bin[1] << 10) | st->bin[2];
-  const int rem = st->rem[2];
-  uint32_t u[kTopkPer];
-  uint64_t valid;
-  load_chunk<VEC>(scores + (int64_t)ri.row * L_max, ri.lo, ri.hi, u, valid);
-
-  // keys kept by earlier chunks of the row, and ties seen before this chunk
-  const int64_t cbase = (int64_t)ri.row * n_chunks;
-  uint32_t gt_b = 0, eq_b = 0;
-  for (int c = threadIdx.x; c < ri.chunk; c += kTopkThreads) {
-    gt_b += (uint32_t)ws.gt[cbase + c];
-    eq_b += (uint32_t)ws.eq[cbase + c];
-  }
-  uint32_t dummy;
-  const uint32_t gt_before = block_exclusive_scan(gt_b, &dummy, lds4);
-  const uint32_t eq_before = block_exclusive_scan(eq_b, &dummy, lds4);
-  const int quota = max(0, min((int)ws.eq[cbase + ri.chunk], rem - (int)eq_before));
-  const int off = (int)gt_before + min((int)eq_before, rem);
-
+// ------------------------------------------------------------------------------------------ finish
+// Exact top-k of a whole row by one workgroup (the fallback): three histogram passes over the
+// row for T and the tie quota, then an ordered block-scan compaction in position order.
+__device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, int32_t* __restrict__ out, TkLds& L) {
+  auto key_at = [&](int i) { return float_key(srow[i]); };
+  uint32_t T;
+  int rem;
+  select_key(L, n, k, key_at, T, rem);
   int gt_carry = 0, eq_carry = 0;
-#pragma unroll
-  for (int v = 0; v < kTopkVpt; ++v) {
-    const int i0 = ri.lo + kTopkVec * (int)threadIdx.x + kTopkThreads * kTopkVec * v;
+  for (int base = 0; base < n; base += kTkThreads * 4) {
+    const int i0 = base + 4 * (int)threadIdx.x;
     uint32_t fgt = 0, feq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ok = (valid >> (4 * v + e)) & 1;
-      fgt |= (uint32_t)(ok && u[4 * v + e] > T) << e;
-      feq |= (uint32_t)(ok && u[4 * v + e] == T) << e;
+      if (i0 + e < n) {
+        const uint32_t u = key_at(i0 + e);
+        fgt |= (uint32_t)(u > T) << e;
+        feq |= (uint32_t)(u == T) << e;
+      }
     }
     const uint32_t packed = (uint32_t)__builtin_popcount(fgt) | ((uint32_t)__builtin_popcount(feq) << 16);
     uint32_t before;
-    const uint32_t tot = block_exclusive_scan(packed, &before, lds4);
+    const uint32_t tot = block_exclusive_scan(packed, &before, L.lds4);
     int g_b = gt_carry + (int)(before & 0xFFFF);
     int q_b = eq_carry + (int)(before >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool g = (fgt >> e) & 1, q = (feq >> e) & 1;
-      const int slot = off + g_b + min(q_b, quota);
-      if ((g || (q && q_b < quota)) && slot < k) out[slot] = i0 + e;
+      const int slot = g_b + min(q_b, rem);
+      if ((g || (q && q_b < rem)) && slot < k) out[slot] = i0 + e;
       g_b += g;
       q_b += q;
     }
@@ -323,33 +367,133 @@ __global__ __launch_bounds__(kTopkThreads) void topk_compact_kernel(
   }
 }
 
+__global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
+  __shared__ uint32_t ckey[kTkCap];
+  __shared__ int cpos[kTkCap];
+  __shared__ uint32_t bitmap[kTkWindow / 32];
+  __shared__ TkLds L;
+  const int row = blockIdx.x;
+  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  int32_t* out = idx + (int64_t)row * k;
+  for (int i = ri.m + (int)threadIdx.x; i < k; i += kTkThreads) out[i] = -1;
+  if (ri.m == ri.n) {                                  // keep every visible token
+    for (int i = threadIdx.x; i < ri.n; i += kTkThreads) out[i] = i;
+    return;
+  }
+  const TkRow* st = ws.rows + row;
+  const int cnt = (int)st->count;
+  if (cnt < k || cnt > kTkCap) {                       // the sample missed: exact scan of the row
+    finish_full_scan(scores + (int64_t)row * L_max, ri.n, k, out, L);
+    return;
+  }
+  const uint2* cand = ws.cand + (int64_t)row * kTkCap;
+  constexpr int kCPer = kTkCap / kTkThreads;
+  uint2 c[kCPer];
+#pragma unroll
+  for (int e = 0; e < kCPer; ++e) {                                        // all loads in flight at once
+    const int i = (int)threadIdx.x + e * kTkThreads;
+    if (i < cnt) c[e] = cand[i];
+  }
+#pragma unroll
+  for (int e = 0; e < kCPer; ++e) {
+    const int i = (int)threadIdx.x + e * kTkThreads;
+    if (i < cnt) { ckey[i] = c[e].x; cpos[i] = (int)c[e].y; }
+  }
+  __syncthreads();
+  uint32_t T;
+  int rem;
+  select_key(L, cnt, k, [&](int i) { return ckey[i]; }, T, rem);
+  // ties at T: all of them, or the rem lowest positions (largest complemented positions)
+  uint32_t eq_local = 0;
+  for (int i = threadIdx.x; i < cnt; i += kTkThreads) eq_local += ckey[i] == T;
+  uint32_t dummy;
+  const int n_eq = (int)block_exclusive_scan(eq_local, &dummy, L.lds4);
+  uint32_t pos_cut = 0;                                // keep ties with (0xFFFFFF - pos) >= pos_cut
+  if (n_eq > rem)
+    pos_cut = select_24(L, cnt, rem, [&](int i) { return 0xFFFFFFu - (uint32_t)cpos[i]; },
+                        [&](int i) { return ckey[i] == T; });
+  // Emit the kept positions in ascending order through a bitmap of a window of positions at a
+  // time: kept candidates set their bits, a block scan of popcounts places them.
+  auto keep = [&](int i) {
+    return ckey[i] > T || (ckey[i] == T && (0xFFFFFFu - (uint32_t)cpos[i]) >= pos_cut);
+  };
+  int emitted = 0;
+  for (int base = 0; base < ri.n; base += kTkWindow) {
+    for (int i = threadIdx.x; i < kTkWindow / 32; i += kTkThreads) bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += kTkThreads) {
+      const int q = cpos[i] - base;
+      if (q >= 0 && q < kTkWindow && keep(i)) atomicOr(&bitmap[q >> 5], 1u << (q & 31));
+    }
+    __syncthreads();
+    constexpr int W = kTkWindow / 32 / kTkThreads;                 // words per thread
+    uint32_t pc = 0;
+#pragma unroll
+    for (int e = 0; e < W; ++e) pc += __builtin_popcount(bitmap[threadIdx.x * W + e]);
+    uint32_t at;
+    const uint32_t tot = block_exclusive_scan(pc, &at, L.lds4);
+    int slot = emitted + (int)at;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      uint32_t m = bitmap[threadIdx.x * W + e];
+      while (m) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1;
+        if (slot < k) out[slot] = base + 32 * (threadIdx.x * W + e) + bit;
+        ++slot;
+      }
+    }
+    emitted += (int)tot;
+    __syncthreads();
+  }
+}
+
 template <bool VEC>
-static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TopkWs w, int rows,
-                       int n_chunks, hipStream_t s) {
-  const dim3 block(kTopkThreads), grid((unsigned)rows * n_chunks);
-  hipLaunchKernelGGL(topk_zero_kernel, dim3(rows), block, 0, s, w.rows);
-  hipLaunchKernelGGL((topk_hist_kernel<0, VEC>), grid, block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL((topk_hist_kernel<1, VEC>), grid, block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL((topk_hist_kernel<2, VEC>), grid, block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL(topk_count_kernel<VEC>, grid, block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL(topk_compact_kernel<VEC>, grid, block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, n_chunks, w, idx);
+static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
+                       hipStream_t s) {
+  const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
+  const dim3 block(kTkThreads);
+  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
+                     bt.L_max, k, w);
+  hipLaunchKernelGGL(topk_gather_kernel<VEC>, dim3((unsigned)rows * n_chunks), block, 0, s, scores, bt.seq_lens,
+                     bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, n_chunks, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
+                     bt.L_max, k, w, idx);
+}
+
+hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const int rows = bt.B * bt.Q;
+  TkWs w = carve(ws, rows);
+  // 16-byte vector loads need every row to start 16-byte aligned
+  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
+    launch_all<true>(bt, scores, k, idx, w, rows, s);
+  else
+    launch_all<false>(bt, scores, k, idx, w, rows, s);
+  return hipGetLastError();
+}
+
+}  // namespace sampled
+
+#ifndef DSA_TOPK_SAMPLED_MIN_SCORES
+#define DSA_TOPK_SAMPLED_MIN_SCORES (1 << 23)
+#endif
+
+// The sampled form once a call holds more than 8M scores (rows x L_max); below that the chunked
+// radix form's extra passes over the scores cost less than one workgroup per row in series.
+static bool use_sampled(const HostBatch& bt) {
+  return (int64_t)bt.B * bt.Q * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES;
+}
+
+// Room for either form, so that any call with at most `rows` rows fits.
+size_t topk_workspace_bytes(int rows, int L_max) {
+  return std::max(radix::workspace_bytes(rows, L_max), sampled::workspace_bytes(rows));
 }
 
 hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s) {
-  const int rows = bt.B * bt.Q;
-  const int n_chunks = (bt.L_max + kTopkChunk - 1) / kTopkChunk;
-  TopkWs w = carve(ws, rows, n_chunks);
-  // 16-byte vector loads need every row to start 16-byte aligned
-  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
-    launch_all<true>(bt, scores, k, idx, w, rows, n_chunks, s);
-  else
-    launch_all<false>(bt, scores, k, idx, w, rows, n_chunks, s);
-  return hipGetLastError();
+  if (use_sampled(bt)) return sampled::launch(bt, scores, k, idx, ws, s);
+  return radix::launch(bt, scores, k, idx, ws, s);
 }
 
 }  // namespace dsa

@@ -97,28 +97,45 @@ def test_index_score_explicit_positions_and_determinism():
 
 
 # ----------------------------------------------------------------------------- top-k
-def run_topk(scores32, seq_lens, k, q_pos=None):
-    t = torch.from_numpy(np.ascontiguousarray(scores32)).to(DEV)
-    sl = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
-    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int32, device=DEV)
-    return np_(dsa.topk(t, sl, k, q_pos=qp))
+# The library takes the chunked radix form for calls of at most this many scores (B * Q * L_max)
+# and the sampled form above it; tests run each case in both forms by repeating the batch.
+SAMPLED_ABOVE_SCORES = 1 << 23
+FORMS = ["radix", "sampled"]
+
+
+def run_topk(scores32, seq_lens, k, q_pos=None, form="radix"):
+    scores32 = np.ascontiguousarray(scores32)
+    B, Q, L_max = scores32.shape
+    reps = 1
+    if form == "sampled":
+        reps = SAMPLED_ABOVE_SCORES // (B * Q * L_max) + 1
+    else:
+        assert B * Q * L_max <= SAMPLED_ABOVE_SCORES
+    t = torch.from_numpy(np.tile(scores32, (reps, 1, 1))).to(DEV)
+    sl = torch.tensor(list(seq_lens) * reps, dtype=torch.int32, device=DEV)
+    qp = None if q_pos is None else torch.tensor(np.tile(np.asarray(q_pos), (reps, 1)), dtype=torch.int32, device=DEV)
+    got = np_(dsa.topk(t, sl, k, q_pos=qp)).reshape(reps, B, Q, k)
+    assert all(np.array_equal(got[0], got[r]) for r in range(1, reps))
+    return got[0]
 
 
 def oracle_topk(scores32, seq_lens, k, q_pos=None):
     return oracle.topk_batch(scores32, seq_lens, k, q_pos=q_pos)
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("k", [2048, 1, 7, 300])
-def test_topk_exact_on_oracle_scores(k):
+def test_topk_exact_on_oracle_scores(k, form):
     wl = synth.small("verify_b64_q8_32k", B=3, Q=2, L=20000, L_max=20480, page_size=0, seq_lens=(20000, 9000, 2100))
     cpu = synth.generate(wl, seed=3, with_mla=False)
     s = oracle.index_scores_batch(np_(cpu.q_idx), np_(cpu.w), key_cache(cpu), wl.lens, wl.lmax)
     s32 = s.astype(np.float32)
-    got = run_topk(s32, wl.lens, k)
+    got = run_topk(s32, wl.lens, k, form=form)
     assert np.array_equal(got, oracle_topk(s32, wl.lens, k))
 
 
-def test_topk_exact_ties_and_degenerate_rows():
+@pytest.mark.parametrize("form", FORMS)
+def test_topk_exact_ties_and_degenerate_rows(form):
     rng = np.random.default_rng(7)
     L = 13000
     rows = [
@@ -132,26 +149,28 @@ def test_topk_exact_ties_and_degenerate_rows():
     s = np.stack(rows)[:, None, :]
     lens = [L, L, L, 12345, L, 4097]
     for k in (2048, 1000, 1):
-        got = run_topk(s, lens, k)
+        got = run_topk(s, lens, k, form=form)
         assert np.array_equal(got, oracle_topk(s, lens, k)), k
 
 
-def test_topk_rows_shorter_than_k_and_positions():
+@pytest.mark.parametrize("form", FORMS)
+def test_topk_rows_shorter_than_k_and_positions(form):
     rng = np.random.default_rng(8)
     L = 6000
     s = rng.normal(size=(2, 4, L)).astype(np.float32)
     lens = [L, 1500]
     q_pos = [[0, 2047, 2048, 5999], [10, 1499, 700, 2047]]
-    got = run_topk(s, lens, 2048, q_pos=q_pos)
+    got = run_topk(s, lens, 2048, q_pos=q_pos, form=form)
     assert np.array_equal(got, oracle_topk(s, lens, 2048, q_pos=np.array(q_pos)))
     assert got[0, 0, 0] == 0 and np.all(got[0, 0, 1:] == -1)
 
 
-def test_topk_deterministic():
+@pytest.mark.parametrize("form", FORMS)
+def test_topk_deterministic(form):
     rng = np.random.default_rng(9)
     s = rng.integers(0, 1000, size=(4, 1, 70000)).astype(np.float32)
-    a = run_topk(s, [70000] * 4, 2048)
-    b = run_topk(s, [70000] * 4, 2048)
+    a = run_topk(s, [70000] * 4, 2048, form=form)
+    b = run_topk(s, [70000] * 4, 2048, form=form)
     assert np.array_equal(a, b)
     assert np.array_equal(a, oracle_topk(s, [70000] * 4, 2048))
 
@@ -253,3 +272,21 @@ def test_forward_shared_small(share_first):
         for b in range(wl.B):
             for j in range(wl.Q):
                 check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
+
+
+def test_topk_when_the_sample_misses():
+    """The sampled form reads one 16-score block in `stride` (32 for k = 2048 on a 128K row).
+    When exactly those blocks, or exactly the blocks between them, carry the high scores, or
+    every score is equal, the candidate list misses or overflows and the exact full-row scan
+    must produce the set."""
+    rng = np.random.default_rng(21)
+    L = 131072
+    s = (1.0 + rng.random((4, 1, L))).astype(np.float32)
+    blk = np.arange(L) // 16
+    s[0, 0, blk % 32 == 0] += 100.0                # exactly the sampled blocks (k = 2048)
+    s[1, 0, blk % 32 != 0] += 100.0                # everything but the sampled blocks
+    s[2, 0, :] = np.float32(7.0)                   # every score equal: a flood of candidates
+    s[3, 0, blk % 4 == 0] += 100.0                 # every fourth block: the sampled ones and more
+    for k in (2048, 300):
+        got = run_topk(s, [L] * 4, k, form="sampled")
+        assert np.array_equal(got, oracle_topk(s, [L] * 4, k)), k
