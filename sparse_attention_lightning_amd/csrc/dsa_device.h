@@ -8,6 +8,7 @@ namespace dsa {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -42,6 +43,13 @@ __device__ __forceinline__ int query_pos(const int32_t* seq_lens, const int32_t*
 // operands must use the same byte order along K. c[r] = C[4*(l/16) + r][l % 16].
 __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32x32x64 FP8(E4M3) x FP8(E4M3) -> fp32 matrix-core product, accumulating into c. Lane l
+// supplies row (l % 32) of A and column (l % 32) of B, 32 bytes each, one shared K order;
+// c[j] = C[8*(j/4) + 4*(l/32) + j%4][l % 32].
+__device__ __forceinline__ v16f mfma_fp8_32(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // 16x16x32 bf16 matrix-core product: lane l supplies 8 bf16 of row (l % 16) of A and of

@@ -170,51 +170,69 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Multi-query form (prefill chunks, speculative verify): the query tokens of one sequence share
-// every key, so a workgroup of NW waves x 2 query tokens stages each tile of 256 keys once in
-// LDS (direct-to-LDS loads into a 3-stage ring, rows XOR-swizzled by 16-byte chunk so the
-// 16 rows of one MFMA operand fetch hit distinct banks). Every B fragment read from LDS then
-// feeds 2 queries x Hi/16 FP8 matrix-core products, and the ReLU / weighted head sum runs in
-// registers as in the decode form. Keys after the last query's position are neither loaded
-// nor scored; scores after each query's own position are -inf.
+// every key, so a workgroup of 8 waves, one query token each, stages each tile of 256 keys once
+// in LDS (direct-to-LDS loads into a 2-stage ring, rows XOR-swizzled by 16-byte chunk so the 16
+// rows of one matrix-core operand fetch hit distinct banks). Each wave runs its 64 heads x 16
+// keys per group through 4 FP8 matrix-core products, pipelined with the ReLU / weighted head
+// sum of the previous group, and a 3-swap reduce-scatter leaves one key per lane for a
+// coalesced store per 64 keys. Keys after the last query's position are neither loaded nor
+// scored; scores after each query's own position are -inf.
+//
+// The kernel is bound by VALU issue: the epilogue costs 2 VALU operations per head x key (an
+// integer max for the ReLU, a multiply-add), 8 per matrix-core product of 32 cycles, so every
+// other VALU instruction comes straight out of the matrix-core rate. Tile loads therefore take
+// wave-uniform (scalar) addresses and the reduce-scatter uses lane-swap instructions.
 #ifndef DSA_MQ_TILE
 #define DSA_MQ_TILE 256
 #endif
 #ifndef DSA_MQ_STAGES
 #define DSA_MQ_STAGES 2
 #endif
+#ifndef DSA_MQ_CHUNK
+#define DSA_MQ_CHUNK 4096
+#endif
+#ifndef DSA_MQ_SCHED
+#define DSA_MQ_SCHED 0
+#endif
 constexpr int kMqTile = DSA_MQ_TILE;                 // keys per LDS tile
 constexpr int kMqStages = DSA_MQ_STAGES;
-constexpr int kMqChunk = 4096;                       // keys per workgroup
-constexpr int kMqTilesPerChunk = kMqChunk / kMqTile;
+constexpr int kMqChunk = DSA_MQ_CHUNK;               // keys per workgroup
 constexpr int kMqDma = kMqTile / 8;                  // 1 KB direct-to-LDS loads per tile
-
-__device__ __forceinline__ int mq_off(int row, int chunk16) {   // chunk16 in 0..7 of a 128 B row
-  return row * 128 + 16 * (chunk16 ^ ((row >> 1) & 7));
-}
+constexpr int kMqWaves = 8;                          // query tokens per workgroup
+static_assert(kMqChunk % kMqTile == 0 && kMqDma % kMqWaves == 0, "tile shape");
 
 template <int VM>
 __device__ __forceinline__ void mq_wait() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void mq_wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-#ifndef DSA_MQ_QPW
-#define DSA_MQ_QPW 1
-#endif
-#ifndef DSA_MQ_WAVES
-#define DSA_MQ_WAVES 8
-#endif
+// p[c] holds, in lane 16g + j, the partial sum of lane group g for key j of group c. Returns in
+// lane 16c + j the sum over the four lane groups of p[c]. Two half-wave swaps put p[0] (p[1])
+// in the low and p[2] (p[3]) in the high half, each summed over g and g ^ 2; one swap of 16-lane
+// rows then pairs g with g ^ 1.
+__device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float x0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float x1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
 
-template <int HI, int NW, int QPW>
-__global__ __launch_bounds__(NW * 64) void index_score_multi_kernel(
+// How a tile load finds its 8 rows.
+enum MqRows { kRowsContiguous = 0, kRowsPaged = 1, kRowsPerLane = 2 };
+
+template <int HI, int ROWS>
+__global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, CacheView keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int n_qgroups, int n_chunks, float* __restrict__ scores) {
   constexpr int MT = HI / 16;
-  constexpr int QG = QPW * NW;                        // query tokens per workgroup
+  constexpr int kG = kMqTile / 16;                    // 16-key groups per tile
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kMqStages][kMqTile * kDi];
   __shared__ int pmax_lds;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   // work item = (b, chunk, query group), query group fastest: groups sharing keys run together
   const int item = blockIdx.x;
@@ -226,69 +244,72 @@ __global__ __launch_bounds__(NW * 64) void index_score_multi_kernel(
   const int t0 = chunk * kMqChunk;
   const int t1 = min(t0 + kMqChunk, L_max);
 
-  // this wave's query tokens
-  int jq[QPW], pq[QPW];
-  bool live[QPW];
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) {
-    jq[qi] = qg * QG + QPW * wave + qi;
-    live[qi] = jq[qi] < Q;
-    pq[qi] = live[qi] ? min(query_pos(seq_lens, q_pos, in_Q, b, jq[qi]), L_max - 1) : -1;
-  }
+  const int jq = qg * kMqWaves + wave;
+  const bool live = jq < Q;
+  const int pq = live ? min(query_pos(seq_lens, q_pos, in_Q, b, jq), L_max - 1) : -1;
   if (threadIdx.x == 0) pmax_lds = -1;
   __syncthreads();
-  int pw = -1;
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) pw = max(pw, pq[qi]);
-  if (lane == 0) atomicMax(&pmax_lds, pw);
+  if (lane == 0) atomicMax(&pmax_lds, pq);
   __syncthreads();
-  const int pmax = pmax_lds;                           // keys after it are never loaded
+  const int pmax = __builtin_amdgcn_readfirstlane(pmax_lds);   // keys after it are never loaded
   const int t_load_end = min(t1, pmax + 1);
   const int n_tiles = t_load_end > t0 ? (t_load_end - t0 + kMqTile - 1) / kMqTile : 0;
-  const int my_dma = (kMqDma - wave + NW - 1) / NW;
+  constexpr int my_dma = kMqDma / kMqWaves;
 
-  // Direct-to-LDS load of tile tt: load d covers rows 8d..8d+7; lane l lands row 8d + l/8,
-  // slot l%8, fetching the 16-byte chunk that the swizzle puts there. Rows past the last
-  // visible key read a valid dummy row; their scores are masked.
+  // Load d covers rows 8d..8d+7 of the tile: lane l lands in row 8d + l/8, slot l%8, and fetches
+  // the 16-byte chunk that the swizzle puts there. The row's swizzle term (row >> 1) & 7 equals
+  // (4 (d & 1) + l / 16) & 7, so the lane's offset from the 8-row base is one of two constants
+  // and the base is wave-uniform: the 8 rows lie in one page (page sizes are multiples of 16),
+  // or inside the sequence when the cache is contiguous and L_max % 8 == 0; otherwise each lane
+  // clamps its own row. Groups past the last visible key re-read the group that holds it.
+  const uint32_t lane_off0 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((lane >> 4) & 7));
+  const uint32_t lane_off1 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((4 + (lane >> 4)) & 7));
+  const int last_group = pmax & ~7;
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)keys.table;     // read-only: scalar loads
   auto issue_tile = [&](int tt) {
-    uint8_t* base = ring[tt % kMqStages];
-    for (int d = wave; d < kMqDma; d += NW) {
-      const int row = 8 * d + (lane >> 3);
-      const int t = t0 + tt * kMqTile + row;
-      const uint8_t* src = keys.base;
-      if (t <= pmax) src = keys.row(b, t);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c),
-                                       (__attribute__((address_space(3))) void*)(base + d * 1024), 16, 0, 0);
+    uint8_t* lds = ring[tt % kMqStages];
+#pragma unroll
+    for (int i = 0; i < my_dma; ++i) {
+      const int d = wave + kMqWaves * i;
+      const int tr = min(t0 + tt * kMqTile + 8 * d, last_group);
+      const uint32_t off = (d & 1) ? lane_off1 : lane_off0;
+      const uint8_t* src;
+      if constexpr (ROWS == kRowsContiguous) {
+        src = keys.base + ((int64_t)b * L_max + tr) * kDi + off;
+      } else if constexpr (ROWS == kRowsPaged) {
+        const int page = table[(int64_t)b * keys.max_pages + tr / keys.page_size];
+        src = keys.base + ((int64_t)page * keys.page_size + tr % keys.page_size) * kDi + off;
+      } else {
+        const int t = min(tr + (lane >> 3), pmax);
+        src = keys.base + ((int64_t)b * L_max + t) * kDi + (off & 127u);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lds + d * 1024),
+                                       16, 0, 0);
     }
   };
 
-  // query operands (A rows = heads 16m + c16) and weights of heads 16m + 4g + r
-  v8i qa[QPW][MT];
-  float wr[QPW][MT][4];
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) {
-    const int jj = live[qi] ? jq[qi] : 0;
+  // A operands: rows = heads 16m + c16, lane group g holds bytes [16g,+16) and [64+16g,+16);
+  // weights of the heads 16m + 4g + r that the accumulator registers hold.
+  v8i qa[MT];
+  float wr[MT][4];
+  {
+    const int jj = live ? jq : 0;
     const uint8_t* qrow = q + ((int64_t)b * in_Q + jj) * HI * kDi;
     const float* wrow = w + ((int64_t)b * in_Q + jj) * HI;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const uint8_t* hp = qrow + (16 * m + c16) * kDi;
       const v4i lo4 = *(const v4i*)(hp + 16 * g), hi4 = *(const v4i*)(hp + 64 + 16 * g);
-      qa[qi][m] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      qa[m] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wr[qi][m][r] = wrow[16 * m + 4 * g + r];
+      for (int r = 0; r < 4; ++r) wr[m][r] = wrow[16 * m + 4 * g + r];
     }
   }
-  float* srow[QPW];
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) srow[qi] = scores + ((int64_t)b * Q + (live[qi] ? jq[qi] : 0)) * L_max;
-
+  float* srow = scores + ((int64_t)b * Q + (live ? jq : 0)) * L_max;
   // scores of keys in this chunk that no tile covers (after pmax): -inf
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi)
-    if (live[qi])
-      for (int t = max(t0, t_load_end) + lane; t < t1; t += kWave) srow[qi][t] = -INFINITY;
+  if (live)
+    for (int t = max(t0, t_load_end) + lane; t < t1; t += kWave) srow[t] = -INFINITY;
 
   // prefetch distance: kMqStages - 1 tiles are in flight while one is computed
   constexpr int kAhead = kMqStages - 1;
@@ -297,14 +318,20 @@ __global__ __launch_bounds__(NW * 64) void index_score_multi_kernel(
   for (int a = 0; a < kAhead; ++a)
     if (a < n_tiles) issue_tile(a);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const int b_lo = mq_off(c16, g), b_hi = mq_off(c16, g + 4);   // per-lane fragment offsets in a 16-row group
+  // per-lane B fragment offsets in a 16-row group (the swizzle repeats every 16 rows)
+  const int b_lo = c16 * 128 + 16 * (g ^ ((c16 >> 1) & 7));
+  const int b_hi = c16 * 128 + 16 * ((g + 4) ^ ((c16 >> 1) & 7));
   for (int tt = 0; tt < n_tiles; ++tt) {
     // tile tt has landed once only the later tiles' loads (at most kAhead - 1 tiles) are in flight
     const int later = min(kAhead - 1, n_tiles - 1 - tt) * my_dma;
     switch (later) {
+      case 1: mq_wait<1>(); break;
       case 2: mq_wait<2>(); break;
+      case 3: mq_wait<3>(); break;
       case 4: mq_wait<4>(); break;
+      case 6: mq_wait<6>(); break;
       case 8: mq_wait<8>(); break;
+      case 12: mq_wait<12>(); break;
       case 16: mq_wait<16>(); break;
       default: mq_wait<0>(); break;
     }
@@ -313,81 +340,79 @@ __global__ __launch_bounds__(NW * 64) void index_score_multi_kernel(
     if (tt + kAhead < n_tiles) issue_tile(tt + kAhead);
     const uint8_t* tile = ring[tt % kMqStages];
     const int tb = t0 + tt * kMqTile;
-    // 4 blocks of 64 keys; each block: 4 groups of 16 keys, reduce-scatter, one store per query
-#pragma unroll 1
-    for (int blk = 0; blk < kMqTile / 64; ++blk) {
-      const int tk0 = tb + 64 * blk;
-      if (tk0 > pmax) break;                          // block-uniform
-      // matrix-core products of group c+1 are issued before the epilogue of group c consumes
-      // its results, so the FP8 pipe and the ReLU / FMA epilogue overlap within the wave
-      float part[QPW][4];
-      v4f acc[2][QPW][MT];
-      auto products = [&](int c, v4f (&a)[QPW][MT]) {
-        const uint8_t* gp = tile + (64 * blk + 16 * c) * 128;   // 16-row group: the swizzle repeats every 16 rows
-        const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
-        const v8i bk = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    auto frag = [&](int gi) {
+      const uint8_t* gp = tile + gi * 16 * 128;
+      const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
+      return (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    // Software pipeline over the tile's groups: the products of group gi + 1 share a scheduling
+    // region with the epilogue of group gi (issued a full group earlier, so no epilogue
+    // instruction waits on a product in flight), and B fragments are read two groups ahead.
+    // Keys after pmax inside the last tile are computed on valid rows and stored as -inf.
+    v4f acc[2][MT];
+    v8i bk_next = frag(1);
+    {
+      const v8i bk0 = frag(0);
 #pragma unroll
-        for (int qi = 0; qi < QPW; ++qi)
+      for (int m = 0; m < MT; ++m) acc[0][m] = mfma_fp8(qa[m], bk0, zero);
+    }
+    float part[4];
 #pragma unroll
-          for (int m = 0; m < MT; ++m) a[qi][m] = mfma_fp8(qa[qi][m], bk, zero);
-      };
-      products(0, acc[0]);
+    for (int gi = 0; gi < kG; ++gi) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (gi + 1 < kG) {
+        const v8i bk_after = frag(gi + 2 < kG ? gi + 2 : gi + 1);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c + 1 < 4) products(c + 1, acc[(c + 1) & 1]);
-#pragma unroll
-        for (int qi = 0; qi < QPW; ++qi) {
-          float sum = 0.f;
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sum += wr[qi][m][r] * relu(acc[c & 1][qi][m][r]);
-          part[qi][c] = sum;
-        }
+        for (int m = 0; m < MT; ++m) acc[(gi + 1) & 1][m] = mfma_fp8(qa[m], bk_next, zero);
+        bk_next = bk_after;
       }
+      float sum = 0.f;
 #pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        const bool lo = g < 2;
-        const float r0 = shfl_xor(lo ? part[qi][2] : part[qi][0], 32);
-        const float r1 = shfl_xor(lo ? part[qi][3] : part[qi][1], 32);
-        const float x0 = (lo ? part[qi][0] : part[qi][2]) + r0;
-        const float x1 = (lo ? part[qi][1] : part[qi][3]) + r1;
-        const bool odd = g & 1;
-        const float r2 = shfl_xor(odd ? x0 : x1, 16);
-        const float v = (odd ? x1 : x0) + r2;
-        const int tk = tk0 + lane;
-        if (live[qi] && tk < t1) srow[qi][tk] = (tk <= pq[qi]) ? v : -INFINITY;
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum += wr[m][r] * relu(acc[gi & 1][m][r]);
+      part[gi & 3] = sum;
+#if DSA_MQ_SCHED
+      if (gi + 2 < kG) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next-but-one fragment
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one product
+        __builtin_amdgcn_sched_group_barrier(0x002, DSA_MQ_SCHED, 0);         // then VALU
+      }
+#endif
+      if ((gi & 3) == 3) {
+        const float v = reduce_scatter4(part);        // lane 16c + j: key j of group c
+        const int tk = tb + 64 * (gi >> 2) + lane;
+        if (live && tk < t1) srow[tk] = (tk <= pq) ? v : -INFINITY;
       }
     }
-    // keys of this tile after pmax (the loop broke early): -inf
-    for (int qi = 0; qi < QPW; ++qi)
-      if (live[qi])
-        for (int t = max(tb, pmax + 1) + lane; t < min(tb + kMqTile, t1); t += kWave) srow[qi][t] = -INFINITY;
   }
 }
 
-template <int HI, int NW, int QPW>
+template <int HI, int ROWS>
 static void launch_multi(const HostBatch& bt, const uint8_t* q, const float* w, const CacheView& kv, float* scores,
                          hipStream_t s) {
-  const int qgroups = (bt.Q + QPW * NW - 1) / (QPW * NW);
+  const int qgroups = (bt.Q + kMqWaves - 1) / kMqWaves;
   const int n_chunks = (bt.L_max + kMqChunk - 1) / kMqChunk;
-  const dim3 grid((unsigned)bt.B * n_chunks * qgroups), block(NW * 64);
-  hipLaunchKernelGGL((index_score_multi_kernel<HI, NW, QPW>), grid, block, 0, s, q, w, kv, bt.seq_lens, bt.q_pos,
-                     bt.Q, bt.in_Q, qgroups, n_chunks, scores);
+  const dim3 grid((unsigned)bt.B * n_chunks * qgroups), block(kMqWaves * 64);
+  hipLaunchKernelGGL((index_score_multi_kernel<HI, ROWS>), grid, block, 0, s, q, w, kv, bt.seq_lens, bt.q_pos, bt.Q,
+                     bt.in_Q, qgroups, n_chunks, scores);
+}
+
+template <int HI>
+static void launch_multi_rows(const HostBatch& bt, const uint8_t* q, const float* w, const CacheView& kv,
+                              float* scores, hipStream_t s) {
+  if (kv.table != nullptr) launch_multi<HI, kRowsPaged>(bt, q, w, kv, scores, s);
+  else if (bt.L_max % 8 == 0) launch_multi<HI, kRowsContiguous>(bt, q, w, kv, scores, s);
+  else launch_multi<HI, kRowsPerLane>(bt, q, w, kv, scores, s);
 }
 
 hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float* w, int Hi,
                               const HostCache& keys, float* scores, hipStream_t s) {
   CacheView kv{(const uint8_t*)keys.base, keys.table, keys.max_pages, keys.page_size, kDi, bt.L_max};
   if (bt.Q >= 2) {
-    // up to 8 query tokens: one per wave of an 8-wave workgroup; more: DSA_MQ_QPW per wave
-    if (Hi == 64) {
-      if (bt.Q > 8) launch_multi<64, DSA_MQ_WAVES, DSA_MQ_QPW>(bt, q, w, kv, scores, s);
-      else launch_multi<64, 8, 1>(bt, q, w, kv, scores, s);
-    } else {
-      if (bt.Q > 8) launch_multi<32, DSA_MQ_WAVES, DSA_MQ_QPW>(bt, q, w, kv, scores, s);
-      else launch_multi<32, 8, 1>(bt, q, w, kv, scores, s);
-    }
+    if (Hi == 64) launch_multi_rows<64>(bt, q, w, kv, scores, s);
+    else launch_multi_rows<32>(bt, q, w, kv, scores, s);
     return hipGetLastError();
   }
   const int n_chunks = (bt.L_max + kScoreChunk - 1) / kScoreChunk;
