@@ -4,16 +4,21 @@
 // attention path). Every head of a query attends the same gathered rows:
 //   z_i = scale * q_h . c_i (576 dims), o_h = sum_i softmax(z)_i c_i[0:512], lse_h = log sum exp z.
 //
-// One workgroup = one query token x 64 heads (4 waves x 16 heads) x one split of the selected
-// tokens. Per step of 32 tokens the workgroup gathers the 32 rows (1152 B each, through the
-// index list and the block table) into a token-major LDS tile, then each wave runs
+// One workgroup = one query token x all H heads (4 waves, one per SIMD, 32 heads each at
+// H = 128) x one split of the selected tokens. Per step of 32 tokens the workgroup gathers the
+// 32 rows (1152 B each, through the index list and the block table) into a token-major LDS
+// tile, then each wave runs, for each of its 16-head tiles,
 //   S^T[32 tok x 16 heads] = K_tile . Q^T      (bf16 16x16x32 matrix cores, K = 576)
-// with its 16 query heads held in registers as the B operand. S^T's accumulator layout
-// (lane = head, 4 tokens per register) is exactly the A-operand layout that P needs for
+// with its query heads held in registers as the B operands: every K fragment read from LDS
+// feeds both head tiles. S^T's accumulator layout (lane = head, 4 tokens per register) is
+// exactly the A-operand layout that P needs for
 //   O[16 heads x 512] += P . V                 (bf16 16x16x32 matrix cores, K = 32 tokens)
 // once the K order of V matches: V's B operand is read straight from the same token-major
-// tile with the LDS transpose read (ds_read_b64_tr_b16), tokens permuted to P's order.
-// The online softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV.
+// tile with the LDS transpose read (ds_read_b64_tr_b16), tokens permuted to P's order, and
+// every V fragment also feeds both head tiles. The 32-head output accumulator (256 registers)
+// lives in the matrix-core accumulator registers; it is only ever written by products, which
+// is why the softmax keeps one reference per head instead of rescaling O (see the kernel).
+// The softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV.
 // With several splits, each workgroup writes its normalised partial (o_s, lse_s) and a
 // combine kernel merges them: lse = log sum_s exp lse_s, o = sum_s exp(lse_s - lse) o_s.
 #include "dsa_device.h"
@@ -25,10 +30,17 @@ constexpr int kTok = 32;                        // tokens per step
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kSegs = kRowBytes / 128;          // 9 segments of 128 B per row
 constexpr int kTileBytes = kTok * kRowBytes;    // 36 KB per step
-constexpr int kStages = 3;                      // LDS ring depth: rows land two steps ahead
+#ifndef DSA_MLA_STAGES
+#define DSA_MLA_STAGES 3
+#endif
+constexpr int kStages = DSA_MLA_STAGES;         // LDS ring depth: rows land kStages - 1 steps ahead
+#ifndef DSA_MLA_AHEAD
+#define DSA_MLA_AHEAD 2
+#endif
+constexpr int kMlaAhead = DSA_MLA_AHEAD;        // LDS fragments read ahead of their products
+constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyRescale = 8.f;             // rescale O only when a head's max grows by > 2^8
 
 #ifndef DSA_MLA_PART_BF16
 #define DSA_MLA_PART_BF16 1
@@ -94,12 +106,15 @@ __device__ __forceinline__ void wait_step(int pending) {
     case 0: wait_counts<0, 15>(); break;
     case 4: wait_counts<4, 15>(); break;
     case 5: wait_counts<5, 15>(); break;
+    case 8: wait_counts<8, 15>(); break;
     case 9: wait_counts<9, 15>(); break;
+    case 10: wait_counts<10, 15>(); break;
+    case 18: wait_counts<18, 15>(); break;
     default: wait_counts<0, 15>(); break;
   }
 }
 
-template <int NW, bool SPLIT>
+template <int NW, int HT, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, CacheView lat, const int32_t* __restrict__ idx, int k, int idx_q_stride,
     int Q, int H, int splits, int split_len, float scale_log2,
@@ -107,21 +122,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kTileBytes];
   __shared__ int rowid[kMaxK];
+  __shared__ int redo_any;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int split = blockIdx.x % splits;
   const int bq = blockIdx.x / splits;
   const int b = bq / Q, j = bq - b * Q;
-  const int h0 = wave * 16;                            // this wave's 16 heads
-  const int my_dma = (kDmaPerStep - wave + NW - 1) / NW;   // loads this wave issues per step
+  const int h0 = wave * 16 * HT;                       // this wave's heads: tile ht = h0 + 16 ht ..
+  constexpr int my_dma = kSegs;                        // loads this wave issues per step
 
   const int32_t* irow = idx + (int64_t)b * (idx_q_stride ? (int64_t)Q * k : k) + (int64_t)j * idx_q_stride;
   const int tok_begin = split * split_len;
   const int tok_end = min(k, tok_begin + split_len);
   const int n_steps = tok_end > tok_begin ? (tok_end - tok_begin + kTok - 1) / kTok : 0;
 
+  // query heads h0 + 16 ht + (l % 16) as the B operands of S^T = K . Q^T: 8 dims per lane per K step;
+  // issued first: they do not depend on the index list
+  v8bf qb[HT][kDqk / 32];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint16_t* qrow = q + ((int64_t)bq * H + h0 + 16 * ht + c16) * kDqk;
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s) qb[ht][s] = *(const v8bf*)(qrow + 32 * s + 8 * g);
+  }
+
   // row index (into the cache's rows) of every token of the split, -1 for masked tokens
+  if (tid == 0) redo_any = 0;
   for (int i = tid; i < n_steps * kTok; i += NW * 64) {
     const int t = tok_begin + i;
     const int pos = t < tok_end ? irow[t] : -1;
@@ -135,40 +162,26 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 
   // Direct-to-LDS gather of step st: load d = (row group rg = d % 4, segment d / 4) lands rows
   // 8rg + l/8, slot l%8 of the segment, fetching the chunk that the swizzle puts there.
-  // Loads are dealt round-robin over the waves.
+  // Loads are dealt round-robin over the waves; with 4 waves, wave w issues exactly the 9
+  // segments of row group w, so one row id per lane serves all of its loads of a step.
+  static_assert(NW == 4, "loads of a wave share one row group");
+  const int my_row = 8 * wave + (lane >> 3);
   auto issue_step = [&](int st) {
-    uint8_t* base = ring[st % kStages];
-    for (int d = wave; d < kDmaPerStep; d += NW) {
-      const int rg = d & 3, sg = d >> 2;
-      const int row = 8 * rg + (lane >> 3);
-      const int r = rowid[st * kTok + row];
-      const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0);
-      const int chunk = 8 * sg + ((lane & 7) ^ ((row >> 1) & 7));
-      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * chunk),
-                                       (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128) + rg * 1024),
-                                       16, 0, 0);
-    }
+    uint8_t* base = ring[st % kStages] + wave * 1024;
+    const int r = rowid[st * kTok + my_row];
+    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0) + 16 * ((lane & 7) ^ ((my_row >> 1) & 7));
+#pragma unroll
+    for (int sg = 0; sg < kSegs; ++sg)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
+                                       (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128)), 16, 0, 0);
   };
   // masked rows this wave landed: overwrite the dummy bytes with zeros
   auto zero_masked = [&](int st) {
-    uint8_t* base = ring[st % kStages];
-    for (int d = wave; d < kDmaPerStep; d += NW) {
-      const int rg = d & 3, sg = d >> 2;
-      const int row = 8 * rg + (lane >> 3);
-      if (rowid[st * kTok + row] < 0) *(v4i*)(base + sg * (kTok * 128) + rg * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
-    }
+    if (rowid[st * kTok + my_row] >= 0) return;
+    uint8_t* base = ring[st % kStages] + wave * 1024;
+#pragma unroll
+    for (int sg = 0; sg < kSegs; ++sg) *(v4i*)(base + sg * (kTok * 128) + 16 * lane) = (v4i){0, 0, 0, 0};
   };
-
-  // query heads h0 + (l % 16) as the B operand of S^T = K . Q^T: 8 dims per lane per K step
-  v8bf qb[kDqk / 32];
-  const uint16_t* qrow = q + ((int64_t)bq * H + h0 + c16) * kDqk;
-#pragma unroll
-  for (int s = 0; s < kDqk / 32; ++s) qb[s] = *(const v8bf*)(qrow + 32 * s + 8 * g);
-  v4f o[kDv / 16];
-#pragma unroll
-  for (int nt = 0; nt < kDv / 16; ++nt) o[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // reference max (log2 domain) of head h0 + c16
-  float l_run = 0.f;         // this lane's share of its softmax denominator
 
   // Per-lane LDS offsets inside a tile. Chunk c of row r sits at segment c/8, slot
   // (c & 7) ^ ((r >> 1) & 7); for the fragments below the slot varies only in bits the XOR
@@ -182,117 +195,155 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   for (int hf = 0; hf < 2; ++hf)
     pv_base[hf] = tile_off(4 * g + (c16 >> 2) + 16 * hf, (c16 & 3) >> 1) + 8 * (c16 & 1);
 
-  if (n_steps > 0) issue_step(0);
-  if (n_steps > 1) issue_step(1);
-  for (int st = 0; st < n_steps; ++st) {
-    wait_step(st + 1 < n_steps ? my_dma : 0);       // this step's rows have landed
-    zero_masked(st);
-    wait_counts<63, 0>();                            // LDS writes done before the barrier
-    __builtin_amdgcn_s_barrier();
-    if (st + 2 < n_steps) issue_step(st + 2);        // its slot was last read in step st - 1
-    const uint8_t* tile = ring[st % kStages];
+  // Softmax reference. Every head keeps one reference m_ref (log2 domain) for the whole split:
+  // the maximum of the first step that has a visible token. P = 2^(z - m_ref) may exceed 1
+  // (fp32 and bf16 hold up to 2^127), so the accumulator O is never rescaled and is touched
+  // only by matrix-core products. Should a later logit exceed m_ref by more than
+  // kRefHeadroom, the split is computed again with m_ref = the exact maximum of its logits,
+  // which the first pass records.
+  v4f o[HT][kDv / 16];
+  float m_ref[HT], m_max[HT], l_run[HT];
+  bool redo = false;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) m_max[ht] = -INFINITY;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      if (!redo_any) break;                            // workgroup-uniform
+      __syncthreads();                                 // every wave is done with the ring
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int nt = 0; nt < kDv / 16; ++nt) o[ht][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+      m_ref[ht] = pass == 0 ? -INFINITY : m_max[ht];
+      l_run[ht] = 0.f;
+    }
+    constexpr int kAheadSteps = kStages - 1;
+#pragma unroll
+    for (int a = 0; a < kAheadSteps; ++a)
+      if (a < n_steps) issue_step(a);
+    for (int st = 0; st < n_steps; ++st) {
+      wait_step(min(kAheadSteps - 1, n_steps - 1 - st) * my_dma);   // this step's rows have landed
+      zero_masked(st);
+      wait_counts<63, 0>();                            // LDS writes done before the barrier
+      __builtin_amdgcn_s_barrier();
+      if (st + kAheadSteps < n_steps) issue_step(st + kAheadSteps);   // its slot was last read in step st - 1
+      const uint8_t* tile = ring[st % kStages];
+      // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
+      const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
-    // ---- S^T = K_tile . Q^T over K = 576
-    v4f sacc[2];
+      // ---- S^T = K_tile . Q^T over K = 576: each K fragment feeds HT products; fragments are
+      // read kMlaAhead fragments ahead of their use
+      v4f sacc[HT][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sacc[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
-    {
-      // fragment i = (s = i / 2, mt = i % 2); the next fragment is read before the current product
-      auto kfrag = [&](int i) {
-        const int s2 = i >> 1, mt = i & 1;
-        return lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s2 & 1))) + (s2 >> 1) * (kTok * 128)));
-      };
-      v8bf cur = kfrag(0);
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int i = 0; i < 2 * (kDqk / 32); ++i) {
-        v8bf nxt;
-        if (i + 1 < 2 * (kDqk / 32)) nxt = kfrag(i + 1);
-        sacc[i & 1] = mfma_bf16(cur, qb[i >> 1], sacc[i & 1]);
-        cur = nxt;
+        for (int mt = 0; mt < 2; ++mt) sacc[ht][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+      {
+        auto kfrag = [&](int i) {
+          const int s2 = i >> 1, mt = i & 1;
+          return lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s2 & 1))) + (s2 >> 1) * (kTok * 128)));
+        };
+        constexpr int NF = 2 * (kDqk / 32);
+        v8bf kb[kMlaAhead];
+#pragma unroll
+        for (int i = 0; i < kMlaAhead; ++i) kb[i] = kfrag(i);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const v8bf cur = kb[i % kMlaAhead];
+          if (i + kMlaAhead < NF) kb[i % kMlaAhead] = kfrag(i + kMlaAhead);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) sacc[ht][i & 1] = mfma_bf16(cur, qb[ht][i >> 1], sacc[ht][i & 1]);
+        }
+      }
+      // ---- softmax weights of heads h0 + 16 ht + c16 over tokens 16mt + 4g + r
+      v8bf pa[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float z[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = (valid >> (16 * mt + 4 * g + r)) & 1u;
+            z[mt][r] = ok ? sacc[ht][mt][r] * scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, z[mt][r]);
+          }
+        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        m_max[ht] = fmaxf(m_max[ht], tmax);
+        if (m_ref[ht] == -INFINITY) m_ref[ht] = tmax;  // the first step with a visible token
+        redo |= tmax > m_ref[ht] + kRefHeadroom;
+        const float m_use = (m_ref[ht] == -INFINITY) ? 0.f : m_ref[ht];
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless here
+            const float pv = __builtin_amdgcn_exp2f(z[mt][r] - m_use);
+            psum += pv;
+            pa[ht][4 * mt + r] = (__bf16)pv;
+          }
+        l_run[ht] += psum;
+      }
+      // ---- O += P . V; V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4);
+      // each V fragment feeds HT products
+      {
+        auto vfrag = [&](int nt) {
+          const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
+          const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
+          return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        constexpr int NV = kDv / 16;
+        v8bf vb[kMlaAhead];
+#pragma unroll
+        for (int i = 0; i < kMlaAhead; ++i) vb[i] = vfrag(i);
+#pragma unroll
+        for (int nt = 0; nt < NV; ++nt) {
+          const v8bf cur = vb[nt % kMlaAhead];
+          if (nt + kMlaAhead < NV) vb[nt % kMlaAhead] = vfrag(nt + kMlaAhead);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_bf16(pa[ht], cur, o[ht][nt]);
+        }
       }
     }
-    // ---- online softmax of head h0 + c16 over tokens 16mt + 4g + r
-    float z[2][4];
-    float tmax = -INFINITY;
+    if (pass == 0) {
+      if (__ballot(redo) != 0ull && lane == 0) atomicOr(&redo_any, 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- finish: denominators of heads h0 + 16 ht + c16, then per accumulator head h0 + 16 ht + 4g + r
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int ht = 0; ht < HT; ++ht) {
+    float l_tot = l_run[ht] + shfl_xor(l_run[ht], 16);
+    l_tot += shfl_xor(l_tot, 32);
+    const float lse_h = (l_tot > 0.f) ? (m_ref[ht] + log2f(l_tot)) * kLn2 : -INFINITY;
+    float inv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = rowid[st * kTok + 16 * mt + 4 * g + r] >= 0;
-        z[mt][r] = ok ? sacc[mt][r] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, z[mt][r]);
-      }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    // lazy reference max: exp2(z - m_ref) stays <= 2^8, exact enough in fp32 / bf16
-    const float m_ref = (tmax > m_run + kLazyRescale) ? tmax : m_run;
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless for softmax weights
-    const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);   // O is 0 at -inf
-    float psum = 0.f;
-    v8bf pa;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(z[mt][r] - m_use);
-        psum += pv;
-        pa[4 * mt + r] = (__bf16)pv;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_ref;
-    if (__ballot(alpha != 1.f) != 0ull) {       // wave-uniform and rare: a head's max jumped by > 2^8
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(l_tot, 4 * g + r, 64);
+      inv[r] = lr > 0.f ? 1.f / lr : 0.f;
+    }
+    const int hb = h0 + 16 * ht;
+    if (SPLIT) {
+      const int64_t ps = (int64_t)bq * splits + split;
+      part_t* pbase = part_o + (ps * H + hb) * kDv;
+      if (g == 0) part_lse[ps * H + hb + c16] = lse_h;
 #pragma unroll
       for (int nt = 0; nt < kDv / 16; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
+        for (int r = 0; r < 4; ++r) pbase[(4 * g + r) * kDv + 16 * nt + c16] = (part_t)(o[ht][nt][r] * inv[r]);
+    } else {
+      float* obase = out + ((int64_t)bq * H + hb) * kDv;
+      if (g == 0 && lse_out) lse_out[(int64_t)bq * H + hb + c16] = lse_h;
+#pragma unroll
+      for (int nt = 0; nt < kDv / 16; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) obase[(4 * g + r) * kDv + 16 * nt + c16] = o[ht][nt][r] * inv[r];
     }
-    // ---- O += P . V; V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4)
-    {
-      auto vfrag = [&](int nt) {
-        const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-        const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-        return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      v8bf cur = vfrag(0);
-#pragma unroll
-      for (int nt = 0; nt < kDv / 16; ++nt) {
-        v8bf nxt;
-        if (nt + 1 < kDv / 16) nxt = vfrag(nt + 1);
-        o[nt] = mfma_bf16(pa, cur, o[nt]);
-        cur = nxt;
-      }
-    }
-  }
-
-  // ---- finish: denominator of head h0 + c16, then per accumulator head h0 + 4g + r
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
-  const float lse_h = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  float inv[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float lr = __shfl(l_tot, 4 * g + r, 64);
-    inv[r] = lr > 0.f ? 1.f / lr : 0.f;
-  }
-  if (SPLIT) {
-    const int64_t ps = (int64_t)bq * splits + split;
-    part_t* pbase = part_o + (ps * H + h0) * kDv;
-    if (g == 0) part_lse[ps * H + h0 + c16] = lse_h;
-#pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pbase[(4 * g + r) * kDv + 16 * nt + c16] = (part_t)(o[nt][r] * inv[r]);
-  } else {
-    float* obase = out + ((int64_t)bq * H + h0) * kDv;
-    if (g == 0 && lse_out) lse_out[(int64_t)bq * H + h0 + c16] = lse_h;
-#pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) obase[(4 * g + r) * kDv + 16 * nt + c16] = o[nt][r] * inv[r];
   }
 }
 
@@ -322,16 +373,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const part_t* __restri
   if (t == 0 && lse_out) lse_out[(int64_t)bq * H + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(den);
 }
 
-template <int NW>
-static void launch_mla(int splits, dim3 grid, hipStream_t s, const uint16_t* q, CacheView lv, const int32_t* idx,
+template <int NW, int HT>
+static void launch_mla(int splits, int n_items, hipStream_t s, const uint16_t* q, CacheView lv, const int32_t* idx,
                        int k, int idx_q_stride, int Q, int H, int split_len, float sl2, float* out, float* lse,
                        part_t* part_o, float* part_lse) {
-  const dim3 block(NW * 64);
+  const dim3 block(NW * 64), grid((unsigned)n_items);
   if (splits == 1)
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, false>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, 1,
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, 1,
                        split_len, sl2, out, lse, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, true>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, splits,
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, splits,
                        split_len, sl2, nullptr, nullptr, part_o, part_lse);
 }
 
@@ -343,7 +394,7 @@ hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, cons
   const int splits = sparse_mla_splits(rows, H, k);
   int split_len = (k + splits - 1) / splits;
   split_len = (split_len + kTok - 1) / kTok * kTok;
-  const dim3 grid((unsigned)rows * splits);
+  const int n_items = rows * splits;
   const float sl2 = scale * kLog2e;
   part_t* part_o = nullptr;
   float* part_lse = nullptr;
@@ -351,10 +402,13 @@ hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, cons
     part_o = (part_t*)ws;
     part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(part_t)));
   }
+  // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64)
   if (H == 128)
-    launch_mla<8>(splits, grid, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o, part_lse);
+    launch_mla<4, 2>(splits, n_items, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o,
+                     part_lse);
   else
-    launch_mla<4>(splits, grid, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o, part_lse);
+    launch_mla<4, 1>(splits, n_items, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o,
+                     part_lse);
   if (splits > 1)
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2)), dim3(256), 0, s, part_o, part_lse, H,
                        splits, out, lse);

@@ -205,6 +205,30 @@ def test_sparse_mla_on_oracle_indices(name, kw):
     print(f"{name}: max abs {worst[0]:.3g} rel L2 {worst[1]:.3g}")
 
 
+@pytest.mark.parametrize("H", [128, 64])
+def test_sparse_mla_logit_jumps_after_the_first_step(H):
+    """Each split keeps one softmax reference per head, taken in its first step with a visible
+    token. Late tokens whose logits exceed it: by about 30 binades (weights above 1, no rerun),
+    by about 130 binades (beyond the headroom: the split is computed again with its exact
+    maximum), and a split whose first step is entirely masked."""
+    gen = torch.Generator().manual_seed(5)
+    B, L, k = 3, 4096, 2048
+    scale = 1.0 / 576 ** 0.5
+    q = torch.randn((B, 1, H, 576), generator=gen).to(torch.bfloat16)
+    lat = torch.randn((B, L, 576), generator=gen).to(torch.bfloat16)
+    idx = torch.arange(k, dtype=torch.int32).repeat(B, 1, 1)
+    lat[0, 2040] = q[0, 0, 3]                                      # head 3: logit ~ 24
+    lat[1, 2040] = (4 * q[1, 0, 5].float()).to(torch.bfloat16)    # head 5: logit ~ 96
+    idx[2, 0, :40] = -1                                            # first step of split 0 masked
+    lat[2, 1000] = (3 * q[2, 0, 1].float()).to(torch.bfloat16)    # head 1: logit ~ 72
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    out, lse = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(lat.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(q), oracle.Cache(bits(lat)), idx.numpy(), scale)
+    for b in range(B):
+        check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0])
+
+
 def test_sparse_mla_shared_index_row_and_empty_sets():
     wl = synth.small("verify_b64_q8_32k", B=2, Q=4, L=2500, L_max=2560, k=512)
     cpu, g = gpu_batch(wl)
