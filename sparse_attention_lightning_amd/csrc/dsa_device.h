@@ -11,6 +11,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -59,6 +60,28 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// All-reduce of x over the lane pairs (l, l ^ 16) and (l, l ^ 32) with gfx950's lane swaps
+// (VALU, no LDS round trip). permlane16_swap(x, x) returns ([x0, x0, x2, x2], [x1, x1, x3, x3])
+// in 16-lane rows, permlane32_swap(x, x) returns ([x.lo, x.lo], [x.hi, x.hi]); combining the
+// two results of a swap pairs every lane with its partner. The operation is applied to the
+// same two operands in every lane, so both lanes of a pair hold the identical result.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // max(x, 0) as one integer max on the bit pattern: every negative float (sign bit set) is a
 // negative int32 and maps to +0; non-negative floats are unchanged. Unlike fmaxf it needs no

@@ -34,10 +34,10 @@ constexpr int kTileBytes = kTok * kRowBytes;    // 36 KB per step
 #define DSA_MLA_STAGES 3
 #endif
 constexpr int kStages = DSA_MLA_STAGES;         // LDS ring depth: rows land kStages - 1 steps ahead
-#ifndef DSA_MLA_AHEAD
-#define DSA_MLA_AHEAD 2
+#ifndef DSA_MLA_FRAG_BATCH
+#define DSA_MLA_FRAG_BATCH 2
 #endif
-constexpr int kMlaAhead = DSA_MLA_AHEAD;        // LDS fragments read ahead of their products
+constexpr int kFragBatch = DSA_MLA_FRAG_BATCH;  // LDS fragments per read batch
 constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -76,11 +76,23 @@ size_t sparse_mla_workspace_bytes(int rows, int H, int k) {
   return align256((size_t)rows * s * H * kDv * sizeof(part_t)) + align256((size_t)rows * s * H * sizeof(float));
 }
 
-__device__ __forceinline__ v8bf lds_v8bf(const uint8_t* p) { return *(const v8bf*)p; }
+typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
 
-__device__ __forceinline__ v4bf lds_tr_read(const uint8_t* lds_byte_ptr) {
+__device__ __forceinline__ v8bf lds_v8bf(lds_ptr p) { return *(const __attribute__((address_space(3))) v8bf*)p; }
+
+// An LDS pointer the compiler may not look through: fragment reads at this pointer plus a
+// constant then keep the constant in the instruction's offset field, instead of the compiler
+// merging it into the XOR-swizzled base (it turns the addition of disjoint bits into an OR,
+// which the offset field cannot absorb) and computing a fresh address per fragment.
+__device__ __forceinline__ lds_ptr opaque_lds(const uint8_t* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(lds_ptr)p;      // the 32-bit LDS address
+  asm volatile("" : "+v"(a));
+  return (lds_ptr)(uintptr_t)a;
+}
+
+__device__ __forceinline__ v4bf lds_tr_read(lds_ptr p) {
   typedef __attribute__((address_space(3))) v4bf lds_v4bf;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(lds_byte_ptr));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(p));
 }
 
 // LDS tile layout of one step: 9 segments of [32 rows][128 B]; inside a row segment the eight
@@ -232,80 +244,123 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
       const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
-      // ---- S^T = K_tile . Q^T over K = 576: each K fragment feeds HT products; fragments are
-      // read kMlaAhead fragments ahead of their use
+      // LDS fragment reads go in batches of kFragBatch, double-buffered: batch b + 1 is issued
+      // right after an explicit wait for batch b and lands while batch b's products run. (While a
+      // direct-to-LDS load is in flight the compiler waits for all LDS reads at every use, so
+      // the distance between a read and its wait is set here, by the order of the code.)
+      // ---- S^T = K_tile . Q^T over K = 576: each K fragment feeds HT products
       v4f sacc[HT][2];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) sacc[ht][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
       {
+        lds_ptr kb[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) kb[mt][x] = opaque_lds(tile + (qk_base[mt] ^ (64 * x)));
         auto kfrag = [&](int i) {
           const int s2 = i >> 1, mt = i & 1;
-          return lds_v8bf(tile + ((qk_base[mt] ^ (64 * (s2 & 1))) + (s2 >> 1) * (kTok * 128)));
+          return lds_v8bf(kb[mt][s2 & 1] + (s2 >> 1) * (kTok * 128));
         };
         constexpr int NF = 2 * (kDqk / 32);
-        v8bf kb[kMlaAhead];
+        static_assert(NF % kFragBatch == 0, "whole batches of K fragments");
+        v8bf kc[kFragBatch], kn[kFragBatch];
 #pragma unroll
-        for (int i = 0; i < kMlaAhead; ++i) kb[i] = kfrag(i);
+        for (int i = 0; i < kFragBatch; ++i) kc[i] = kfrag(i);
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const v8bf cur = kb[i % kMlaAhead];
-          if (i + kMlaAhead < NF) kb[i % kMlaAhead] = kfrag(i + kMlaAhead);
+        for (int bt = 0; bt < NF / kFragBatch; ++bt) {
+          wait_counts<63, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+          if (bt + 1 < NF / kFragBatch) {
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) sacc[ht][i & 1] = mfma_bf16(cur, qb[ht][i >> 1], sacc[ht][i & 1]);
+            for (int i = 0; i < kFragBatch; ++i) kn[i] = kfrag((bt + 1) * kFragBatch + i);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < kFragBatch; ++i) {
+            const int f = bt * kFragBatch + i;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) sacc[ht][f & 1] = mfma_bf16(kc[i], qb[ht][f >> 1], sacc[ht][f & 1]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < kFragBatch; ++i) kc[i] = kn[i];
         }
       }
-      // ---- softmax weights of heads h0 + 16 ht + c16 over tokens 16mt + 4g + r
+      // V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4); the first batch
+      // is issued before the softmax, which has no LDS traffic of its own
+      lds_ptr vb[2][4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vb[hf][x] = opaque_lds(tile + (pv_base[hf] ^ (32 * x)));
+      auto vfrag = [&](int nt) {
+        const v4bf lo = lds_tr_read(vb[0][nt & 3] + (nt >> 2) * (kTok * 128));
+        const v4bf hi = lds_tr_read(vb[1][nt & 3] + (nt >> 2) * (kTok * 128));
+        return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      v8bf vc[kFragBatch], vn[kFragBatch];
+#pragma unroll
+      for (int i = 0; i < kFragBatch; ++i) vc[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- softmax weights of heads h0 + 16 ht + c16 over tokens 16mt + 4g + r. The maximum is
+      // taken over the raw logits (the scale is positive, so it commutes with the maximum) and
+      // the scale is folded into the exponent's multiply-add; masked tokens (only in a step
+      // with -1 entries or past the end of the split) become -inf.
+      const bool all_valid = valid == 0xffffffffu;     // wave-uniform
       v8bf pa[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        float z[2][4];
-        float tmax = -INFINITY;
+        float z[8];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int i = 0; i < 8; ++i) z[i] = sacc[ht][i >> 2][i & 3];
+        if (!all_valid) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool ok = (valid >> (16 * mt + 4 * g + r)) & 1u;
-            z[mt][r] = ok ? sacc[ht][mt][r] * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, z[mt][r]);
-          }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+          for (int i = 0; i < 8; ++i)
+            if (!((valid >> (16 * (i >> 2) + 4 * g + (i & 3))) & 1u)) z[i] = -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+        tmax = max_xor32(max_xor16(tmax)) * scale_log2;
         m_max[ht] = fmaxf(m_max[ht], tmax);
         if (m_ref[ht] == -INFINITY) m_ref[ht] = tmax;  // the first step with a visible token
         redo |= tmax > m_ref[ht] + kRefHeadroom;
-        const float m_use = (m_ref[ht] == -INFINITY) ? 0.f : m_ref[ht];
+        const float neg_m = (m_ref[ht] == -INFINITY) ? 0.f : -m_ref[ht];
         float psum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless here
-            const float pv = __builtin_amdgcn_exp2f(z[mt][r] - m_use);
-            psum += pv;
-            pa[ht][4 * mt + r] = (__bf16)pv;
-          }
+        for (int i = 0; i < 8; ++i) {
+          // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless here
+          const float pv = __builtin_amdgcn_exp2f(fmaf(z[i], scale_log2, neg_m));
+          psum += pv;                                  // the denominator sums the fp32 weights
+          pa[ht][i] = (__bf16)pv;
+        }
         l_run[ht] += psum;
       }
-      // ---- O += P . V; V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4);
-      // each V fragment feeds HT products
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- O += P . V; each V fragment feeds HT products
       {
-        auto vfrag = [&](int nt) {
-          const v4bf lo = lds_tr_read(tile + ((pv_base[0] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-          const v4bf hi = lds_tr_read(tile + ((pv_base[1] ^ (32 * (nt & 3))) + (nt >> 2) * (kTok * 128)));
-          return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
         constexpr int NV = kDv / 16;
-        v8bf vb[kMlaAhead];
+        static_assert(NV % kFragBatch == 0, "whole batches of V fragments");
 #pragma unroll
-        for (int i = 0; i < kMlaAhead; ++i) vb[i] = vfrag(i);
+        for (int bt = 0; bt < NV / kFragBatch; ++bt) {
+          wait_counts<63, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+          if (bt + 1 < NV / kFragBatch) {
 #pragma unroll
-        for (int nt = 0; nt < NV; ++nt) {
-          const v8bf cur = vb[nt % kMlaAhead];
-          if (nt + kMlaAhead < NV) vb[nt % kMlaAhead] = vfrag(nt + kMlaAhead);
+            for (int i = 0; i < kFragBatch; ++i) vn[i] = vfrag((bt + 1) * kFragBatch + i);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_bf16(pa[ht], cur, o[ht][nt]);
+          for (int i = 0; i < kFragBatch; ++i) {
+            const int nt = bt * kFragBatch + i;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_bf16(pa[ht], vc[i], o[ht][nt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < kFragBatch; ++i) vc[i] = vn[i];
         }
       }
     }
@@ -318,8 +373,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   // ---- finish: denominators of heads h0 + 16 ht + c16, then per accumulator head h0 + 16 ht + 4g + r
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    float l_tot = l_run[ht] + shfl_xor(l_run[ht], 16);
-    l_tot += shfl_xor(l_tot, 32);
+    const float l_tot = sum_xor32(sum_xor16(l_run[ht]));
     const float lse_h = (l_tot > 0.f) ? (m_ref[ht] + log2f(l_tot)) * kLn2 : -INFINITY;
     float inv[4];
 #pragma unroll
