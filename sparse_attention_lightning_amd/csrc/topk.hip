@@ -2,10 +2,11 @@
 // highest-scoring tokens). Exact top-k on the order-preserving uint32 image of the fp32
 // scores; equal scores go to the lower position; output ascending, -1 padded.
 //
-// Two implementations with identical results. For small calls (decode, long-context share
-// groups) the chunked radix form (topk_radix.hip) keeps the chip busy; for large ones (prefill,
-// multi-token verification) the sampled form below reads the scores about once instead of five
-// times. Three launches:
+// Three implementations with identical results. Rows of up to 256K scores go to the row form
+// (one workgroup per row, one launch; further below). Longer rows (long-context share groups)
+// go to the chunked radix form (topk_radix.hip), which spreads a few long rows over the chip,
+// or for calls of more than 8M scores to the sampled form below, which reads the scores about
+// once instead of five times. The sampled form takes three launches:
 //   sample   one workgroup per row reads a block-strided sample (whole 64-byte lines, one
 //            16-score block in `stride`, stride <= k / 64 so that about 128 sampled scores are
 //            expected above the threshold) and radix-selects in LDS the key tau that about 2k
@@ -23,6 +24,8 @@
 // Rows with p + 1 <= k keep every visible token. Results are deterministic: the kept set is
 // defined by score and position alone, never by the order of the appends.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "dsa_device.h"
 #include "dsa_launch.h"
@@ -85,8 +88,10 @@ __device__ __forceinline__ TkRowInfo tk_row(const int32_t* seq_lens, const int32
   return ri;
 }
 
-// Block-wide exclusive scan of one uint32 per thread (256 threads); returns the total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* excl, uint32_t* lds4) {
+// Block-wide exclusive scan of one uint32 per thread (NT threads); returns the total.
+template <int NT = kTkThreads>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* excl, uint32_t* wsum) {
+  constexpr int NWV = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -94,12 +99,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* e
     const uint32_t y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  if (lane == 63) lds4[wave] = x;
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = lds4[i];
+  for (int i = 0; i < NWV; ++i) {
+    const uint32_t t = wsum[i];
     before += (i < wave) ? t : 0u;
     total += t;
   }
@@ -111,15 +116,17 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* e
 // Radix-select scratch shared by the helpers below (LDS).
 struct TkLds {
   uint32_t hist[4096];
-  uint32_t lds4[4];
+  uint32_t lds4[16];      // one partial sum per wave (up to 16 waves)
+  uint32_t mm[32];        // block min / max partials
   uint32_t res[2];
 };
 
 // The bin of hist[0..NB) holding the need-th largest element and how many are still needed
 // from it. Every thread of the block must call it.
-template <int NB>
+template <int NB, int NT = kTkThreads>
 __device__ __forceinline__ void find_bin(TkLds& L, int need, uint32_t& bin, int& rem) {
-  constexpr int PER = NB / kTkThreads;
+  constexpr int PER = NB / NT;
+  static_assert(PER >= 1 && NB % NT == 0, "whole bins per thread");
   if (threadIdx.x == 0) { L.res[0] = 0; L.res[1] = 0; }
   const int top = NB - PER * (int)threadIdx.x;
   uint32_t h[PER];
@@ -130,7 +137,7 @@ __device__ __forceinline__ void find_bin(TkLds& L, int need, uint32_t& bin, int&
     mine += h[e];
   }
   uint32_t above;
-  block_exclusive_scan(mine, &above, L.lds4);
+  block_exclusive_scan<NT>(mine, &above, L.lds4);
   uint32_t cum = above;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -146,24 +153,31 @@ __device__ __forceinline__ void find_bin(TkLds& L, int need, uint32_t& bin, int&
   __syncthreads();
 }
 
+template <int NT = kTkThreads>
 __device__ __forceinline__ void zero_hist(TkLds& L, int nb) {
-  for (int i = threadIdx.x; i < nb; i += kTkThreads) L.hist[i] = 0u;
+  for (int i = threadIdx.x; i < nb; i += NT) L.hist[i] = 0u;
   __syncthreads();
 }
 
 // Block-wide min and max of one uint32 per thread.
+template <int NT = kTkThreads>
 __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TkLds& L, uint32_t& out_lo, uint32_t& out_hi) {
+  constexpr int NWV = NT / 64;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
     hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
   }
   const int wave = threadIdx.x >> 6;
-  __shared__ uint32_t mm[8];
-  if ((threadIdx.x & 63) == 0) { mm[wave] = lo; mm[4 + wave] = hi; }
+  if ((threadIdx.x & 63) == 0) { L.mm[wave] = lo; L.mm[16 + wave] = hi; }
   __syncthreads();
-  out_lo = min(min(mm[0], mm[1]), min(mm[2], mm[3]));
-  out_hi = max(max(mm[4], mm[5]), max(mm[6], mm[7]));
+  out_lo = 0xFFFFFFFFu;
+  out_hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) {
+    out_lo = min(out_lo, L.mm[i]);
+    out_hi = max(out_hi, L.mm[16 + i]);
+  }
   __syncthreads();
 }
 
@@ -171,30 +185,30 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TkLds& L,
 // taken. The radix digits are taken from key - min over only the significant bits of the
 // observed range (up to 11 bits per level), so even tightly clustered keys spread over the
 // histogram instead of piling onto one or two LDS counters; equal keys need no level at all.
-template <typename KeyFn>
+template <int NT = kTkThreads, typename KeyFn>
 __device__ void select_key(TkLds& L, int n, int need, KeyFn key, uint32_t& T, int& rem) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = threadIdx.x; i < n; i += kTkThreads) {
+  for (int i = threadIdx.x; i < n; i += NT) {
     const uint32_t u = key(i);
     lo = min(lo, u);
     hi = max(hi, u);
   }
-  block_minmax(lo, hi, L, lo, hi);
+  block_minmax<NT>(lo, hi, L, lo, hi);
   const uint32_t span = hi - lo;
   int bits = span ? 32 - __clz((int)span) : 0;
   uint32_t prefix = 0;                    // offset bits resolved so far (those above `bits`)
   int nd = need;
   while (bits > 0) {                      // block-uniform
     const int w = min(11, bits), shift = bits - w;
-    zero_hist(L, 2048);
-    for (int i = threadIdx.x; i < n; i += kTkThreads) {
+    zero_hist<NT>(L, 2048);
+    for (int i = threadIdx.x; i < n; i += NT) {
       const uint32_t off = key(i) - lo;
       if ((uint32_t)((uint64_t)off >> bits) == prefix) atomicAdd(&L.hist[(off >> shift) & ((1u << w) - 1)], 1u);
     }
     __syncthreads();
     uint32_t b;
     int r;
-    find_bin<2048>(L, nd, b, r);
+    find_bin<2048, NT>(L, nd, b, r);
     prefix = (prefix << w) | b;
     nd = r;
     bits = shift;
@@ -204,20 +218,20 @@ __device__ void select_key(TkLds& L, int n, int need, KeyFn key, uint32_t& T, in
 }
 
 // The need-th largest 24-bit value v(i) among the i with use(i): two 12-bit levels.
-template <typename ValFn, typename UseFn>
+template <int NT = kTkThreads, typename ValFn, typename UseFn>
 __device__ uint32_t select_24(TkLds& L, int n, int need, ValFn v, UseFn use) {
   uint32_t b1, b2;
   int r1, r2;
-  zero_hist(L, 4096);
-  for (int i = threadIdx.x; i < n; i += kTkThreads)
+  zero_hist<NT>(L, 4096);
+  for (int i = threadIdx.x; i < n; i += NT)
     if (use(i)) atomicAdd(&L.hist[v(i) >> 12], 1u);
   __syncthreads();
-  find_bin<4096>(L, need, b1, r1);
-  zero_hist(L, 4096);
-  for (int i = threadIdx.x; i < n; i += kTkThreads)
+  find_bin<4096, NT>(L, need, b1, r1);
+  zero_hist<NT>(L, 4096);
+  for (int i = threadIdx.x; i < n; i += NT)
     if (use(i) && (v(i) >> 12) == b1) atomicAdd(&L.hist[v(i) & 0xFFF], 1u);
   __syncthreads();
-  find_bin<4096>(L, r1, b2, r2);
+  find_bin<4096, NT>(L, r1, b2, r2);
   return (b1 << 12) | b2;
 }
 
@@ -332,13 +346,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
 // ------------------------------------------------------------------------------------------ finish
 // Exact top-k of a whole row by one workgroup (the fallback): three histogram passes over the
 // row for T and the tie quota, then an ordered block-scan compaction in position order.
+template <int NT = kTkThreads>
 __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, int32_t* __restrict__ out, TkLds& L) {
   auto key_at = [&](int i) { return float_key(srow[i]); };
   uint32_t T;
   int rem;
-  select_key(L, n, k, key_at, T, rem);
+  select_key<NT>(L, n, k, key_at, T, rem);
   int gt_carry = 0, eq_carry = 0;
-  for (int base = 0; base < n; base += kTkThreads * 4) {
+  for (int base = 0; base < n; base += NT * 4) {
     const int i0 = base + 4 * (int)threadIdx.x;
     uint32_t fgt = 0, feq = 0;
 #pragma unroll
@@ -351,7 +366,7 @@ __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, i
     }
     const uint32_t packed = (uint32_t)__builtin_popcount(fgt) | ((uint32_t)__builtin_popcount(feq) << 16);
     uint32_t before;
-    const uint32_t tot = block_exclusive_scan(packed, &before, L.lds4);
+    const uint32_t tot = block_exclusive_scan<NT>(packed, &before, L.lds4);
     int g_b = gt_carry + (int)(before & 0xFFFF);
     int q_b = eq_carry + (int)(before >> 16);
 #pragma unroll
@@ -476,23 +491,422 @@ hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx,
 
 }  // namespace sampled
 
+// ------------------------------------------------------------------------------------------ rowsel
+// The same selection (sample -> tau -> candidates >= tau -> exact select -> ordered emission)
+// by one workgroup of 1024 threads per row in a single launch, with the candidate list in LDS
+// instead of global memory. It reads the row once plus an 8192-score sample, so it suits calls
+// with enough rows to fill the chip and rows short enough for one workgroup to stream. Being one
+// long chain of block-wide steps, it keeps each step short: wave scans and reductions by DPP
+// row shifts and broadcasts (no LDS round trip), one barrier per block scan, candidate keys held
+// in registers across the radix levels, and a double-buffered gather that compares the floats
+// against tau directly (float_key is monotone, so key >= tau is f >= the float of tau).
+namespace rowsel {
+
+constexpr int kRT = 1024;                  // threads per row workgroup
+constexpr int kRW = kRT / 64;              // waves
+constexpr int kRCap = 4096;                // candidates kept in LDS (2 x the largest k)
+constexpr int kRSample = 512;              // sampled 16-score blocks (8192 scores, 2 float4 per thread)
+constexpr int kRWindow = 1 << 17;          // positions per emission bitmap window (16 KB)
+constexpr int kRUnroll = 2;                // float4 per thread per gather pass (double-buffered)
+constexpr int kRBins = 4096;               // 12-bit radix levels
+constexpr int kRCPer = kRCap / kRT;        // candidate slots per thread
+static_assert(kRCap >= 2 * kMaxK, "room for about 1.5k candidates plus spread");
+static_assert(kRBins % kRT == 0, "whole bins per thread");
+
+struct RowLds {
+  union {
+    uint32_t skey[kRSample * 16];          // unused slot (the sample stays in registers)
+    struct {
+      uint32_t key[kRCap];                 // candidates: key and position
+      int pos[kRCap];
+    } c;
+  } u;
+  uint32_t bitmap[kRWindow / 32];
+  union {
+    uint32_t hist[2][kRBins];              // radix levels alternate between two histograms
+    sampled::TkLds full;                   // the exact full-row fallback
+  } h;
+  uint32_t wred[4][kRW];                   // per-wave partials, rotated over the block steps
+  uint32_t res[2];
+  uint32_t count;
+};
+
+// Wave-inclusive scans by DPP: row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15
+// and 31 carry the row totals across rows (lanes shifted in from outside a row read `id`).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWMASK, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_u32<0x111, 0xf>(x, id));
+  x = op(x, dpp_u32<0x112, 0xf>(x, id));
+  x = op(x, dpp_u32<0x114, 0xf>(x, id));
+  x = op(x, dpp_u32<0x118, 0xf>(x, id));
+  x = op(x, dpp_u32<0x142, 0xa>(x, id));
+  x = op(x, dpp_u32<0x143, 0xc>(x, id));
+  return x;
+}
+
+struct Blk {
+  RowLds& S;
+  int tid, lane, wave;
+  int slot = 0;                            // wred slot of the next block step
+  int cur = 0;                             // the histogram that is clean
+
+  // Exclusive prefix sum over the threads in order (one barrier); *total gets the block sum.
+  __device__ uint32_t scan(uint32_t v, uint32_t* total) {
+    uint32_t* w = S.wred[slot];
+    slot = (slot + 1) & 3;
+    const uint32_t x = wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+    if (lane == 63) w[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kRW; ++i) {
+      const uint32_t t = w[i];
+      before += i < wave ? t : 0u;
+      tot += t;
+    }
+    *total = tot;
+    return before + x - v;
+  }
+  __device__ uint32_t sum(uint32_t v) {
+    uint32_t t;
+    scan(v, &t);
+    return t;
+  }
+  // Block min and max (one barrier).
+  __device__ void minmax(uint32_t lo, uint32_t hi, uint32_t& olo, uint32_t& ohi) {
+    uint32_t* w = S.wred[slot];
+    slot = (slot + 2) & 3;
+    uint32_t* w2 = S.wred[(slot + 3) & 3];
+    lo = wave_incl_scan(lo, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
+    hi = wave_incl_scan(hi, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    if (lane == 63) { w[wave] = lo; w2[wave] = hi; }
+    __syncthreads();
+    olo = 0xFFFFFFFFu;
+    ohi = 0u;
+#pragma unroll
+    for (int i = 0; i < kRW; ++i) {
+      olo = min(olo, w[i]);
+      ohi = max(ohi, w2[i]);
+    }
+  }
+  // The bin of hist[cur] holding the need-th largest counted element, and how many are still
+  // needed from it (two barriers). Thread t owns bins [kRBins - 4(t+1), kRBins - 4t).
+  __device__ void find_bin(int need, uint32_t& bin, int& rem) {
+    constexpr int PER = kRBins / kRT;
+    const uint32_t* hist = S.h.hist[cur];
+    const int top = kRBins - PER * tid;
+    uint32_t h[PER], mine = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      h[e] = hist[top - 1 - e];
+      mine += h[e];
+    }
+    uint32_t tot;
+    uint32_t cum = scan(mine, &tot);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (cum < (uint32_t)need && (uint32_t)need <= cum + h[e]) {
+        S.res[0] = (uint32_t)(top - 1 - e);
+        S.res[1] = (uint32_t)(need - (int)cum);
+      }
+      cum += h[e];
+    }
+    __syncthreads();
+    bin = S.res[0];
+    rem = (int)S.res[1];
+  }
+  // Radix select over the keys k[i] with ok[i] of every thread: the need-th largest key (exact,
+  // and then *rem = how many keys equal to it are needed), or after at most two 12-bit levels a
+  // lower bound of it (the low edge of its bin). Digits come from key - min over the significant
+  // bits of the observed range.
+  template <int PER>
+  __device__ uint32_t select(const uint32_t (&k)[PER], const bool (&ok)[PER], int need, bool exact, int* rem) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (ok[e]) { lo = min(lo, k[e]); hi = max(hi, k[e]); }
+    minmax(lo, hi, lo, hi);
+    const uint32_t span = hi - lo;
+    int bits = span ? 32 - __clz((int)span) : 0;
+    uint32_t prefix = 0;
+    int nd = need;
+    for (int level = 0; bits > 0; ++level) {           // block-uniform
+      if (!exact && level == 2) break;
+      const int w = min(12, bits), shift = bits - w;
+      uint32_t* hist = S.h.hist[cur];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const uint32_t off = k[e] - lo;
+        if (ok[e] && (uint32_t)((uint64_t)off >> bits) == prefix) atomicAdd(&hist[(off >> shift) & ((1u << w) - 1)], 1u);
+      }
+      uint32_t* other = S.h.hist[cur ^ 1];
+      for (int i = tid; i < kRBins; i += kRT) other[i] = 0u;
+      __syncthreads();
+      uint32_t b;
+      int r;
+      find_bin(nd, b, r);
+      cur ^= 1;
+      prefix = (prefix << w) | b;
+      nd = r;
+      bits = shift;
+    }
+    if (rem) *rem = nd;
+    return lo + (uint32_t)((uint64_t)prefix << bits);
+  }
+};
+
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kRT) void topk_row_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, int32_t* __restrict__ idx) {
+  __shared__ RowLds S;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  Blk B{S, tid, lane, tid >> 6};
+  const sampled::TkRowInfo ri = sampled::tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  int32_t* out = idx + (int64_t)row * k;
+  for (int i = ri.m + tid; i < k; i += kRT) out[i] = -1;
+  if (ri.m == ri.n) {                                  // keep every visible token
+    for (int i = tid; i < ri.n; i += kRT) out[i] = i;
+    return;
+  }
+  const float* srow = scores + (int64_t)row * L_max;
+  const int n = ri.n;
+  for (int i = tid; i < 2 * kRBins; i += kRT) (&S.h.hist[0][0])[i] = 0u;
+  if (tid == 0) S.count = 0u;
+
+  // ---- tau: a lower bound of the r-th largest of a block-strided sample, r chosen so that about
+  // 3k/2 of the row's scores are expected to reach it (rows that fit the list keep every score)
+  float tau_f = -INFINITY;
+  if (n > kRCap) {
+    const int n_blocks = (n + 15) / 16;
+    const int stride = (n_blocks + kRSample - 1) / kRSample;
+    const int s_blocks = (n_blocks + stride - 1) / stride;
+    constexpr int kPer = kRSample * 4 / kRT;           // float4 slots per thread
+    uint32_t sk[kPer * 4];
+    bool sok[kPer * 4];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int v = tid + e * kRT;
+      const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
+      float f[4];
+      if (VEC && v < s_blocks * 4 && i0 + 3 < n) {
+        const float4 x = *(const float4*)(srow + i0);
+        f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f[c] = (v < s_blocks * 4 && i0 + c < n) ? srow[i0 + c] : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sok[4 * e + c] = v < s_blocks * 4 && i0 + c < n;
+        sk[4 * e + c] = float_key(f[c]);
+      }
+    }
+    int ns_local = 0;
+#pragma unroll
+    for (int e = 0; e < kPer * 4; ++e) ns_local += sok[e];
+    const int ns = (int)B.sum((uint32_t)ns_local);     // also orders the zeroing above before use
+    const int r = max(1, min((3 * k / 2 + stride - 1) / stride, ns));
+    tau_f = key_float(B.select(sk, sok, r, false, nullptr));
+  } else {
+    __syncthreads();
+  }
+
+  // ---- candidates: every visible score >= tau, appended to LDS (one atomic per wave and pass)
+  constexpr int kStep = kRT * 4 * kRUnroll;
+  float4 cur[kRUnroll], nxt[kRUnroll];
+  auto load = [&](float4 (&d)[kRUnroll], int base) {
+#pragma unroll
+    for (int u = 0; u < kRUnroll; ++u) {
+      const int i0 = base + 4 * (tid + u * kRT);
+      if (VEC && i0 + 3 < n) {
+        d[u] = *(const float4*)(srow + i0);
+      } else {
+        d[u].x = i0 + 0 < n ? srow[i0 + 0] : -INFINITY;
+        d[u].y = i0 + 1 < n ? srow[i0 + 1] : -INFINITY;
+        d[u].z = i0 + 2 < n ? srow[i0 + 2] : -INFINITY;
+        d[u].w = i0 + 3 < n ? srow[i0 + 3] : -INFINITY;
+      }
+    }
+  };
+  load(cur, 0);
+  for (int base = 0; base < n; base += kStep) {
+    if (base + kStep < n) load(nxt, base + kStep);
+    uint64_t bal[kRUnroll][4];
+    uint32_t total = 0;
+#pragma unroll
+    for (int u = 0; u < kRUnroll; ++u) {
+      const int i0 = base + 4 * (tid + u * kRT);
+      const float f[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bal[u][c] = __ballot(i0 + c < n && f[c] >= tau_f);
+        total += (uint32_t)__popcll(bal[u][c]);
+      }
+    }
+    if (total) {                                       // wave-uniform
+      uint32_t at = 0;
+      if (lane == 0) at = atomicAdd(&S.count, total);
+      at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+      for (int u = 0; u < kRUnroll; ++u) {
+        const int i0 = base + 4 * (tid + u * kRT);
+        const float f[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t b = bal[u][c];
+          if ((b >> lane) & 1ull) {
+            const uint32_t slot =
+                at + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            if (slot < (uint32_t)kRCap) {
+              S.u.c.key[slot] = float_key(f[c]);
+              S.u.c.pos[slot] = i0 + c;
+            }
+          }
+          at += (uint32_t)__popcll(b);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRUnroll; ++u) cur[u] = nxt[u];
+  }
+  __syncthreads();
+  const int cnt = (int)S.count;
+  if (cnt < k || cnt > kRCap) {                        // the sample missed: exact scan of the row
+    sampled::finish_full_scan<kRT>(srow, n, k, out, S.h.full);
+    return;
+  }
+
+  // ---- exact selection among the candidates (held in registers): the k-th largest key T, then
+  // the ties at T by the lowest positions
+  uint32_t ck[kRCPer];
+  int cp[kRCPer];
+  bool cok[kRCPer];
+#pragma unroll
+  for (int e = 0; e < kRCPer; ++e) {
+    const int i = tid + e * kRT;
+    cok[e] = i < cnt;
+    ck[e] = cok[e] ? S.u.c.key[i] : 0u;
+    cp[e] = cok[e] ? S.u.c.pos[i] : 0;
+  }
+  int rem;
+  const uint32_t T = B.select(ck, cok, k, true, &rem);
+  uint32_t eq_local = 0;
+#pragma unroll
+  for (int e = 0; e < kRCPer; ++e) eq_local += cok[e] && ck[e] == T;
+  const int n_eq = (int)B.sum(eq_local);
+  uint32_t pos_cut = 0;                                // keep ties with (0xFFFFFF - pos) >= pos_cut
+  if (n_eq > rem) {
+    uint32_t tk[kRCPer];
+    bool tok[kRCPer];
+#pragma unroll
+    for (int e = 0; e < kRCPer; ++e) {
+      tok[e] = cok[e] && ck[e] == T;
+      tk[e] = 0xFFFFFFu - (uint32_t)cp[e];
+    }
+    pos_cut = B.select(tk, tok, rem, true, nullptr);
+  }
+  bool keep[kRCPer];
+#pragma unroll
+  for (int e = 0; e < kRCPer; ++e)
+    keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
+
+  // ---- emission in ascending position order through a bitmap of kRWindow positions at a time
+  int emitted = 0;
+  for (int wbase = 0; wbase < n; wbase += kRWindow) {
+    for (int i = tid; i < kRWindow / 32; i += kRT) S.bitmap[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kRCPer; ++e) {
+      const int q = cp[e] - wbase;
+      if (keep[e] && q >= 0 && q < kRWindow) atomicOr(&S.bitmap[q >> 5], 1u << (q & 31));
+    }
+    __syncthreads();
+    constexpr int W = kRWindow / 32 / kRT;             // words per thread
+    uint32_t words[W], pc = 0;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      words[e] = S.bitmap[tid * W + e];
+      pc += __builtin_popcount(words[e]);
+    }
+    uint32_t tot;
+    int slot = emitted + (int)B.scan(pc, &tot);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      uint32_t m = words[e];
+      while (m) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1;
+        if (slot < k) out[slot] = wbase + 32 * (tid * W + e) + bit;
+        ++slot;
+      }
+    }
+    emitted += (int)tot;
+    __syncthreads();
+  }
+}
+
+hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, hipStream_t s) {
+  const int rows = bt.B * bt.Q;
+  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
+    hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
+                       bt.in_Q, bt.L_max, k, idx);
+  else
+    hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
+                       bt.in_Q, bt.L_max, k, idx);
+  return hipGetLastError();
+}
+
+}  // namespace rowsel
+
 #ifndef DSA_TOPK_SAMPLED_MIN_SCORES
 #define DSA_TOPK_SAMPLED_MIN_SCORES (1 << 23)
 #endif
+#ifndef DSA_TOPK_ROW_MAX_LEN
+#define DSA_TOPK_ROW_MAX_LEN (1 << 18)
+#endif
 
-// The sampled form once a call holds more than 8M scores (rows x L_max); below that the chunked
-// radix form's extra passes over the scores cost less than one workgroup per row in series.
-static bool use_sampled(const HostBatch& bt) {
-  return (int64_t)bt.B * bt.Q * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES;
+enum TopkForm { kFormAuto = 0, kFormRadix, kFormSampled, kFormRow };
+
+// DSA_TOPK_FORM = radix | sampled | row pins one form (all give identical results); unset or
+// anything else leaves the choice to the size rules below.
+static TopkForm forced_form() {
+  const char* e = getenv("DSA_TOPK_FORM");
+  if (!e) return kFormAuto;
+  if (!strcmp(e, "radix")) return kFormRadix;
+  if (!strcmp(e, "sampled")) return kFormSampled;
+  if (!strcmp(e, "row")) return kFormRow;
+  return kFormAuto;
 }
 
-// Room for either form, so that any call with at most `rows` rows fits.
+// Rows up to 256K scores go to the one-launch row form; longer rows to the sampled form once a
+// call holds more than 8M scores (rows x L_max), else to the chunked radix form, whose extra
+// passes over the scores cost less than one workgroup per long row in series.
+static TopkForm auto_form(const HostBatch& bt) {
+  if (bt.L_max <= DSA_TOPK_ROW_MAX_LEN) return kFormRow;
+  if ((int64_t)bt.B * bt.Q * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES) return kFormSampled;
+  return kFormRadix;
+}
+
+// Room for any form, so that any call with at most `rows` rows fits (the row form needs none).
 size_t topk_workspace_bytes(int rows, int L_max) {
   return std::max(radix::workspace_bytes(rows, L_max), sampled::workspace_bytes(rows));
 }
 
 hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s) {
-  if (use_sampled(bt)) return sampled::launch(bt, scores, k, idx, ws, s);
+  TopkForm f = forced_form();
+  if (f == kFormAuto) f = auto_form(bt);
+  if (f == kFormRow) return rowsel::launch(bt, scores, k, idx, s);
+  if (f == kFormSampled) return sampled::launch(bt, scores, k, idx, ws, s);
   return radix::launch(bt, scores, k, idx, ws, s);
 }
 

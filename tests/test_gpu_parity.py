@@ -5,6 +5,8 @@ a ragged tail. Tolerances and their derivations are in tests/helpers.py.
 """
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -97,26 +99,26 @@ def test_index_score_explicit_positions_and_determinism():
 
 
 # ----------------------------------------------------------------------------- top-k
-# The library takes the chunked radix form for calls of at most this many scores (B * Q * L_max)
-# and the sampled form above it; tests run each case in both forms by repeating the batch.
-SAMPLED_ABOVE_SCORES = 1 << 23
-FORMS = ["radix", "sampled"]
+# Three top-k forms give identical results; DSA_TOPK_FORM pins one (unset, the library picks by
+# shape). Every top-k case runs in each form.
+FORMS = ["radix", "sampled", "row"]
 
 
 def run_topk(scores32, seq_lens, k, q_pos=None, form="radix"):
     scores32 = np.ascontiguousarray(scores32)
-    B, Q, L_max = scores32.shape
-    reps = 1
-    if form == "sampled":
-        reps = SAMPLED_ABOVE_SCORES // (B * Q * L_max) + 1
-    else:
-        assert B * Q * L_max <= SAMPLED_ABOVE_SCORES
-    t = torch.from_numpy(np.tile(scores32, (reps, 1, 1))).to(DEV)
-    sl = torch.tensor(list(seq_lens) * reps, dtype=torch.int32, device=DEV)
-    qp = None if q_pos is None else torch.tensor(np.tile(np.asarray(q_pos), (reps, 1)), dtype=torch.int32, device=DEV)
-    got = np_(dsa.topk(t, sl, k, q_pos=qp)).reshape(reps, B, Q, k)
-    assert all(np.array_equal(got[0], got[r]) for r in range(1, reps))
-    return got[0]
+    t = torch.from_numpy(scores32).to(DEV)
+    sl = torch.tensor(list(seq_lens), dtype=torch.int32, device=DEV)
+    qp = None if q_pos is None else torch.tensor(np.asarray(q_pos), dtype=torch.int32, device=DEV)
+    prev = os.environ.get("DSA_TOPK_FORM")
+    os.environ["DSA_TOPK_FORM"] = form
+    try:
+        got = np_(dsa.topk(t, sl, k, q_pos=qp))
+    finally:
+        if prev is None:
+            del os.environ["DSA_TOPK_FORM"]
+        else:
+            os.environ["DSA_TOPK_FORM"] = prev
+    return got
 
 
 def oracle_topk(scores32, seq_lens, k, q_pos=None):
@@ -298,19 +300,22 @@ def test_forward_shared_small(share_first):
                 check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
 
 
-def test_topk_when_the_sample_misses():
-    """The sampled form reads one 16-score block in `stride` (32 for k = 2048 on a 128K row).
-    When exactly those blocks, or exactly the blocks between them, carry the high scores, or
-    every score is equal, the candidate list misses or overflows and the exact full-row scan
-    must produce the set."""
+@pytest.mark.parametrize("form", ["sampled", "row"])
+def test_topk_when_the_sample_misses(form):
+    """The sampled forms read a block-strided sample of each row (one 16-score block in 32 for
+    k = 2048 on a 128K row in the sampled form, one in 16 in the row form). When exactly those
+    blocks, or exactly the blocks between them, carry the high scores, or every score is equal,
+    the candidate list misses or overflows and the exact full-row scan must produce the set."""
     rng = np.random.default_rng(21)
     L = 131072
-    s = (1.0 + rng.random((4, 1, L))).astype(np.float32)
+    s = (1.0 + rng.random((6, 1, L))).astype(np.float32)
     blk = np.arange(L) // 16
-    s[0, 0, blk % 32 == 0] += 100.0                # exactly the sampled blocks (k = 2048)
-    s[1, 0, blk % 32 != 0] += 100.0                # everything but the sampled blocks
+    s[0, 0, blk % 32 == 0] += 100.0                # the sampled blocks of the sampled form
+    s[1, 0, blk % 32 != 0] += 100.0                # everything but them
     s[2, 0, :] = np.float32(7.0)                   # every score equal: a flood of candidates
-    s[3, 0, blk % 4 == 0] += 100.0                 # every fourth block: the sampled ones and more
+    s[3, 0, blk % 4 == 0] += 100.0                 # every fourth block
+    s[4, 0, blk % 16 == 0] += 100.0                # the sampled blocks of the row form
+    s[5, 0, blk % 16 != 0] += 100.0                # everything but them
     for k in (2048, 300):
-        got = run_topk(s, [L] * 4, k, form="sampled")
-        assert np.array_equal(got, oracle_topk(s, [L] * 4, k)), k
+        got = run_topk(s, [L] * 6, k, form=form)
+        assert np.array_equal(got, oracle_topk(s, [L] * 6, k)), k
