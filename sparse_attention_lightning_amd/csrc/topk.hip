@@ -2,25 +2,24 @@
 // highest-scoring tokens). Exact top-k on the order-preserving uint32 image of the fp32
 // scores; equal scores go to the lower position; output ascending, -1 padded.
 //
-// Three implementations with identical results. Rows of up to 256K scores go to the row form
-// (one workgroup per row, one launch; further below). Longer rows (long-context share groups)
-// go to the chunked radix form (topk_radix.hip), which spreads a few long rows over the chip,
-// or for calls of more than 8M scores to the sampled form below, which reads the scores about
-// once instead of five times. The sampled form takes three launches:
-//   sample   one workgroup per row reads a block-strided sample (whole 64-byte lines, one
-//            16-score block in `stride`, stride <= k / 64 so that about 128 sampled scores are
-//            expected above the threshold) and radix-selects in LDS the key tau that about 2k
-//            of the row's scores are expected to reach.
+// Three implementations with identical results, chosen by shape (see auto_form): the row form
+// (one workgroup per row, one launch; further below) for short rows or many rows, the sampled
+// form below for few rows of up to 256K and for large calls of longer rows, and the chunked
+// radix form (topk_radix.hip) for small calls of long rows. The sampled form takes three
+// launches:
+//   sample   one 1024-thread workgroup per row reads a block-strided sample (whole 64-byte
+//            lines, up to 512 blocks of 16 scores) and radix-selects a lower bound tau of the
+//            sample rank that about 2k of the row's scores are expected to reach.
 //   gather   chunk workgroups over the whole row append (key, position) of every score >= tau
 //            to the row's candidate list (wave-aggregated atomics; order is irrelevant).
-//   finish   one workgroup per row. If the list holds between k and kTkCap candidates it
-//            contains the exact top-k (all scores >= tau, and tau is at most the k-th
-//            largest); the workgroup radix-selects the k-th largest key T among them, breaks
-//            ties at T toward lower positions with a second radix select on the complemented
-//            position, and emits the k kept positions in order through LDS bitmaps of windows
-//            of positions. Otherwise (a sample that missed,
-//            or a flood of equal scores) it falls back to an exact scan of the whole row:
-//            three histogram passes for T, then an ordered block-scan compaction.
+//   finish   one 1024-thread workgroup per row. If the list holds between k and kTkCap
+//            candidates it contains the exact top-k (all scores >= tau, and tau is at most the
+//            k-th largest); holding them in registers, the workgroup radix-selects the k-th
+//            largest key T, breaks ties at T toward lower positions with a second radix select
+//            on the complemented position, and emits the k kept positions in order through LDS
+//            bitmaps of windows of positions. Otherwise (a sample that missed, or a flood of
+//            equal scores) it falls back to an exact scan of the whole row: histogram passes
+//            for T, then an ordered block-scan compaction.
 // Rows with p + 1 <= k keep every visible token. Results are deterministic: the kept set is
 // defined by score and position alone, never by the order of the appends.
 #include <algorithm>
@@ -41,10 +40,6 @@ namespace sampled {
 
 constexpr int kTkThreads = 256;
 constexpr int kTkCap = 8192;               // candidates kept per row (4 x the largest k)
-#ifndef DSA_TK_SAMPLE_BLOCKS
-#define DSA_TK_SAMPLE_BLOCKS 1024
-#endif
-constexpr int kTkSampleBlocks = DSA_TK_SAMPLE_BLOCKS;   // sampled 16-score blocks per row
 constexpr int kTkChunk = 4096;             // scores per gather workgroup (16 per thread)
 constexpr int kTkWindow = 1 << 18;         // positions per bitmap window in the finish step (32 KB)
 static_assert(kTkCap >= 2 * kMaxK, "room for about 2k candidates plus spread");
@@ -235,59 +230,6 @@ __device__ uint32_t select_24(TkLds& L, int n, int need, ValFn v, UseFn use) {
   return (b1 << 12) | b2;
 }
 
-// ------------------------------------------------------------------------------------------ sample
-template <bool VEC>
-__global__ __launch_bounds__(kTkThreads) void topk_sample_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, TkWs ws) {
-  __shared__ uint32_t skey[kTkSampleBlocks * 16];
-  __shared__ TkLds L;
-  const int row = blockIdx.x;
-  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
-  TkRow* st = ws.rows + row;
-  if (ri.m == ri.n) {
-    if (threadIdx.x == 0) { st->count = 0; st->tau = 0; }
-    return;
-  }
-  if (ri.n <= kTkCap) {                                // the whole row fits the candidate list
-    if (threadIdx.x == 0) { st->tau = 0u; st->count = 0; }
-    return;
-  }
-  const float* srow = scores + (int64_t)row * L_max;
-  const int n_blocks = (ri.n + 15) / 16;
-  const int stride = max(max(1, k / 64), (n_blocks + kTkSampleBlocks - 1) / kTkSampleBlocks);
-  const int s_blocks = (n_blocks + stride - 1) / stride;
-  constexpr int kPer = kTkSampleBlocks * 4 / kTkThreads;                   // float4 slots per thread
-  float f[kPer][4];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {                                         // all loads in flight at once
-    const int v = (int)threadIdx.x + e * kTkThreads;
-    const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
-    if (VEC && v < s_blocks * 4 && i0 + 3 < ri.n) {
-      const float4 x = *(const float4*)(srow + i0);
-      f[e][0] = x.x; f[e][1] = x.y; f[e][2] = x.z; f[e][3] = x.w;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) f[e][c] = (v < s_blocks * 4 && i0 + c < ri.n) ? srow[i0 + c] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int v = (int)threadIdx.x + e * kTkThreads;
-    const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (v < s_blocks * 4) skey[4 * v + c] = (i0 + c < ri.n) ? float_key(f[e][c]) : 0u;   // 0: below every score
-  }
-  __syncthreads();
-  const int s = s_blocks * 16;
-  const int r = max(1, min((2 * k + stride - 1) / stride, s));   // ~2k scores of the row should reach tau
-  uint32_t T;
-  int rem;
-  select_key(L, s, r, [&](int i) { return skey[i]; }, T, rem);
-  if (threadIdx.x == 0) { st->tau = T; st->count = 0; }
-}
-
 // ------------------------------------------------------------------------------------------ gather
 template <bool VEC>
 __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
@@ -382,113 +324,6 @@ __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, i
   }
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
-  __shared__ uint32_t ckey[kTkCap];
-  __shared__ int cpos[kTkCap];
-  __shared__ uint32_t bitmap[kTkWindow / 32];
-  __shared__ TkLds L;
-  const int row = blockIdx.x;
-  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
-  int32_t* out = idx + (int64_t)row * k;
-  for (int i = ri.m + (int)threadIdx.x; i < k; i += kTkThreads) out[i] = -1;
-  if (ri.m == ri.n) {                                  // keep every visible token
-    for (int i = threadIdx.x; i < ri.n; i += kTkThreads) out[i] = i;
-    return;
-  }
-  const TkRow* st = ws.rows + row;
-  const int cnt = (int)st->count;
-  if (cnt < k || cnt > kTkCap) {                       // the sample missed: exact scan of the row
-    finish_full_scan(scores + (int64_t)row * L_max, ri.n, k, out, L);
-    return;
-  }
-  const uint2* cand = ws.cand + (int64_t)row * kTkCap;
-  constexpr int kCPer = kTkCap / kTkThreads;
-  uint2 c[kCPer];
-#pragma unroll
-  for (int e = 0; e < kCPer; ++e) {                                        // all loads in flight at once
-    const int i = (int)threadIdx.x + e * kTkThreads;
-    if (i < cnt) c[e] = cand[i];
-  }
-#pragma unroll
-  for (int e = 0; e < kCPer; ++e) {
-    const int i = (int)threadIdx.x + e * kTkThreads;
-    if (i < cnt) { ckey[i] = c[e].x; cpos[i] = (int)c[e].y; }
-  }
-  __syncthreads();
-  uint32_t T;
-  int rem;
-  select_key(L, cnt, k, [&](int i) { return ckey[i]; }, T, rem);
-  // ties at T: all of them, or the rem lowest positions (largest complemented positions)
-  uint32_t eq_local = 0;
-  for (int i = threadIdx.x; i < cnt; i += kTkThreads) eq_local += ckey[i] == T;
-  uint32_t dummy;
-  const int n_eq = (int)block_exclusive_scan(eq_local, &dummy, L.lds4);
-  uint32_t pos_cut = 0;                                // keep ties with (0xFFFFFF - pos) >= pos_cut
-  if (n_eq > rem)
-    pos_cut = select_24(L, cnt, rem, [&](int i) { return 0xFFFFFFu - (uint32_t)cpos[i]; },
-                        [&](int i) { return ckey[i] == T; });
-  // Emit the kept positions in ascending order through a bitmap of a window of positions at a
-  // time: kept candidates set their bits, a block scan of popcounts places them.
-  auto keep = [&](int i) {
-    return ckey[i] > T || (ckey[i] == T && (0xFFFFFFu - (uint32_t)cpos[i]) >= pos_cut);
-  };
-  int emitted = 0;
-  for (int base = 0; base < ri.n; base += kTkWindow) {
-    for (int i = threadIdx.x; i < kTkWindow / 32; i += kTkThreads) bitmap[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < cnt; i += kTkThreads) {
-      const int q = cpos[i] - base;
-      if (q >= 0 && q < kTkWindow && keep(i)) atomicOr(&bitmap[q >> 5], 1u << (q & 31));
-    }
-    __syncthreads();
-    constexpr int W = kTkWindow / 32 / kTkThreads;                 // words per thread
-    uint32_t pc = 0;
-#pragma unroll
-    for (int e = 0; e < W; ++e) pc += __builtin_popcount(bitmap[threadIdx.x * W + e]);
-    uint32_t at;
-    const uint32_t tot = block_exclusive_scan(pc, &at, L.lds4);
-    int slot = emitted + (int)at;
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      uint32_t m = bitmap[threadIdx.x * W + e];
-      while (m) {
-        const int bit = __builtin_ctz(m);
-        m &= m - 1;
-        if (slot < k) out[slot] = base + 32 * (threadIdx.x * W + e) + bit;
-        ++slot;
-      }
-    }
-    emitted += (int)tot;
-    __syncthreads();
-  }
-}
-
-template <bool VEC>
-static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
-                       hipStream_t s) {
-  const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
-  const dim3 block(kTkThreads);
-  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, w);
-  hipLaunchKernelGGL(topk_gather_kernel<VEC>, dim3((unsigned)rows * n_chunks), block, 0, s, scores, bt.seq_lens,
-                     bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), block, 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q,
-                     bt.L_max, k, w, idx);
-}
-
-hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s) {
-  const int rows = bt.B * bt.Q;
-  TkWs w = carve(ws, rows);
-  // 16-byte vector loads need every row to start 16-byte aligned
-  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
-    launch_all<true>(bt, scores, k, idx, w, rows, s);
-  else
-    launch_all<false>(bt, scores, k, idx, w, rows, s);
-  return hipGetLastError();
-}
-
 }  // namespace sampled
 
 // ------------------------------------------------------------------------------------------ rowsel
@@ -513,14 +348,9 @@ constexpr int kRCPer = kRCap / kRT;        // candidate slots per thread
 static_assert(kRCap >= 2 * kMaxK, "room for about 1.5k candidates plus spread");
 static_assert(kRBins % kRT == 0, "whole bins per thread");
 
-struct RowLds {
-  union {
-    uint32_t skey[kRSample * 16];          // unused slot (the sample stays in registers)
-    struct {
-      uint32_t key[kRCap];                 // candidates: key and position
-      int pos[kRCap];
-    } c;
-  } u;
+// LDS of the block-wide selection steps (shared by the row form and the sampled form's
+// per-row kernels).
+struct SelLds {
   uint32_t bitmap[kRWindow / 32];
   union {
     uint32_t hist[2][kRBins];              // radix levels alternate between two histograms
@@ -529,6 +359,12 @@ struct RowLds {
   uint32_t wred[4][kRW];                   // per-wave partials, rotated over the block steps
   uint32_t res[2];
   uint32_t count;
+};
+
+struct RowLds {
+  uint32_t key[kRCap];                     // candidates: key and position
+  int pos[kRCap];
+  SelLds s;
 };
 
 // Wave-inclusive scans by DPP: row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15
@@ -549,7 +385,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t id, Op o
 }
 
 struct Blk {
-  RowLds& S;
+  SelLds& S;
   int tid, lane, wave;
   int slot = 0;                            // wred slot of the next block step
   int cur = 0;                             // the histogram that is clean
@@ -663,11 +499,113 @@ __device__ __forceinline__ float key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// tau (a key) for a row of n > 0 scores: a lower bound of the r-th largest of a block-strided
+// sample of up to kRSample 16-score blocks, r chosen so that about `target` of the row's scores
+// are expected to reach it. The histograms must be zero on entry; returns with them ready.
+template <bool VEC>
+__device__ uint32_t sample_tau(Blk& B, const float* __restrict__ srow, int n, int target) {
+  const int tid = B.tid;
+  const int n_blocks = (n + 15) / 16;
+  const int stride = (n_blocks + kRSample - 1) / kRSample;
+  const int s_blocks = (n_blocks + stride - 1) / stride;
+  constexpr int kPer = kRSample * 4 / kRT;             // float4 slots per thread
+  uint32_t sk[kPer * 4];
+  bool sok[kPer * 4];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = tid + e * kRT;
+    const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
+    float f[4];
+    if (VEC && v < s_blocks * 4 && i0 + 3 < n) {
+      const float4 x = *(const float4*)(srow + i0);
+      f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f[c] = (v < s_blocks * 4 && i0 + c < n) ? srow[i0 + c] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sok[4 * e + c] = v < s_blocks * 4 && i0 + c < n;
+      sk[4 * e + c] = float_key(f[c]);
+    }
+  }
+  int ns_local = 0;
+#pragma unroll
+  for (int e = 0; e < kPer * 4; ++e) ns_local += sok[e];
+  const int ns = (int)B.sum((uint32_t)ns_local);       // also orders the caller's zeroing before use
+  const int r = max(1, min((target + stride - 1) / stride, ns));
+  return B.select(sk, sok, r, false, nullptr);
+}
+
+// Exact top-k of the candidates held in registers (PER per thread; every score of the row that
+// can be among the k largest is a candidate, cnt >= k of them) written to out[0..k) in
+// ascending position order: the k-th largest key T, the ties at T by the lowest positions, then
+// an ordered emission through a bitmap of kRWindow positions at a time.
+template <int PER>
+__device__ void select_emit(Blk& B, const uint32_t (&ck)[PER], const int (&cp)[PER], const bool (&cok)[PER], int n,
+                            int k, int32_t* __restrict__ out) {
+  const int tid = B.tid;
+  int rem;
+  const uint32_t T = B.select(ck, cok, k, true, &rem);
+  uint32_t eq_local = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) eq_local += cok[e] && ck[e] == T;
+  const int n_eq = (int)B.sum(eq_local);
+  uint32_t pos_cut = 0;                                // keep ties with (0xFFFFFF - pos) >= pos_cut
+  if (n_eq > rem) {
+    uint32_t tk[PER];
+    bool tok[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      tok[e] = cok[e] && ck[e] == T;
+      tk[e] = 0xFFFFFFu - (uint32_t)cp[e];
+    }
+    pos_cut = B.select(tk, tok, rem, true, nullptr);
+  }
+  bool keep[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
+  int emitted = 0;
+  for (int wbase = 0; wbase < n; wbase += kRWindow) {
+    for (int i = tid; i < kRWindow / 32; i += kRT) B.S.bitmap[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int q = cp[e] - wbase;
+      if (keep[e] && q >= 0 && q < kRWindow) atomicOr(&B.S.bitmap[q >> 5], 1u << (q & 31));
+    }
+    __syncthreads();
+    constexpr int W = kRWindow / 32 / kRT;             // words per thread
+    uint32_t words[W], pc = 0;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      words[e] = B.S.bitmap[tid * W + e];
+      pc += __builtin_popcount(words[e]);
+    }
+    uint32_t tot;
+    int slot = emitted + (int)B.scan(pc, &tot);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      uint32_t m = words[e];
+      while (m) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1;
+        if (slot < k) out[slot] = wbase + 32 * (tid * W + e) + bit;
+        ++slot;
+      }
+    }
+    emitted += (int)tot;
+    __syncthreads();
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kRT) void topk_row_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, int32_t* __restrict__ idx) {
-  __shared__ RowLds S;
+  __shared__ RowLds R;
+  SelLds& S = R.s;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   Blk B{S, tid, lane, tid >> 6};
@@ -683,43 +621,13 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   for (int i = tid; i < 2 * kRBins; i += kRT) (&S.h.hist[0][0])[i] = 0u;
   if (tid == 0) S.count = 0u;
 
-  // ---- tau: a lower bound of the r-th largest of a block-strided sample, r chosen so that about
-  // 3k/2 of the row's scores are expected to reach it (rows that fit the list keep every score)
+  // ---- tau: about 3k/2 of the row's scores are expected to reach it (rows that fit the list
+  // keep every score)
   float tau_f = -INFINITY;
-  if (n > kRCap) {
-    const int n_blocks = (n + 15) / 16;
-    const int stride = (n_blocks + kRSample - 1) / kRSample;
-    const int s_blocks = (n_blocks + stride - 1) / stride;
-    constexpr int kPer = kRSample * 4 / kRT;           // float4 slots per thread
-    uint32_t sk[kPer * 4];
-    bool sok[kPer * 4];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int v = tid + e * kRT;
-      const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
-      float f[4];
-      if (VEC && v < s_blocks * 4 && i0 + 3 < n) {
-        const float4 x = *(const float4*)(srow + i0);
-        f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) f[c] = (v < s_blocks * 4 && i0 + c < n) ? srow[i0 + c] : 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sok[4 * e + c] = v < s_blocks * 4 && i0 + c < n;
-        sk[4 * e + c] = float_key(f[c]);
-      }
-    }
-    int ns_local = 0;
-#pragma unroll
-    for (int e = 0; e < kPer * 4; ++e) ns_local += sok[e];
-    const int ns = (int)B.sum((uint32_t)ns_local);     // also orders the zeroing above before use
-    const int r = max(1, min((3 * k / 2 + stride - 1) / stride, ns));
-    tau_f = key_float(B.select(sk, sok, r, false, nullptr));
-  } else {
+  if (n > kRCap)
+    tau_f = key_float(sample_tau<VEC>(B, srow, n, 3 * k / 2));
+  else
     __syncthreads();
-  }
 
   // ---- candidates: every visible score >= tau, appended to LDS (one atomic per wave and pass)
   constexpr int kStep = kRT * 4 * kRUnroll;
@@ -768,8 +676,8 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
             const uint32_t slot =
                 at + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
             if (slot < (uint32_t)kRCap) {
-              S.u.c.key[slot] = float_key(f[c]);
-              S.u.c.pos[slot] = i0 + c;
+              R.key[slot] = float_key(f[c]);
+              R.pos[slot] = i0 + c;
             }
           }
           at += (uint32_t)__popcll(b);
@@ -785,9 +693,6 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
     sampled::finish_full_scan<kRT>(srow, n, k, out, S.h.full);
     return;
   }
-
-  // ---- exact selection among the candidates (held in registers): the k-th largest key T, then
-  // the ties at T by the lowest positions
   uint32_t ck[kRCPer];
   int cp[kRCPer];
   bool cok[kRCPer];
@@ -795,64 +700,10 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   for (int e = 0; e < kRCPer; ++e) {
     const int i = tid + e * kRT;
     cok[e] = i < cnt;
-    ck[e] = cok[e] ? S.u.c.key[i] : 0u;
-    cp[e] = cok[e] ? S.u.c.pos[i] : 0;
+    ck[e] = cok[e] ? R.key[i] : 0u;
+    cp[e] = cok[e] ? R.pos[i] : 0;
   }
-  int rem;
-  const uint32_t T = B.select(ck, cok, k, true, &rem);
-  uint32_t eq_local = 0;
-#pragma unroll
-  for (int e = 0; e < kRCPer; ++e) eq_local += cok[e] && ck[e] == T;
-  const int n_eq = (int)B.sum(eq_local);
-  uint32_t pos_cut = 0;                                // keep ties with (0xFFFFFF - pos) >= pos_cut
-  if (n_eq > rem) {
-    uint32_t tk[kRCPer];
-    bool tok[kRCPer];
-#pragma unroll
-    for (int e = 0; e < kRCPer; ++e) {
-      tok[e] = cok[e] && ck[e] == T;
-      tk[e] = 0xFFFFFFu - (uint32_t)cp[e];
-    }
-    pos_cut = B.select(tk, tok, rem, true, nullptr);
-  }
-  bool keep[kRCPer];
-#pragma unroll
-  for (int e = 0; e < kRCPer; ++e)
-    keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
-
-  // ---- emission in ascending position order through a bitmap of kRWindow positions at a time
-  int emitted = 0;
-  for (int wbase = 0; wbase < n; wbase += kRWindow) {
-    for (int i = tid; i < kRWindow / 32; i += kRT) S.bitmap[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kRCPer; ++e) {
-      const int q = cp[e] - wbase;
-      if (keep[e] && q >= 0 && q < kRWindow) atomicOr(&S.bitmap[q >> 5], 1u << (q & 31));
-    }
-    __syncthreads();
-    constexpr int W = kRWindow / 32 / kRT;             // words per thread
-    uint32_t words[W], pc = 0;
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      words[e] = S.bitmap[tid * W + e];
-      pc += __builtin_popcount(words[e]);
-    }
-    uint32_t tot;
-    int slot = emitted + (int)B.scan(pc, &tot);
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      uint32_t m = words[e];
-      while (m) {
-        const int bit = __builtin_ctz(m);
-        m &= m - 1;
-        if (slot < k) out[slot] = wbase + 32 * (tid * W + e) + bit;
-        ++slot;
-      }
-    }
-    emitted += (int)tot;
-    __syncthreads();
-  }
+  select_emit(B, ck, cp, cok, n, k, out);
 }
 
 hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, hipStream_t s) {
@@ -867,6 +718,93 @@ hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx,
 }
 
 }  // namespace rowsel
+
+namespace sampled {
+
+// sample: one 1024-thread workgroup per row; tau for about 2k candidates (rows that fit the
+// candidate list keep every score: tau = 0, below every key).
+template <bool VEC>
+__global__ __launch_bounds__(rowsel::kRT) void topk_sample_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, TkWs ws) {
+  __shared__ rowsel::SelLds S;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  TkRow* st = ws.rows + row;
+  if (ri.m == ri.n || ri.n <= kTkCap) {
+    if (tid == 0) { st->count = 0; st->tau = 0u; }
+    return;
+  }
+  rowsel::Blk B{S, tid, tid & 63, tid >> 6};
+  for (int i = tid; i < 2 * rowsel::kRBins; i += rowsel::kRT) (&S.h.hist[0][0])[i] = 0u;
+  const uint32_t tau = rowsel::sample_tau<VEC>(B, scores + (int64_t)row * L_max, ri.n, 2 * k);
+  if (tid == 0) { st->tau = tau; st->count = 0; }
+}
+
+// finish: one 1024-thread workgroup per row over its candidate list (held in registers), or the
+// exact full-row scan when the list missed (fewer than k) or overflowed.
+__global__ __launch_bounds__(rowsel::kRT) void topk_finish_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
+    int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
+  constexpr int PER = kTkCap / rowsel::kRT;
+  __shared__ rowsel::SelLds S;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
+  int32_t* out = idx + (int64_t)row * k;
+  for (int i = ri.m + tid; i < k; i += rowsel::kRT) out[i] = -1;
+  if (ri.m == ri.n) {                                  // keep every visible token
+    for (int i = tid; i < ri.n; i += rowsel::kRT) out[i] = i;
+    return;
+  }
+  rowsel::Blk B{S, tid, tid & 63, tid >> 6};
+  const int cnt = (int)ws.rows[row].count;
+  if (cnt < k || cnt > kTkCap) {                       // the sample missed: exact scan of the row
+    finish_full_scan<rowsel::kRT>(scores + (int64_t)row * L_max, ri.n, k, out, S.h.full);
+    return;
+  }
+  for (int i = tid; i < 2 * rowsel::kRBins; i += rowsel::kRT) (&S.h.hist[0][0])[i] = 0u;
+  const uint2* cand = ws.cand + (int64_t)row * kTkCap;
+  uint32_t ck[PER];
+  int cp[PER];
+  bool cok[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid + e * rowsel::kRT;
+    cok[e] = i < cnt;
+    const uint2 c = cok[e] ? cand[i] : make_uint2(0u, 0u);
+    ck[e] = c.x;
+    cp[e] = (int)c.y;
+  }
+  __syncthreads();                                     // the zeroed histograms before the first level
+  rowsel::select_emit(B, ck, cp, cok, ri.n, k, out);
+}
+
+template <bool VEC>
+static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
+                       hipStream_t s) {
+  const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
+  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), dim3(rowsel::kRT), 0, s, scores, bt.seq_lens, bt.q_pos,
+                     bt.Q, bt.in_Q, bt.L_max, k, w);
+  hipLaunchKernelGGL(topk_gather_kernel<VEC>, dim3((unsigned)rows * n_chunks), dim3(kTkThreads), 0, s, scores,
+                     bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, n_chunks, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(rowsel::kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
+                     bt.in_Q, bt.L_max, k, w, idx);
+}
+
+hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const int rows = bt.B * bt.Q;
+  TkWs w = carve(ws, rows);
+  // 16-byte vector loads need every row to start 16-byte aligned
+  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
+    launch_all<true>(bt, scores, k, idx, w, rows, s);
+  else
+    launch_all<false>(bt, scores, k, idx, w, rows, s);
+  return hipGetLastError();
+}
+
+}  // namespace sampled
 
 #ifndef DSA_TOPK_SAMPLED_MIN_SCORES
 #define DSA_TOPK_SAMPLED_MIN_SCORES (1 << 23)
@@ -888,12 +826,18 @@ static TopkForm forced_form() {
   return kFormAuto;
 }
 
-// Rows up to 256K scores go to the one-launch row form; longer rows to the sampled form once a
-// call holds more than 8M scores (rows x L_max), else to the chunked radix form, whose extra
-// passes over the scores cost less than one workgroup per long row in series.
+// One workgroup per row streams a row at a few tens of GB/s, so the one-launch row form wins
+// when rows are short (at most 64K scores) or many (128 rows or more, enough to fill the chip).
+// Other rows up to 256K go to the sampled form, whose gather spreads each row over the chip;
+// longer rows to the sampled form once a call holds more than 8M scores (rows x L_max), else to
+// the chunked radix form.
 static TopkForm auto_form(const HostBatch& bt) {
-  if (bt.L_max <= DSA_TOPK_ROW_MAX_LEN) return kFormRow;
-  if ((int64_t)bt.B * bt.Q * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES) return kFormSampled;
+  const int64_t rows = (int64_t)bt.B * bt.Q;
+  if (bt.L_max <= DSA_TOPK_ROW_MAX_LEN) {
+    if (bt.L_max <= (1 << 16) || rows >= 128) return kFormRow;
+    return kFormSampled;
+  }
+  if (rows * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES) return kFormSampled;
   return kFormRadix;
 }
 

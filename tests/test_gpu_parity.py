@@ -302,19 +302,19 @@ def test_forward_shared_small(share_first):
 
 @pytest.mark.parametrize("form", ["sampled", "row"])
 def test_topk_when_the_sample_misses(form):
-    """The sampled forms read a block-strided sample of each row (one 16-score block in 32 for
-    k = 2048 on a 128K row in the sampled form, one in 16 in the row form). When exactly those
-    blocks, or exactly the blocks between them, carry the high scores, or every score is equal,
-    the candidate list misses or overflows and the exact full-row scan must produce the set."""
+    """Both sampled forms read a block-strided sample of each row: up to 512 blocks of 16
+    scores, one block in 16 on a 128K row. When exactly those blocks, or exactly the blocks
+    between them, carry the high scores, or every score is equal, the candidate list misses or
+    overflows and the exact full-row scan must produce the set."""
     rng = np.random.default_rng(21)
     L = 131072
     s = (1.0 + rng.random((6, 1, L))).astype(np.float32)
     blk = np.arange(L) // 16
-    s[0, 0, blk % 32 == 0] += 100.0                # the sampled blocks of the sampled form
+    s[0, 0, blk % 32 == 0] += 100.0                # half of the sampled blocks
     s[1, 0, blk % 32 != 0] += 100.0                # everything but them
     s[2, 0, :] = np.float32(7.0)                   # every score equal: a flood of candidates
     s[3, 0, blk % 4 == 0] += 100.0                 # every fourth block
-    s[4, 0, blk % 16 == 0] += 100.0                # the sampled blocks of the row form
+    s[4, 0, blk % 16 == 0] += 100.0                # exactly the sampled blocks
     s[5, 0, blk % 16 != 0] += 100.0                # everything but them
     for k in (2048, 300):
         got = run_topk(s, [L] * 6, k, form=form)
