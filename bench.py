@@ -156,10 +156,18 @@ def main():
                           device=dev)
     n_mla = dsa.workspace_size(dsa.OP_SPARSE_MLA, wl.B, wl.Q, wl.lmax, H=wl.H, k=wl.k)
     ws_mla = torch.empty(max(n_mla, 1), dtype=torch.uint8, device=dev)
+    # A group of layers sharing one index set (IndexShare) runs as one dsa_forward_shared call,
+    # which launches every layer's MLA together; a single layer runs as the three stage calls.
+    group = wl.n_layers > 1
+    ws_fs = None
+    if group:
+        n_fs = dsa.workspace_size(dsa.OP_FORWARD_SHARED, wl.B, wl.Q, wl.lmax, H=wl.H, k=wl.k, n_layers=wl.n_layers)
+        ws_fs = torch.empty(n_fs, dtype=torch.uint8, device=dev)
+        idx_fs = torch.empty((wl.B, 1 if wl.share_first_query else wl.Q, wl.k), dtype=torch.int32, device=dev)
     q_pos = None
     if wl.share_first_query:   # scores + top-k for query token 0 of each sequence only
         q_pos = torch.tensor([[n - wl.Q] for n in wl.lens], dtype=torch.int32, device=dev)
-    ev = {k: [] for k in ("index", "topk", "mla")}
+    ev = {k: [] for k in ("index", "topk", "mla", "group")}
     # per-batch call arguments, built once (nothing but the three library calls runs in a step)
     prepared = []
     for g in batches:
@@ -171,12 +179,37 @@ def main():
             "g": g,
         })
 
+    def group_call(pr, g):
+        dsa.forward_shared(g.q_idx, g.w, pr["keys"], wl.k, g.q_mla, pr["lats"], wl.scale, g.seq_lens, wl.lmax,
+                           share_first_query=bool(wl.share_first_query), outs=outs, lses=lses, idx=idx_fs, ws=ws_fs,
+                           stream=stream)
+
     def step(i, record):
         """One pass of the hot path. record = "index": timing events around the index scan only (an event
         record costs a few microseconds of queue time, so the timed steps carry just these two);
         "all": events around every stage."""
         pr = prepared[i % len(prepared)]
         g = pr["g"]
+        if group:
+            if record == "all":
+                # breakdown: index scan and top-k as separate calls, then the whole group call; the MLA
+                # launches are the group call minus those two stages
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                e[0].record(stream)
+                dsa.index_score(pr["qi"], pr["wi"], pr["keys"], g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores,
+                                stream=stream)
+                e[1].record(stream)
+                dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
+                e[2].record(stream)
+                e[3].record(stream)
+                group_call(pr, g)
+                e[4].record(stream)
+                ev["index"].append((e[0], e[1]))
+                ev["topk"].append((e[1], e[2]))
+                ev["group"].append((e[3], e[4]))
+            else:
+                group_call(pr, g)
+            return
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             e[0].record(stream)
@@ -206,14 +239,17 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    index_us = sum(a.elapsed_time(b) for a, b in ev["index"]) / len(ev["index"]) * 1e3
+    index_us = sum(a.elapsed_time(b) for a, b in ev["index"]) / len(ev["index"]) * 1e3 if ev["index"] else None
     # stage breakdown, outside the timed region: a few steps with events around every stage
-    ev = {k: [] for k in ("index", "topk", "mla")}
+    ev = {k: [] for k in ("index", "topk", "mla", "group")}
     for i in range(3):
         step(args.warmup + args.steps + i, "all")
     torch.cuda.synchronize()
-    avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items()}   # microseconds
-    avg["index"] = index_us
+    avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items() if v}   # microseconds
+    if group:
+        avg["mla"] = avg["group"] - avg["index"] - avg["topk"]
+    else:
+        avg["index"] = index_us
 
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
@@ -244,8 +280,11 @@ def main():
                    "planted": wl.planted},
         "roofline": roof,
         "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"],
-                       "note": "index_score: HIP events around the scan in every timed step; topk and sparse_mla: "
-                               "events around each stage in 3 steps after the timed region"},
+                       "note": ("one dsa_forward_shared call per timed step (all layers' MLA launched together); "
+                                "index_score and topk: events around separate calls in 3 steps after the timed "
+                                "region; sparse_mla: the group call minus those two" if group else
+                                "index_score: HIP events around the scan in every timed step; topk and sparse_mla: "
+                                "events around each stage in 3 steps after the timed region")},
         "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "index_tflops": iflops / index_s / 1e12,
         "mla_tflops": mflops * wl.n_layers / (avg["mla"] * 1e-6) / 1e12,

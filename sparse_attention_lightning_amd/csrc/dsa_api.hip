@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -109,17 +110,16 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 size_t dsa_workspace_size(int op, const dsa_batch_t* bt, int Hi, int H, int k, int n_layers) {
   (void)Hi;
-  (void)n_layers;
   if (!bt || bt->B < 1 || bt->Q < 1 || bt->L_max < 1 || k < 1) return 0;
   const int rows = bt->B * bt->Q;
   switch (op) {
     case DSA_OP_INDEX_SCORE: return 0;
     case DSA_OP_TOPK: return dsa::topk_workspace_bytes(rows, bt->L_max);
-    case DSA_OP_SPARSE_MLA: return (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k) : 0;
+    case DSA_OP_SPARSE_MLA: return (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k, 1) : 0;
     case DSA_OP_FORWARD_SHARED: {
       // scores + top-k state for every query token (the largest case), then the MLA partials
       size_t a = scores_bytes(rows, bt->L_max) + align256(dsa::topk_workspace_bytes(rows, bt->L_max));
-      size_t m = (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k) : 0;
+      size_t m = ((H == 64 || H == 128) && n_layers >= 1) ? dsa::sparse_mla_workspace_bytes(rows, H, k, n_layers) : 0;
       return a + align256(m);
     }
   }
@@ -166,7 +166,7 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H
   TRY(check_ptr(out, 16, who, "out"));
   if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse misaligned", who);
   TRY(check_cache(latent, batch->L_max, who, "latent"));
-  TRY(check_ws(ws, ws_bytes, dsa::sparse_mla_workspace_bytes(batch->B * batch->Q, H, k), who));
+  TRY(check_ws(ws, ws_bytes, dsa::sparse_mla_workspace_bytes(batch->B * batch->Q, H, k, 1), who));
   g_last_error.clear();
   return launched(dsa::launch_sparse_mla(host_batch(batch), q, H, host_cache(latent), idx, k, idx_q_stride,
                                          softmax_scale, out, lse, ws, (hipStream_t)stream),
@@ -218,11 +218,16 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
   TRY(launched(dsa::launch_index_score(sel, q_e4m3, w, Hi, host_cache(keys), scores, s), who));
   TRY(launched(dsa::launch_topk(sel, scores, k, idx_out, topk_ws, s), who));
   const int stride = share_first_query ? 0 : k;
+  std::vector<dsa::HostCache> lat(n_layers);
+  std::vector<float*> lse_l(n_layers);
   for (int l = 0; l < n_layers; ++l) {
-    TRY(launched(dsa::launch_sparse_mla(host_batch(batch), q_bf16[l], H, host_cache(&latents[l]), idx_out, k, stride,
-                                        softmax_scale, out[l], lse ? lse[l] : nullptr, mla_ws, s),
-                 who));
+    lat[l] = host_cache(&latents[l]);
+    lse_l[l] = lse ? lse[l] : nullptr;
   }
+  // all layers of the group in one launch (up to 8 at a time): they share the index set
+  TRY(launched(dsa::launch_sparse_mla_layers(host_batch(batch), q_bf16, H, lat.data(), idx_out, k, stride,
+                                             softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
+               who));
   return DSA_OK;
 }
 

@@ -27,11 +27,16 @@ hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float
 size_t topk_workspace_bytes(int rows, int L_max);
 hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t* idx, void* ws, hipStream_t s);
 
-// Sparse MLA (MQA mode). Workspace holds split partials.
+// Sparse MLA (MQA mode). Workspace holds split partials. Layers that share one index set go up
+// to kMlaMaxLayers per launch.
+constexpr int kMlaMaxLayers = 8;
 int sparse_mla_splits(int rows, int H, int k);
-size_t sparse_mla_workspace_bytes(int rows, int H, int k);
+size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers);
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out,
                              float* lse, void* ws, hipStream_t s);
+hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                    const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
+                                    float* const* lse, int n_layers, void* ws, hipStream_t s);
 
 }  // namespace dsa

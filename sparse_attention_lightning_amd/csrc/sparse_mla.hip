@@ -21,6 +21,9 @@
 // The softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV.
 // With several splits, each workgroup writes its normalised partial (o_s, lse_s) and a
 // combine kernel merges them: lse = log sum_s exp lse_s, o = sum_s exp(lse_s - lse) o_s.
+#include <algorithm>
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -53,6 +56,15 @@ typedef __bf16 part_t;
 typedef float part_t;
 #endif
 
+// Per-layer arguments of a launch over up to kMlaMaxLayers layers that share one index set
+// (IndexShare): blockIdx.y picks the layer.
+struct MlaLayers {
+  const uint16_t* q[kMlaMaxLayers];
+  CacheView lat[kMlaMaxLayers];
+  float* out[kMlaMaxLayers];
+  float* lse[kMlaMaxLayers];
+};
+
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
 #endif
@@ -60,34 +72,48 @@ typedef float part_t;
 #define DSA_MLA_MIN_SPLIT 128
 #endif
 
+// Splits per query token: enough workgroups to fill the chip while each split keeps a minimum
+// of tokens. Chosen per layer, so that a launch of several layers gives every layer exactly the
+// result of a launch of that layer alone.
 int sparse_mla_splits(int rows, int H, int k) {
   (void)H;
   int s = 1;
-  // enough workgroups to fill the chip while each split keeps a minimum of tokens
   while (rows * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < 16) s *= 2;
   return s;
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t sparse_mla_workspace_bytes(int rows, int H, int k) {
+// Split partials of one launch of nl layers: per layer [rows][splits][H][512] part_t, then
+// [rows][splits][H] fp32 lse.
+static size_t part_o_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * kDv * sizeof(part_t)); }
+static size_t part_lse_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * sizeof(float)); }
+static size_t launch_ws_bytes(int rows, int H, int k, int nl) {
   const int s = sparse_mla_splits(rows, H, k);
   if (s == 1) return 0;
-  return align256((size_t)rows * s * H * kDv * sizeof(part_t)) + align256((size_t)rows * s * H * sizeof(float));
+  return (size_t)nl * (part_o_layer(rows, s, H) + part_lse_layer(rows, s, H));
+}
+
+size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers) {
+  // layers go kMlaMaxLayers per launch; the last launch may hold fewer
+  size_t b = launch_ws_bytes(rows, H, k, std::min(n_layers, kMlaMaxLayers));
+  if (n_layers > kMlaMaxLayers && n_layers % kMlaMaxLayers)
+    b = std::max(b, launch_ws_bytes(rows, H, k, n_layers % kMlaMaxLayers));
+  return b;
 }
 
 typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
 
 __device__ __forceinline__ v8bf lds_v8bf(lds_ptr p) { return *(const __attribute__((address_space(3))) v8bf*)p; }
 
-// An LDS pointer the compiler may not look through: fragment reads at this pointer plus a
-// constant then keep the constant in the instruction's offset field, instead of the compiler
-// merging it into the XOR-swizzled base (it turns the addition of disjoint bits into an OR,
-// which the offset field cannot absorb) and computing a fresh address per fragment.
-__device__ __forceinline__ lds_ptr opaque_lds(const uint8_t* p) {
-  uint32_t a = (uint32_t)(uintptr_t)(lds_ptr)p;      // the 32-bit LDS address
+// An offset the compiler may not look through: fragment reads at (slot + offset) plus a constant
+// then keep the constant in the instruction's offset field, instead of the compiler merging it
+// into the XOR-swizzled offset (it turns the addition of disjoint bits into an OR, which the
+// offset field cannot absorb) and computing a fresh address per fragment. Only the offset is
+// hidden: the pointer keeps its LDS variable, which the wait analysis below relies on.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t a) {
   asm volatile("" : "+v"(a));
-  return (lds_ptr)(uintptr_t)a;
+  return a;
 }
 
 __device__ __forceinline__ v4bf lds_tr_read(lds_ptr p) {
@@ -128,11 +154,34 @@ __device__ __forceinline__ void wait_step(int pending) {
 
 template <int NW, int HT, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, CacheView lat, const int32_t* __restrict__ idx, int k, int idx_q_stride,
-    int Q, int H, int splits, int split_len, float scale_log2,
-    float* __restrict__ out, float* __restrict__ lse_out, part_t* __restrict__ part_o, float* __restrict__ part_lse) {
+    MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, int Q, int H, int splits,
+    int split_len, float scale_log2, part_t* __restrict__ part_o_all, float* __restrict__ part_lse_all,
+    int64_t part_o_stride, int64_t part_lse_stride) {
+  // layer blockIdx.y of the launch: its query, latent cache, outputs and partials
+  const int layer = blockIdx.y;
+  const uint16_t* __restrict__ q = layers.q[layer];
+  const CacheView lat = layers.lat[layer];
+  float* __restrict__ out = layers.out[layer];
+  float* __restrict__ lse_out = layers.lse[layer];
+  part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
+  float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
   constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kTileBytes];
+  // The ring of gathered tiles, as three LDS variables. While a direct-to-LDS load is in flight
+  // the compiler makes every LDS read that may alias its destination wait for it (a wait on the
+  // vector-memory counter, i.e. for every gather issued so far); reads and loads that name
+  // different LDS variables are known not to alias. With the step loop unrolled by three, every
+  // read and every load names its slot statically, so the gather of step st + 2 stays in flight
+  // through step st.
+  static_assert(kStages == 3, "three named ring slots");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kTileBytes];
+  auto ring_of = [&](auto slot) -> uint8_t* {
+    constexpr int S = decltype(slot)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else return ring2;
+  };
   __shared__ int rowid[kMaxK];
   __shared__ int redo_any;
 
@@ -178,9 +227,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   // segments of row group w, so one row id per lane serves all of its loads of a step.
   static_assert(NW == 4, "loads of a wave share one row group");
   const int my_row = 8 * wave + (lane >> 3);
-  auto issue_step = [&](int st) {
-    uint8_t* base = ring[st % kStages] + wave * 1024;
-    const int r = rowid[st * kTok + my_row];
+  // Steps past the last one load row 0 into a slot that is read no more: every step issues the
+  // same loads, so the number of loads in flight is the same on every path.
+  auto issue_step = [&](int st, auto slot) {
+    uint8_t* base = ring_of(slot) + wave * 1024;
+    const int r = st < n_steps ? rowid[st * kTok + my_row] : -1;
     const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0) + 16 * ((lane & 7) ^ ((my_row >> 1) & 7));
 #pragma unroll
     for (int sg = 0; sg < kSegs; ++sg)
@@ -188,9 +239,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                                        (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128)), 16, 0, 0);
   };
   // masked rows this wave landed: overwrite the dummy bytes with zeros
-  auto zero_masked = [&](int st) {
+  auto zero_masked = [&](int st, auto slot) {
     if (rowid[st * kTok + my_row] >= 0) return;
-    uint8_t* base = ring[st % kStages] + wave * 1024;
+    uint8_t* base = ring_of(slot) + wave * 1024;
 #pragma unroll
     for (int sg = 0; sg < kSegs; ++sg) *(v4i*)(base + sg * (kTok * 128) + 16 * lane) = (v4i){0, 0, 0, 0};
   };
@@ -231,16 +282,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       l_run[ht] = 0.f;
     }
     constexpr int kAheadSteps = kStages - 1;
-#pragma unroll
-    for (int a = 0; a < kAheadSteps; ++a)
-      if (a < n_steps) issue_step(a);
-    for (int st = 0; st < n_steps; ++st) {
-      wait_step(min(kAheadSteps - 1, n_steps - 1 - st) * my_dma);   // this step's rows have landed
-      zero_masked(st);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    issue_step(0, I0{});
+    issue_step(1, I1{});
+    // step st in ring slot S = st % 3
+    auto step_body = [&](int st, auto slot) {
+      constexpr int S = decltype(slot)::value;
+      static_assert(kAheadSteps == 2, "one step of loads in flight behind the current one");
+      wait_counts<my_dma, 15>();                       // this step's rows have landed
+      zero_masked(st, slot);
       wait_counts<63, 0>();                            // LDS writes done before the barrier
       __builtin_amdgcn_s_barrier();
-      if (st + kAheadSteps < n_steps) issue_step(st + kAheadSteps);   // its slot was last read in step st - 1
-      const uint8_t* tile = ring[st % kStages];
+      // into step st - 1's slot, which every wave has finished reading
+      issue_step(st + kAheadSteps, std::integral_constant<int, (S + kAheadSteps) % kStages>{});
+      const uint8_t* tile = ring_of(slot);
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
       const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
@@ -259,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int x = 0; x < 2; ++x) kb[mt][x] = opaque_lds(tile + (qk_base[mt] ^ (64 * x)));
+          for (int x = 0; x < 2; ++x) kb[mt][x] = (lds_ptr)tile + opaque_u32(qk_base[mt] ^ (64 * x));
         auto kfrag = [&](int i) {
           const int s2 = i >> 1, mt = i & 1;
           return lds_v8bf(kb[mt][s2 & 1] + (s2 >> 1) * (kTok * 128));
@@ -295,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) vb[hf][x] = opaque_lds(tile + (pv_base[hf] ^ (32 * x)));
+        for (int x = 0; x < 4; ++x) vb[hf][x] = (lds_ptr)tile + opaque_u32(pv_base[hf] ^ (32 * x));
       auto vfrag = [&](int nt) {
         const v4bf lo = lds_tr_read(vb[0][nt & 3] + (nt >> 2) * (kTok * 128));
         const v4bf hi = lds_tr_read(vb[1][nt & 3] + (nt >> 2) * (kTok * 128));
@@ -363,7 +419,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
           for (int i = 0; i < kFragBatch; ++i) vc[i] = vn[i];
         }
       }
+    };
+    // unrolled by the three ring slots, so that every step names its slots statically
+    for (int st = 0; st < n_steps; st += kStages) {
+      step_body(st, I0{});
+      if (st + 1 < n_steps) step_body(st + 1, I1{});
+      if (st + 2 < n_steps) step_body(st + 2, std::integral_constant<int, 2>{});
     }
+    wait_counts<0, 15>();                              // the loads past the last step have landed
     if (pass == 0) {
       if (__ballot(redo) != 0ull && lane == 0) atomicOr(&redo_any, 1);
       __syncthreads();
@@ -402,9 +465,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 }
 
 // Merge split partials: one workgroup per (query token, 2 heads), 128 threads x 4 dims per head.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const part_t* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse, int H, int splits,
-                                                          float* __restrict__ out, float* __restrict__ lse_out) {
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
+                                                          const float* __restrict__ part_lse_all, int H, int splits,
+                                                          int64_t part_o_stride, int64_t part_lse_stride) {
+  const int layer = blockIdx.y;
+  const part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
+  const float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
+  float* __restrict__ out = layers.out[layer];
+  float* __restrict__ lse_out = layers.lse[layer];
   const int hl = threadIdx.x >> 7, t = threadIdx.x & 127;
   const int bq = blockIdx.x / (H / 2);
   const int h = (blockIdx.x - bq * (H / 2)) * 2 + hl;
@@ -428,45 +496,67 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const part_t* __restri
 }
 
 template <int NW, int HT>
-static void launch_mla(int splits, int n_items, hipStream_t s, const uint16_t* q, CacheView lv, const int32_t* idx,
-                       int k, int idx_q_stride, int Q, int H, int split_len, float sl2, float* out, float* lse,
-                       part_t* part_o, float* part_lse) {
-  const dim3 block(NW * 64), grid((unsigned)n_items);
+static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L, const int32_t* idx, int k,
+                       int idx_q_stride, int Q, int H, int split_len, float sl2, part_t* part_o, float* part_lse,
+                       int64_t so, int64_t sl) {
+  const dim3 block(NW * 64);
   if (splits == 1)
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, 1,
-                       split_len, sl2, out, lse, nullptr, nullptr);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
+                       split_len, sl2, nullptr, nullptr, (int64_t)0, (int64_t)0);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true>), grid, block, 0, s, q, lv, idx, k, idx_q_stride, Q, H, splits,
-                       split_len, sl2, nullptr, nullptr, part_o, part_lse);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, splits,
+                       split_len, sl2, part_o, part_lse, so, sl);
+}
+
+hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                    const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
+                                    float* const* lse, int n_layers, void* ws, hipStream_t s) {
+  const int rows = bt.B * bt.Q;
+  const float sl2 = scale * kLog2e;
+  for (int l0 = 0; l0 < n_layers; l0 += kMlaMaxLayers) {
+    const int nl = std::min(kMlaMaxLayers, n_layers - l0);
+    MlaLayers L{};
+    for (int i = 0; i < nl; ++i) {
+      const HostCache& c = latents[l0 + i];
+      L.q[i] = q[l0 + i];
+      L.lat[i] = CacheView{(const uint8_t*)c.base, c.table, c.max_pages, c.page_size, kRowBytes, bt.L_max};
+      L.out[i] = out[l0 + i];
+      L.lse[i] = lse ? lse[l0 + i] : nullptr;
+    }
+    const int splits = sparse_mla_splits(rows, H, k);
+    int split_len = (k + splits - 1) / splits;
+    split_len = (split_len + kTok - 1) / kTok * kTok;
+    part_t* part_o = nullptr;
+    float* part_lse = nullptr;
+    int64_t so = 0, sl = 0;
+    if (splits > 1) {
+      // every layer of the launch has its own partials
+      so = (int64_t)(part_o_layer(rows, splits, H) / sizeof(part_t));
+      sl = (int64_t)(part_lse_layer(rows, splits, H) / sizeof(float));
+      part_o = (part_t*)ws;
+      part_lse = (float*)((char*)ws + (size_t)nl * part_o_layer(rows, splits, H));
+    }
+    const dim3 grid((unsigned)(rows * splits), (unsigned)nl);
+    // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64)
+    if (H == 128)
+      launch_mla<4, 2>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, part_o, part_lse, so, sl);
+    else
+      launch_mla<4, 1>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, part_o, part_lse, so, sl);
+    if (splits > 1)
+      hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2), (unsigned)nl), dim3(256), 0, s, L,
+                         part_o, part_lse, H, splits, so, sl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out, float* lse,
                              void* ws, hipStream_t s) {
-  CacheView lv{(const uint8_t*)latent.base, latent.table, latent.max_pages, latent.page_size, kRowBytes, bt.L_max};
-  const int rows = bt.B * bt.Q;
-  const int splits = sparse_mla_splits(rows, H, k);
-  int split_len = (k + splits - 1) / splits;
-  split_len = (split_len + kTok - 1) / kTok * kTok;
-  const int n_items = rows * splits;
-  const float sl2 = scale * kLog2e;
-  part_t* part_o = nullptr;
-  float* part_lse = nullptr;
-  if (splits > 1) {
-    part_o = (part_t*)ws;
-    part_lse = (float*)((char*)ws + align256((size_t)rows * splits * H * kDv * sizeof(part_t)));
-  }
-  // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64)
-  if (H == 128)
-    launch_mla<4, 2>(splits, n_items, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o,
-                     part_lse);
-  else
-    launch_mla<4, 1>(splits, n_items, s, q, lv, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, out, lse, part_o,
-                     part_lse);
-  if (splits > 1)
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2)), dim3(256), 0, s, part_o, part_lse, H,
-                       splits, out, lse);
-  return hipGetLastError();
+  float* lse_arr[1] = {lse};
+  return launch_sparse_mla_layers(bt, &q, H, &latent, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr, 1,
+                                  ws, s);
 }
 
 }  // namespace dsa
