@@ -95,4 +95,21 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-inclusive scans by DPP: row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15
+// and 31 carry the row totals across rows (lanes shifted in from outside a row read `id`).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWMASK, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_u32<0x111, 0xf>(x, id));
+  x = op(x, dpp_u32<0x112, 0xf>(x, id));
+  x = op(x, dpp_u32<0x114, 0xf>(x, id));
+  x = op(x, dpp_u32<0x118, 0xf>(x, id));
+  x = op(x, dpp_u32<0x142, 0xa>(x, id));
+  x = op(x, dpp_u32<0x143, 0xc>(x, id));
+  return x;
+}
+
 }  // namespace dsa

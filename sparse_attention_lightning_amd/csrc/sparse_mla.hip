@@ -65,6 +65,8 @@ struct MlaLayers {
   float* lse[kMlaMaxLayers];
 };
 
+constexpr int kMaxSplits = 16;                  // splits per query token, at most
+
 #ifndef DSA_MLA_TARGET_WGS
 #define DSA_MLA_TARGET_WGS 256
 #endif
@@ -78,7 +80,7 @@ struct MlaLayers {
 int sparse_mla_splits(int rows, int H, int k) {
   (void)H;
   int s = 1;
-  while (rows * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < 16) s *= 2;
+  while (rows * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < kMaxSplits) s *= 2;
   return s;
 }
 
@@ -464,10 +466,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   }
 }
 
-// Merge split partials: one workgroup per (query token, 2 heads), 128 threads x 4 dims per head.
+// Merge split partials: one workgroup per (query token, 2 heads), 128 threads x 4 dims per head;
+// every split's lse and partial are loaded before the merge, so the loads overlap.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
                                                           const float* __restrict__ part_lse_all, int H, int splits,
                                                           int64_t part_o_stride, int64_t part_lse_stride) {
+  typedef part_t p4 __attribute__((ext_vector_type(4)));
   const int layer = blockIdx.y;
   const part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
   const float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
@@ -476,18 +480,28 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
   const int hl = threadIdx.x >> 7, t = threadIdx.x & 127;
   const int bq = blockIdx.x / (H / 2);
   const int h = (blockIdx.x - bq * (H / 2)) * 2 + hl;
+  float ls[kMaxSplits];
+  p4 po[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int64_t ps = (int64_t)bq * splits + s;
+    ls[s] = s < splits ? part_lse[ps * H + h] : -INFINITY;
+    if (s < splits) po[s] = *(const p4*)(part_o + (ps * H + h) * kDv + 4 * t);
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[((int64_t)bq * splits + s) * H + h]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) mx = fmaxf(mx, ls[s]);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const int64_t ps = (int64_t)bq * splits + s;
-      const float wgt = expf(part_lse[ps * H + h] - mx);
-      den += wgt;
-      const part_t* src = part_o + (ps * H + h) * kDv + 4 * t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += wgt * (float)src[e];
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < splits) {
+        const float wgt = expf(ls[s] - mx);
+        den += wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wgt * (float)po[s][e];
+      }
     }
     acc *= 1.f / den;
   }

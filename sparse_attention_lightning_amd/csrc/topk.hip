@@ -268,18 +268,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
       }
     }
   }
-  // one atomic per wave reserves room for the wave's candidates
-  int incl = mine;
+  // one atomic per workgroup reserves room for its candidates: wave scans, then the four wave
+  // totals through LDS (the early returns above are workgroup-uniform)
+  __shared__ uint32_t wtot[kTkThreads / 64];
+  __shared__ uint32_t wg_base;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan((uint32_t)mine, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
+    for (int i = 0; i < kTkThreads / 64; ++i) t += wtot[i];
+    wg_base = t ? atomicAdd(&st->count, t) : 0u;
   }
-  const int total = __shfl(incl, 63, 64);
-  if (total == 0) return;
-  uint32_t base = 0;
-  if (lane == 63) base = atomicAdd(&st->count, (uint32_t)total);
-  base = __shfl(base, 63, 64) + (uint32_t)(incl - mine);
+  __syncthreads();
+  uint32_t base = wg_base;
+#pragma unroll
+  for (int i = 0; i < kTkThreads / 64; ++i) base += i < wave ? wtot[i] : 0u;
+  base += incl - (uint32_t)mine;
   uint2* cand = ws.cand + (int64_t)row * kTkCap;
   for (int c = 0; c < mine; ++c)
     if (base + c < (uint32_t)kTkCap) cand[base + c] = make_uint2(u[c], (uint32_t)pos[c]);
@@ -366,23 +373,6 @@ struct RowLds {
   int pos[kRCap];
   SelLds s;
 };
-
-// Wave-inclusive scans by DPP: row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15
-// and 31 carry the row totals across rows (lanes shifted in from outside a row read `id`).
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t id) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWMASK, 0xf, false);
-}
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t id, Op op) {
-  x = op(x, dpp_u32<0x111, 0xf>(x, id));
-  x = op(x, dpp_u32<0x112, 0xf>(x, id));
-  x = op(x, dpp_u32<0x114, 0xf>(x, id));
-  x = op(x, dpp_u32<0x118, 0xf>(x, id));
-  x = op(x, dpp_u32<0x142, 0xa>(x, id));
-  x = op(x, dpp_u32<0x143, 0xc>(x, id));
-  return x;
-}
 
 struct Blk {
   SelLds& S;

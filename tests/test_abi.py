@@ -140,3 +140,12 @@ def test_workspace_sizes_scale_with_batch():
     assert dsa.workspace_size(dsa.OP_INDEX_SCORE, 32, 1, 131072) == 0
     shared = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 32, 1, 131072)
     assert shared >= 32 * 131072 * 4 + big
+    # layers that share an index set are launched together (up to 8), each with its own split
+    # partials: the group's workspace grows with the layer count up to 8 and then stays
+    one = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=1)
+    four = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=4)
+    eight = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=8)
+    many = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=20)
+    mla1 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
+    assert mla1 > 0
+    assert four - one == 3 * mla1 and eight - one == 7 * mla1 and many == eight

@@ -300,6 +300,29 @@ def test_forward_shared_small(share_first):
                 check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
 
 
+@pytest.mark.parametrize("H", [128, 64])
+def test_forward_shared_many_layers(H):
+    """Ten layers share one index set: the library launches their MLA eight layers at a time
+    (two launches here). Every layer equals a separate sparse-MLA call bit for bit and matches
+    the oracle."""
+    wl = synth.small("indexshare_b8_1m_4layers", B=2, L=3000, L_max=3008, seq_lens=(3000, 2345), n_layers=10, H=H)
+    cpu, g = gpu_batch(wl)
+    lats = [lat_arg(g, l) for l in range(wl.n_layers)]
+    idx, res = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax)
+    o_idx, exact = oracle_idx(cpu, wl)
+    idx_np = np_(idx)
+    for b in range(wl.B):
+        check_topk_sets(idx_np[b, 0], o_idx[b, 0], exact[b, 0], wl.k)
+    for layer in range(wl.n_layers):
+        out, lse = dsa.sparse_mla_fwd(g.q_mla[layer], lats[layer], idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+        assert torch.equal(res[layer][0], out) and torch.equal(res[layer][1], lse), layer
+    for layer in (0, 8, 9):                                # one layer of each launch, and the last
+        ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[layer]), latent_cache(cpu, layer), o_idx, wl.scale)
+        out_l, lse_l = np_(res[layer][0]), np_(res[layer][1])
+        for b in range(wl.B):
+            check_mla(out_l[b, 0], lse_l[b, 0], ref_o[b, 0], ref_l[b, 0])
+
+
 @pytest.mark.parametrize("form", ["sampled", "row"])
 def test_topk_when_the_sample_misses(form):
     """Both sampled forms read a block-strided sample of each row: up to 512 blocks of 16
