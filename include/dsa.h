@@ -88,9 +88,9 @@ dsa_status dsa_index_score(const dsa_batch_t* batch, const uint8_t* q, const flo
  *           not allowed in scores 0..p.
  * 1 <= k <= 2048. ws: dsa_workspace_size(DSA_OP_TOPK, ...) bytes, 256-byte aligned.
  * Three implementations give identical results; the library picks one by shape (one workgroup
- * per row when rows hold at most 65536 scores, or at most 262144 with 128 rows or more; a
- * sampled-threshold form for other rows up to 262144 and for calls of longer rows above 8M
- * scores; else a chunked radix form). The environment variable DSA_TOPK_FORM =
+ * per row for rows of at most 32768 scores, of at most 65536 with 128 rows or more, or of at
+ * most 262144 with 256 rows or more; a sampled-threshold form for other rows up to 262144 and
+ * for calls of longer rows holding 8M scores or more; else a chunked radix form). The environment variable DSA_TOPK_FORM =
  * radix | sampled | row, read at each call, pins one of them (for tests and measurements). */
 dsa_status dsa_topk(const dsa_batch_t* batch, const float* scores, int k, int32_t* idx,
                     void* ws, size_t ws_bytes, void* stream);

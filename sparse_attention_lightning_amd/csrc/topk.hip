@@ -335,7 +335,7 @@ __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, i
 
 // ------------------------------------------------------------------------------------------ rowsel
 // The same selection (sample -> tau -> candidates >= tau -> exact select -> ordered emission)
-// by one workgroup of 1024 threads per row in a single launch, with the candidate list in LDS
+// by one workgroup of 512 threads per row in a single launch, with the candidate list in LDS
 // instead of global memory. It reads the row once plus an 8192-score sample, so it suits calls
 // with enough rows to fill the chip and rows short enough for one workgroup to stream. Being one
 // long chain of block-wide steps, it keeps each step short: wave scans and reductions by DPP
@@ -344,26 +344,28 @@ __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, i
 // against tau directly (float_key is monotone, so key >= tau is f >= the float of tau).
 namespace rowsel {
 
-constexpr int kRT = 1024;                  // threads per row workgroup
-constexpr int kRW = kRT / 64;              // waves
+constexpr int kRT = 512;                   // threads per row workgroup (two workgroups per CU)
 constexpr int kRCap = 4096;                // candidates kept in LDS (2 x the largest k)
-constexpr int kRSample = 512;              // sampled 16-score blocks (8192 scores, 2 float4 per thread)
-constexpr int kRWindow = 1 << 17;          // positions per emission bitmap window (16 KB)
+constexpr int kRSample = 512;              // sampled 16-score blocks (8192 scores) ...
+constexpr int kRSampleLong = 1024;         // ... and for rows above kRLongRow scores
+constexpr int kRLongRow = 1 << 17;
 constexpr int kRUnroll = 2;                // float4 per thread per gather pass (double-buffered)
 constexpr int kRBins = 4096;               // 12-bit radix levels
 constexpr int kRCPer = kRCap / kRT;        // candidate slots per thread
 static_assert(kRCap >= 2 * kMaxK, "room for about 1.5k candidates plus spread");
-static_assert(kRBins % kRT == 0, "whole bins per thread");
 
-// LDS of the block-wide selection steps (shared by the row form and the sampled form's
-// per-row kernels).
+// LDS of the block-wide selection steps of an NT-thread workgroup (shared by the row form and
+// the sampled form's per-row kernels).
+template <int NT>
 struct SelLds {
-  uint32_t bitmap[kRWindow / 32];
+  static constexpr int kWindow = NT * 128; // positions per emission bitmap window (4 words per thread)
+  static_assert(kRBins % NT == 0, "whole bins per thread");
+  uint32_t bitmap[kWindow / 32];
   union {
     uint32_t hist[2][kRBins];              // radix levels alternate between two histograms
     sampled::TkLds full;                   // the exact full-row fallback
   } h;
-  uint32_t wred[4][kRW];                   // per-wave partials, rotated over the block steps
+  uint32_t wred[4][NT / 64];               // per-wave partials, rotated over the block steps
   uint32_t res[2];
   uint32_t count;
 };
@@ -371,11 +373,13 @@ struct SelLds {
 struct RowLds {
   uint32_t key[kRCap];                     // candidates: key and position
   int pos[kRCap];
-  SelLds s;
+  SelLds<kRT> s;
 };
 
+template <int NT>
 struct Blk {
-  SelLds& S;
+  static constexpr int kW = NT / 64;       // waves
+  SelLds<NT>& S;
   int tid, lane, wave;
   int slot = 0;                            // wred slot of the next block step
   int cur = 0;                             // the histogram that is clean
@@ -389,7 +393,7 @@ struct Blk {
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kRW; ++i) {
+    for (int i = 0; i < kW; ++i) {
       const uint32_t t = w[i];
       before += i < wave ? t : 0u;
       tot += t;
@@ -414,7 +418,7 @@ struct Blk {
     olo = 0xFFFFFFFFu;
     ohi = 0u;
 #pragma unroll
-    for (int i = 0; i < kRW; ++i) {
+    for (int i = 0; i < kW; ++i) {
       olo = min(olo, w[i]);
       ohi = max(ohi, w2[i]);
     }
@@ -422,7 +426,7 @@ struct Blk {
   // The bin of hist[cur] holding the need-th largest counted element, and how many are still
   // needed from it (two barriers). Thread t owns bins [kRBins - 4(t+1), kRBins - 4t).
   __device__ void find_bin(int need, uint32_t& bin, int& rem) {
-    constexpr int PER = kRBins / kRT;
+    constexpr int PER = kRBins / NT;
     const uint32_t* hist = S.h.hist[cur];
     const int top = kRBins - PER * tid;
     uint32_t h[PER], mine = 0;
@@ -470,7 +474,7 @@ struct Blk {
         if (ok[e] && (uint32_t)((uint64_t)off >> bits) == prefix) atomicAdd(&hist[(off >> shift) & ((1u << w) - 1)], 1u);
       }
       uint32_t* other = S.h.hist[cur ^ 1];
-      for (int i = tid; i < kRBins; i += kRT) other[i] = 0u;
+      for (int i = tid; i < kRBins; i += NT) other[i] = 0u;
       __syncthreads();
       uint32_t b;
       int r;
@@ -490,20 +494,20 @@ __device__ __forceinline__ float key_float(uint32_t key) {
 }
 
 // tau (a key) for a row of n > 0 scores: a lower bound of the r-th largest of a block-strided
-// sample of up to kRSample 16-score blocks, r chosen so that about `target` of the row's scores
+// sample of up to NS 16-score blocks, r chosen so that about `target` of the row's scores
 // are expected to reach it. The histograms must be zero on entry; returns with them ready.
-template <bool VEC>
-__device__ uint32_t sample_tau(Blk& B, const float* __restrict__ srow, int n, int target) {
+template <int NT, int NS, bool VEC>
+__device__ uint32_t sample_tau(Blk<NT>& B, const float* __restrict__ srow, int n, int target) {
   const int tid = B.tid;
   const int n_blocks = (n + 15) / 16;
-  const int stride = (n_blocks + kRSample - 1) / kRSample;
+  const int stride = (n_blocks + NS - 1) / NS;
   const int s_blocks = (n_blocks + stride - 1) / stride;
-  constexpr int kPer = kRSample * 4 / kRT;             // float4 slots per thread
+  constexpr int kPer = NS * 4 / NT;                    // float4 slots per thread
   uint32_t sk[kPer * 4];
   bool sok[kPer * 4];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int v = tid + e * kRT;
+    const int v = tid + e * NT;
     const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
     float f[4];
     if (VEC && v < s_blocks * 4 && i0 + 3 < n) {
@@ -530,9 +534,9 @@ __device__ uint32_t sample_tau(Blk& B, const float* __restrict__ srow, int n, in
 // Exact top-k of the candidates held in registers (PER per thread; every score of the row that
 // can be among the k largest is a candidate, cnt >= k of them) written to out[0..k) in
 // ascending position order: the k-th largest key T, the ties at T by the lowest positions, then
-// an ordered emission through a bitmap of kRWindow positions at a time.
-template <int PER>
-__device__ void select_emit(Blk& B, const uint32_t (&ck)[PER], const int (&cp)[PER], const bool (&cok)[PER], int n,
+// an ordered emission through a bitmap of NT * 128 positions at a time.
+template <int NT, int PER>
+__device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&cp)[PER], const bool (&cok)[PER], int n,
                             int k, int32_t* __restrict__ out) {
   const int tid = B.tid;
   int rem;
@@ -557,16 +561,17 @@ __device__ void select_emit(Blk& B, const uint32_t (&ck)[PER], const int (&cp)[P
   for (int e = 0; e < PER; ++e)
     keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
   int emitted = 0;
-  for (int wbase = 0; wbase < n; wbase += kRWindow) {
-    for (int i = tid; i < kRWindow / 32; i += kRT) B.S.bitmap[i] = 0u;
+  constexpr int kWindow = SelLds<NT>::kWindow;
+  for (int wbase = 0; wbase < n; wbase += kWindow) {
+    for (int i = tid; i < kWindow / 32; i += NT) B.S.bitmap[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int q = cp[e] - wbase;
-      if (keep[e] && q >= 0 && q < kRWindow) atomicOr(&B.S.bitmap[q >> 5], 1u << (q & 31));
+      if (keep[e] && q >= 0 && q < kWindow) atomicOr(&B.S.bitmap[q >> 5], 1u << (q & 31));
     }
     __syncthreads();
-    constexpr int W = kRWindow / 32 / kRT;             // words per thread
+    constexpr int W = kWindow / 32 / NT;               // words per thread
     uint32_t words[W], pc = 0;
 #pragma unroll
     for (int e = 0; e < W; ++e) {
@@ -590,15 +595,15 @@ __device__ void select_emit(Blk& B, const uint32_t (&ck)[PER], const int (&cp)[P
   }
 }
 
-template <bool VEC>
+template <bool VEC, int NS>
 __global__ __launch_bounds__(kRT) void topk_row_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, int32_t* __restrict__ idx) {
   __shared__ RowLds R;
-  SelLds& S = R.s;
+  SelLds<kRT>& S = R.s;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
-  Blk B{S, tid, lane, tid >> 6};
+  Blk<kRT> B{S, tid, lane, tid >> 6};
   const sampled::TkRowInfo ri = sampled::tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
   int32_t* out = idx + (int64_t)row * k;
   for (int i = ri.m + tid; i < k; i += kRT) out[i] = -1;
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   // keep every score)
   float tau_f = -INFINITY;
   if (n > kRCap)
-    tau_f = key_float(sample_tau<VEC>(B, srow, n, 3 * k / 2));
+    tau_f = key_float(sample_tau<kRT, NS, VEC>(B, srow, n, 3 * k / 2));
   else
     __syncthreads();
 
@@ -696,14 +701,24 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   select_emit(B, ck, cp, cok, n, k, out);
 }
 
-hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, hipStream_t s) {
+template <bool VEC>
+static void launch_vec(const HostBatch& bt, const float* scores, int k, int32_t* idx, hipStream_t s) {
   const int rows = bt.B * bt.Q;
-  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
-    hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
-                       bt.in_Q, bt.L_max, k, idx);
+  // The count of scores above tau spreads as sqrt(target x sampling stride): longer rows take a
+  // denser sample so that the list still holds between k and kRCap of them nearly always.
+  if (bt.L_max > kRLongRow)
+    hipLaunchKernelGGL((topk_row_kernel<VEC, kRSampleLong>), dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens,
+                       bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, idx);
   else
-    hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
-                       bt.in_Q, bt.L_max, k, idx);
+    hipLaunchKernelGGL((topk_row_kernel<VEC, kRSample>), dim3(rows), dim3(kRT), 0, s, scores, bt.seq_lens,
+                       bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, idx);
+}
+
+hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx, hipStream_t s) {
+  if (bt.L_max % 4 == 0 && ((uintptr_t)scores & 15) == 0)
+    launch_vec<true>(bt, scores, k, idx, s);
+  else
+    launch_vec<false>(bt, scores, k, idx, s);
   return hipGetLastError();
 }
 
@@ -711,13 +726,15 @@ hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx,
 
 namespace sampled {
 
+constexpr int kST = 1024;                  // threads of the per-row sample and finish workgroups
+
 // sample: one 1024-thread workgroup per row; tau for about 2k candidates (rows that fit the
 // candidate list keep every score: tau = 0, below every key).
 template <bool VEC>
-__global__ __launch_bounds__(rowsel::kRT) void topk_sample_kernel(
+__global__ __launch_bounds__(kST) void topk_sample_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, TkWs ws) {
-  __shared__ rowsel::SelLds S;
+  __shared__ rowsel::SelLds<kST> S;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
@@ -726,42 +743,42 @@ __global__ __launch_bounds__(rowsel::kRT) void topk_sample_kernel(
     if (tid == 0) { st->count = 0; st->tau = 0u; }
     return;
   }
-  rowsel::Blk B{S, tid, tid & 63, tid >> 6};
-  for (int i = tid; i < 2 * rowsel::kRBins; i += rowsel::kRT) (&S.h.hist[0][0])[i] = 0u;
-  const uint32_t tau = rowsel::sample_tau<VEC>(B, scores + (int64_t)row * L_max, ri.n, 2 * k);
+  rowsel::Blk<kST> B{S, tid, tid & 63, tid >> 6};
+  for (int i = tid; i < 2 * rowsel::kRBins; i += kST) (&S.h.hist[0][0])[i] = 0u;
+  const uint32_t tau = rowsel::sample_tau<kST, rowsel::kRSample, VEC>(B, scores + (int64_t)row * L_max, ri.n, 2 * k);
   if (tid == 0) { st->tau = tau; st->count = 0; }
 }
 
 // finish: one 1024-thread workgroup per row over its candidate list (held in registers), or the
 // exact full-row scan when the list missed (fewer than k) or overflowed.
-__global__ __launch_bounds__(rowsel::kRT) void topk_finish_kernel(
+__global__ __launch_bounds__(kST) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
-  constexpr int PER = kTkCap / rowsel::kRT;
-  __shared__ rowsel::SelLds S;
+  constexpr int PER = kTkCap / kST;
+  __shared__ rowsel::SelLds<kST> S;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
   int32_t* out = idx + (int64_t)row * k;
-  for (int i = ri.m + tid; i < k; i += rowsel::kRT) out[i] = -1;
+  for (int i = ri.m + tid; i < k; i += kST) out[i] = -1;
   if (ri.m == ri.n) {                                  // keep every visible token
-    for (int i = tid; i < ri.n; i += rowsel::kRT) out[i] = i;
+    for (int i = tid; i < ri.n; i += kST) out[i] = i;
     return;
   }
-  rowsel::Blk B{S, tid, tid & 63, tid >> 6};
+  rowsel::Blk<kST> B{S, tid, tid & 63, tid >> 6};
   const int cnt = (int)ws.rows[row].count;
   if (cnt < k || cnt > kTkCap) {                       // the sample missed: exact scan of the row
-    finish_full_scan<rowsel::kRT>(scores + (int64_t)row * L_max, ri.n, k, out, S.h.full);
+    finish_full_scan<kST>(scores + (int64_t)row * L_max, ri.n, k, out, S.h.full);
     return;
   }
-  for (int i = tid; i < 2 * rowsel::kRBins; i += rowsel::kRT) (&S.h.hist[0][0])[i] = 0u;
+  for (int i = tid; i < 2 * rowsel::kRBins; i += kST) (&S.h.hist[0][0])[i] = 0u;
   const uint2* cand = ws.cand + (int64_t)row * kTkCap;
   uint32_t ck[PER];
   int cp[PER];
   bool cok[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int i = tid + e * rowsel::kRT;
+    const int i = tid + e * kST;
     cok[e] = i < cnt;
     const uint2 c = cok[e] ? cand[i] : make_uint2(0u, 0u);
     ck[e] = c.x;
@@ -775,11 +792,11 @@ template <bool VEC>
 static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
                        hipStream_t s) {
   const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
-  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), dim3(rowsel::kRT), 0, s, scores, bt.seq_lens, bt.q_pos,
+  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), dim3(kST), 0, s, scores, bt.seq_lens, bt.q_pos,
                      bt.Q, bt.in_Q, bt.L_max, k, w);
   hipLaunchKernelGGL(topk_gather_kernel<VEC>, dim3((unsigned)rows * n_chunks), dim3(kTkThreads), 0, s, scores,
                      bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, n_chunks, w);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(rowsel::kRT), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kST), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,
                      bt.in_Q, bt.L_max, k, w, idx);
 }
 
@@ -796,13 +813,6 @@ hipError_t launch(const HostBatch& bt, const float* scores, int k, int32_t* idx,
 
 }  // namespace sampled
 
-#ifndef DSA_TOPK_SAMPLED_MIN_SCORES
-#define DSA_TOPK_SAMPLED_MIN_SCORES (1 << 23)
-#endif
-#ifndef DSA_TOPK_ROW_MAX_LEN
-#define DSA_TOPK_ROW_MAX_LEN (1 << 18)
-#endif
-
 enum TopkForm { kFormAuto = 0, kFormRadix, kFormSampled, kFormRow };
 
 // DSA_TOPK_FORM = radix | sampled | row pins one form (all give identical results); unset or
@@ -816,18 +826,19 @@ static TopkForm forced_form() {
   return kFormAuto;
 }
 
-// One workgroup per row streams a row at a few tens of GB/s, so the one-launch row form wins
-// when rows are short (at most 64K scores) or many (128 rows or more, enough to fill the chip).
-// Other rows up to 256K go to the sampled form, whose gather spreads each row over the chip;
-// longer rows to the sampled form once a call holds more than 8M scores (rows x L_max), else to
-// the chunked radix form.
+// One workgroup per row streams a row at a few GB/s, so the one-launch row form wins when rows
+// are short (at most 32K scores) or many (128 rows or more up to 64K scores, 256 or more up to
+// 256K: two workgroups per CU then keep the chip busy). Other rows up to 256K go to the sampled
+// form, whose gather spreads each row over the chip; longer rows to the sampled form once a call
+// holds 8M scores (rows x L_max) or more, else to the chunked radix form.
 static TopkForm auto_form(const HostBatch& bt) {
   const int64_t rows = (int64_t)bt.B * bt.Q;
-  if (bt.L_max <= DSA_TOPK_ROW_MAX_LEN) {
-    if (bt.L_max <= (1 << 16) || rows >= 128) return kFormRow;
+  const int64_t L = bt.L_max;
+  if (L <= (1 << 18)) {
+    if (L <= (1 << 15) || (L <= (1 << 16) && rows >= 128) || rows >= 256) return kFormRow;
     return kFormSampled;
   }
-  if (rows * bt.L_max > (int64_t)DSA_TOPK_SAMPLED_MIN_SCORES) return kFormSampled;
+  if (rows * L >= (int64_t)(1 << 23)) return kFormSampled;
   return kFormRadix;
 }
 

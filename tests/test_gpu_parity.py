@@ -324,21 +324,24 @@ def test_forward_shared_many_layers(H):
 
 
 @pytest.mark.parametrize("form", ["sampled", "row"])
-def test_topk_when_the_sample_misses(form):
+@pytest.mark.parametrize("L", [131072, 200000])
+def test_topk_when_the_sample_misses(form, L):
     """Both sampled forms read a block-strided sample of each row: up to 512 blocks of 16
-    scores, one block in 16 on a 128K row. When exactly those blocks, or exactly the blocks
-    between them, carry the high scores, or every score is equal, the candidate list misses or
-    overflows and the exact full-row scan must produce the set."""
+    scores (the row form takes 1024 on rows above 128K scores), so one block in `stride`. When
+    exactly those blocks, or exactly the blocks between them, carry the high scores, or every
+    score is equal, the candidate list misses or overflows and the exact full-row scan must
+    produce the set."""
     rng = np.random.default_rng(21)
-    L = 131072
+    n_sample = 1024 if (form == "row" and L > 131072) else 512
+    stride = -(-(-(-L // 16)) // n_sample)
     s = (1.0 + rng.random((6, 1, L))).astype(np.float32)
     blk = np.arange(L) // 16
-    s[0, 0, blk % 32 == 0] += 100.0                # half of the sampled blocks
-    s[1, 0, blk % 32 != 0] += 100.0                # everything but them
+    s[0, 0, blk % (2 * stride) == 0] += 100.0      # half of the sampled blocks
+    s[1, 0, blk % (2 * stride) != 0] += 100.0      # everything but them
     s[2, 0, :] = np.float32(7.0)                   # every score equal: a flood of candidates
     s[3, 0, blk % 4 == 0] += 100.0                 # every fourth block
-    s[4, 0, blk % 16 == 0] += 100.0                # exactly the sampled blocks
-    s[5, 0, blk % 16 != 0] += 100.0                # everything but them
+    s[4, 0, blk % stride == 0] += 100.0            # exactly the sampled blocks
+    s[5, 0, blk % stride != 0] += 100.0            # everything but them
     for k in (2048, 300):
         got = run_topk(s, [L] * 6, k, form=form)
         assert np.array_equal(got, oracle_topk(s, [L] * 6, k)), k
