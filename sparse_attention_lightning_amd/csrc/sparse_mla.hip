@@ -200,29 +200,6 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   const int tok_end = min(k, tok_begin + split_len);
   const int n_steps = tok_end > tok_begin ? (tok_end - tok_begin + kTok - 1) / kTok : 0;
 
-  // query heads h0 + 16 ht + (l % 16) as the B operands of S^T = K . Q^T: 8 dims per lane per K step;
-  // issued first: they do not depend on the index list
-  v8bf qb[HT][kDqk / 32];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const uint16_t* qrow = q + ((int64_t)bq * H + h0 + 16 * ht + c16) * kDqk;
-#pragma unroll
-    for (int s = 0; s < kDqk / 32; ++s) qb[ht][s] = *(const v8bf*)(qrow + 32 * s + 8 * g);
-  }
-
-  // row index (into the cache's rows) of every token of the split, -1 for masked tokens
-  if (tid == 0) redo_any = 0;
-  for (int i = tid; i < n_steps * kTok; i += NW * 64) {
-    const int t = tok_begin + i;
-    const int pos = t < tok_end ? irow[t] : -1;
-    int r = -1;
-    if (pos >= 0)
-      r = lat.table ? lat.table[(int64_t)b * lat.max_pages + pos / lat.page_size] * lat.page_size + pos % lat.page_size
-                    : b * lat.L_max + pos;
-    rowid[i] = r;
-  }
-  __syncthreads();
-
   // Direct-to-LDS gather of step st: load d = (row group rg = d % 4, segment d / 4) lands rows
   // 8rg + l/8, slot l%8 of the segment, fetching the chunk that the swizzle puts there.
   // Loads are dealt round-robin over the waves; with 4 waves, wave w issues exactly the 9
@@ -240,6 +217,46 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
                                        (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128)), 16, 0, 0);
   };
+
+  // Row index (into the cache's rows) of every token of the split, -1 for masked tokens. The
+  // chain index -> block table -> gather is the kernel's start-up latency, so every index load
+  // goes out at once, then every table load (unconditional, a masked token reading the
+  // sequence's first entry, and in one branch, so that they issue as one batch), then the
+  // query: the loads complete in order, and the query's latency then overlaps the table's.
+  const int n_tok = n_steps * kTok;
+  constexpr int kPerThread = kMaxK / (NW * 64);
+  int pos_t[kPerThread], page_t[kPerThread] = {};
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = tid + e * NW * 64;
+    pos_t[e] = (i < n_tok && tok_begin + i < tok_end) ? irow[tok_begin + i] : -1;
+  }
+  const int32_t* trow = lat.table ? lat.table + (int64_t)b * lat.max_pages : nullptr;
+  if (trow) {                                          // block-uniform
+    const uint32_t ps = (uint32_t)lat.page_size;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) page_t[e] = trow[(uint32_t)max(pos_t[e], 0) / ps];
+  }
+
+  // query heads h0 + 16 ht + (l % 16) as the B operands of S^T = K . Q^T: 8 dims per lane per K step
+  v8bf qb[HT][kDqk / 32];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint16_t* qrow = q + ((int64_t)bq * H + h0 + 16 * ht + c16) * kDqk;
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s) qb[ht][s] = *(const v8bf*)(qrow + 32 * s + 8 * g);
+  }
+
+  if (tid == 0) redo_any = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = tid + e * NW * 64;
+    const int pos = pos_t[e];
+    if (i < n_tok)
+      rowid[i] = pos < 0 ? -1 : trow ? page_t[e] * lat.page_size + pos % lat.page_size : b * lat.L_max + pos;
+  }
+  __syncthreads();
+
   // masked rows this wave landed: overwrite the dummy bytes with zeros
   auto zero_masked = [&](int st, auto slot) {
     if (rowid[st * kTok + my_row] >= 0) return;
