@@ -29,7 +29,7 @@ METRIC = "sparse-attn decode tokens/s and HBM GB/s at 128K ctx; prefill indexer 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_b32_128k_paged")
     ap.add_argument("--rotate", type=int, default=3, help="independent input batches cycled through")
@@ -186,7 +186,7 @@ def main():
 
     def step(i, record):
         """One pass of the hot path. record = "index": timing events around the index scan only (an event
-        record costs a few microseconds of queue time, so the timed steps carry just these two);
+        record costs a few microseconds of queue time, so only every fourth timed step carries these two);
         "all": events around every stage."""
         pr = prepared[i % len(prepared)]
         g = pr["g"]
@@ -235,7 +235,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, "index")
+        step(args.warmup + i, "index" if i % 4 == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -283,7 +283,7 @@ def main():
                        "note": ("one dsa_forward_shared call per timed step (all layers' MLA launched together); "
                                 "index_score and topk: events around separate calls in 3 steps after the timed "
                                 "region; sparse_mla: the group call minus those two" if group else
-                                "index_score: HIP events around the scan in every timed step; topk and sparse_mla: "
+                                "index_score: HIP events around the scan in every fourth timed step; topk and sparse_mla: "
                                 "events around each stage in 3 steps after the timed region")},
         "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "index_tflops": iflops / index_s / 1e12,
