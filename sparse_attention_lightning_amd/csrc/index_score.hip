@@ -7,7 +7,8 @@
 // reduce-scatter across the four 16-lane groups leaves lane l with the score of key t + l: one
 // coalesced 256-byte store per 64 keys. Keys reach LDS through direct-to-LDS loads of 8 whole
 // rows (1 KB, wave-uniform base address) with rows XOR-swizzled by 16-byte chunk, so that the
-// 16 rows of one B operand read from LDS hit distinct banks.
+// rows of one B operand read from LDS hit distinct banks (the LDS serves 16-byte reads eight
+// lanes at a time over 32 banks; the swizzle by row & 7 spreads those eight rows).
 //
 // Two forms: decode (one query token per sequence: each wave streams its own key range through
 // a private ring, HBM-bound) and multi-query (prefill chunks, speculative verify: 8 query tokens
@@ -39,7 +40,7 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // ------------------------------------------------------------------------------------------
 // Multi-query form (prefill chunks, speculative verify): the query tokens of one sequence share
 // every key, so a workgroup of 8 waves, one query token each, stages each tile of 256 keys once
-// in LDS (direct-to-LDS loads into a 2-stage ring, rows XOR-swizzled by 16-byte chunk so the 16
+// in LDS (direct-to-LDS loads into a 2-stage ring, rows XOR-swizzled by 16-byte chunk so the
 // rows of one matrix-core operand fetch hit distinct banks). Each wave runs its 64 heads x 16
 // keys per group through 4 FP8 matrix-core products, pipelined with the ReLU / weighted head
 // sum of the previous group, and a 3-swap reduce-scatter leaves one key per lane for a
@@ -128,13 +129,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
   constexpr int my_dma = kMqDma / kMqWaves;
 
   // Load d covers rows 8d..8d+7 of the tile: lane l lands in row 8d + l/8, slot l%8, and fetches
-  // the 16-byte chunk that the swizzle puts there. The row's swizzle term (row >> 1) & 7 equals
-  // (4 (d & 1) + l / 16) & 7, so the lane's offset from the 8-row base is one of two constants
-  // and the base is wave-uniform: the 8 rows lie in one page (page sizes are multiples of 16),
-  // or inside the sequence when the cache is contiguous and L_max % 8 == 0; otherwise each lane
-  // clamps its own row. Groups past the last visible key re-read the group that holds it.
-  const uint32_t lane_off0 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((lane >> 4) & 7));
-  const uint32_t lane_off1 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((4 + (lane >> 4)) & 7));
+  // the 16-byte chunk that the swizzle puts there. The row's swizzle term row & 7 equals l / 8,
+  // so the lane's offset from the 8-row base is one constant and the base is wave-uniform: the
+  // 8 rows lie in one page (page sizes are multiples of 16), or inside the sequence when the
+  // cache is contiguous and L_max % 8 == 0; otherwise each lane clamps its own row. Groups past
+  // the last visible key re-read the group that holds it.
+  const uint32_t lane_off = (lane >> 3) * 128 + 16 * ((lane & 7) ^ (lane >> 3));
   const int last_group = pmax & ~7;
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)keys.table;     // read-only: scalar loads
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
     for (int i = 0; i < my_dma; ++i) {
       const int d = wave + kMqWaves * i;
       const int tr = min(t0 + tt * kMqTile + 8 * d, last_group);
-      const uint32_t off = (d & 1) ? lane_off1 : lane_off0;
+      const uint32_t off = lane_off;
       const uint8_t* src;
       if constexpr (ROWS == kRowsContiguous) {
         src = keys.base + ((int64_t)b * L_max + tr) * kDi + off;
@@ -189,9 +189,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
   for (int a = 0; a < kAhead; ++a)
     if (a < n_tiles) issue_tile(a);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // per-lane B fragment offsets in a 16-row group (the swizzle repeats every 16 rows)
-  const int b_lo = c16 * 128 + 16 * (g ^ ((c16 >> 1) & 7));
-  const int b_hi = c16 * 128 + 16 * ((g + 4) ^ ((c16 >> 1) & 7));
+  // per-lane B fragment offsets in a 16-row group (the swizzle repeats every 8 rows)
+  const int b_lo = c16 * 128 + 16 * (g ^ (c16 & 7));
+  const int b_hi = c16 * 128 + 16 * ((g + 4) ^ (c16 & 7));
   for (int tt = 0; tt < n_tiles; ++tt) {
     // tile tt has landed once only the later tiles' loads (at most kAhead - 1 tiles) are in flight
     const int later = min(kAhead - 1, n_tiles - 1 - tt) * my_dma;
@@ -336,15 +336,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void index_score_decode_kernel(
     const int pg = page0 + lane;
     if (pg <= p / keys.page_size && pg * keys.page_size < t_end) my_page = keys.table[(int64_t)b * keys.max_pages + pg];
   }
-  const uint32_t lane_off0 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((lane >> 4) & 7));
-  const uint32_t lane_off1 = (lane >> 3) * 128 + 16 * ((lane & 7) ^ ((4 + (lane >> 4)) & 7));
+  const uint32_t lane_off = (lane >> 3) * 128 + 16 * ((lane & 7) ^ (lane >> 3));
   const int last_group = p & ~7;
   auto issue_tile = [&](int tt) {
     uint8_t* lds = ring[wave][tt % kDecStages];
 #pragma unroll
     for (int d = 0; d < kDecTile / 8; ++d) {
       const int tr = min(t_begin + tt * kDecTile + 8 * d, last_group);
-      const uint32_t off = (d & 1) ? lane_off1 : lane_off0;
+      const uint32_t off = lane_off;
       const uint8_t* src;
       if constexpr (ROWS == kRowsContiguous) {
         src = keys.base + ((int64_t)b * L_max + tr) * kDi + off;
@@ -378,8 +377,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void index_score_decode_kernel(
   for (int a = 0; a < kAhead; ++a)
     if (a < n_tiles) issue_tile(a);
 
-  const int b_lo = c16 * 128 + 16 * (g ^ ((c16 >> 1) & 7));
-  const int b_hi = c16 * 128 + 16 * ((g + 4) ^ ((c16 >> 1) & 7));
+  const int b_lo = c16 * 128 + 16 * (g ^ (c16 & 7));
+  const int b_hi = c16 * 128 + 16 * ((g + 4) ^ (c16 & 7));
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   constexpr int my_dma = kDecTile / 8;
   for (int tt = 0; tt < n_tiles; ++tt) {
