@@ -9,3 +9,4 @@ from .dsa import (E4M3, Cache, attention_flops, bf16_to_f64, dense_mla_causal, e
                   forward_shared, index_scores, index_scores_batch, indexer_flops, query_positions,
                   select_topk, sparse_mla, sparse_mla_batch, sparse_mla_one, sparse_to_dense_ratio,
                   topk_batch)
+from .hisparse import HotBufferState, selected_pages, swap_in  # noqa: F401,E402
