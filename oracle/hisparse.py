@@ -22,8 +22,9 @@ Readings where the page is silent (listed with their reasons in the design notes
     its page (a hit or the step that pulled it in); a slot never used has clock -1;
   - a slot whose page the current step selected is never a victim, so the buffer must hold
     the step's whole selected set (n_slots >= the positions selected per sequence);
-  - among equally old slots the lower slot index goes first, and the i-th missing page in
-    ascending page order takes the i-th victim in ascending (clock, slot) order;
+  - among equally old slots the lower slot index goes first; the page fixes which slots are
+    evicted, not which freed slot each missing page takes: the i-th missing page in ascending
+    page order takes the i-th victim in ascending slot order;
   - the state also records, per logical page, the last step that selected it (page clock).
 
 State of one batch (all int32, -1 = none), as returned and consumed by swap_in():
@@ -88,7 +89,7 @@ def swap_in(state: HotBufferState, idx: np.ndarray, step: int, page_size: int, h
         # 2. LRU eviction among the slots this step does not use
         free = [s for s in range(n_slots) if state.slot_clock[b, s] < step]
         free.sort(key=lambda s: (int(state.slot_clock[b, s]), s))
-        victims = free[:len(missing)]
+        victims = sorted(free[:len(missing)])
         # 3. page-table update and H2D pull
         for p, s in zip(missing, victims):
             old = state.slot_page[b, s]
