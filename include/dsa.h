@@ -132,8 +132,52 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                               float softmax_scale, float* const* out, float* const* lse,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* HiSparse hot buffer ("GLM-5.2 inference deployment" page, HiSparse section: a GPU hot
+ * buffer over the KV cache kept whole in pinned host memory, driven by the step's top-K; one
+ * slot per KV page; the page gives 4096-6144 device slots and 8-10x that in host memory).
+ * Every sequence owns n_slots device slots of one page each; its whole latent cache stays in
+ * host memory. State, in device memory owned by the caller and kept across steps (every entry
+ * -1 before the first step):
+ *   block_table [B][max_pages] int32  physical page b*n_slots + s of each resident logical
+ *                                      page, else -1. {device_pool, block_table, max_pages,
+ *                                      page_size} is then the latent cache for dsa_sparse_mla_fwd.
+ *   slot_page   [B][n_slots]   int32  logical page held by each slot, else -1
+ *   slot_clock  [B][n_slots]   int32  last step whose selected set used the slot, else -1
+ *   page_clock  [B][max_pages] int32  last step whose selected set held the page, else -1 */
+typedef struct {
+  int32_t* block_table;
+  int32_t* slot_page;
+  int32_t* slot_clock;
+  int32_t* page_clock;
+  int32_t max_pages;           /* (host) logical pages per sequence                          */
+  int32_t n_slots;             /* (host) device slots per sequence                           */
+  int32_t page_size;           /* (host) tokens per page (= per slot), a positive multiple of 16 */
+} dsa_hot_buffer_t;
+
+/* One swap-in step, after dsa_topk of the step (page's three steps: top-K miss detection, LRU
+ * eviction, page-table update with an asynchronous host-to-device pull).
+ *   idx          [B][n_sets][k] int32 selected positions as dsa_topk writes them (-1 skipped)
+ *   step         >= 0, larger than the step of every earlier call on the same state
+ *   host_pool    [B][max_pages][page_size][576] bf16, every page of every sequence: pinned host
+ *                memory mapped for the device (hipHostMalloc, torch pin_memory), or device
+ *                memory. Checked with hipPointerGetAttributes: DSA_ERR_INVALID_ARG otherwise.
+ *   device_pool  [B*n_slots][page_size][576] bf16 device memory
+ * Afterwards every page holding a selected position is resident. Hits refresh their slot's
+ * clock. The missing pages evict as many of the slots this step does not use, least recently
+ * used first (never-used slots have clock -1; equal clocks: lower slot first); the i-th missing
+ * page in ascending page order takes the i-th of those slots in ascending slot order, is copied
+ * from host_pool, and the page the slot held leaves block_table.
+ * Requires n_sets*k <= n_slots (DSA_ERR_UNSUPPORTED otherwise), so a step's selected set fits.
+ * The pages are read from host memory by the copy kernel itself: no host thread waits for the
+ * miss list. ws: dsa_workspace_size(DSA_OP_HISPARSE_SWAP_IN, batch with B, Q = n_sets and any
+ * L_max >= 1, 0, 0, k, 0) bytes, 256-byte aligned. */
+dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
+                                const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace sizes, from host fields of `batch` only (B, Q, L_max). */
-enum { DSA_OP_INDEX_SCORE = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD_SHARED = 3 };
+enum { DSA_OP_INDEX_SCORE = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD_SHARED = 3,
+       DSA_OP_HISPARSE_SWAP_IN = 4 };
 size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int Hi, int H, int k, int n_layers);
 
 const char* dsa_status_str(dsa_status s);

@@ -15,10 +15,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED = range(4)
+OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED, OP_HISPARSE_SWAP_IN = range(5)
 
 # every symbol include/dsa.h declares
-EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared",
+EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared", "dsa_hisparse_swap_in",
            "dsa_workspace_size", "dsa_status_str", "dsa_last_error")
 
 
@@ -30,6 +30,12 @@ class CacheT(C.Structure):
 class BatchT(C.Structure):
     _fields_ = [("B", C.c_int32), ("Q", C.c_int32), ("L_max", C.c_int32), ("seq_lens", C.c_void_p),
                 ("q_pos", C.c_void_p)]
+
+
+class HotBufferT(C.Structure):
+    _fields_ = [("block_table", C.c_void_p), ("slot_page", C.c_void_p), ("slot_clock", C.c_void_p),
+                ("page_clock", C.c_void_p), ("max_pages", C.c_int32), ("n_slots", C.c_int32),
+                ("page_size", C.c_int32)]
 
 
 class DsaError(RuntimeError):
@@ -53,13 +59,14 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_sparse_mla_fwd.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), P, I, I, F, P, P, P, S, P]
     lib.dsa_forward_shared.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
+    lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, S, P]
     lib.dsa_workspace_size.argtypes = [I, C.POINTER(BatchT), I, I, I, I]
     lib.dsa_workspace_size.restype = S
     lib.dsa_status_str.argtypes = [I]
     lib.dsa_status_str.restype = C.c_char_p
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = C.c_char_p
-    for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared"):
+    for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared", "dsa_hisparse_swap_in"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -198,3 +205,37 @@ def forward_shared(q_idx, w, keys: Cache, k: int, q_mla: Sequence, latents: Sequ
                                     int(share_first_query), nl, qs, H, lats, float(scale), os_, ls, idx.data_ptr(),
                                     _ptr(ws), n, _stream(stream)))
     return idx, list(zip(outs, lses))
+
+
+@dataclass
+class HotBuffer:
+    """HiSparse hot buffer of B sequences: device slots of one page each over a latent cache
+    kept whole in host memory. Every state tensor is int32 on the device, -1 before the first
+    step: block_table [B, max_pages], slot_page [B, n_slots], slot_clock [B, n_slots],
+    page_clock [B, max_pages]. device_pool [B * n_slots, page_size, 576] bf16."""
+    block_table: "object"
+    slot_page: "object"
+    slot_clock: "object"
+    page_clock: "object"
+    device_pool: "object"
+    page_size: int
+
+    def c(self) -> HotBufferT:
+        return HotBufferT(self.block_table.data_ptr(), self.slot_page.data_ptr(), self.slot_clock.data_ptr(),
+                          self.page_clock.data_ptr(), self.block_table.shape[1], self.slot_page.shape[1],
+                          self.page_size)
+
+    def latent_cache(self) -> Cache:
+        """The latent cache that sparse MLA reads once the step's pages are resident."""
+        return Cache(self.device_pool, self.block_table, self.page_size)
+
+
+def hisparse_swap_in(idx, step: int, hb: HotBuffer, host_pool, ws=None, stream=None):
+    """idx [B, n_sets, k] int32 from topk; host_pool [B, max_pages, page_size, 576] bf16 pinned."""
+    B, n_sets, k = idx.shape
+    bt = BatchT(B, n_sets, 1, None, None)
+    n = lib().dsa_workspace_size(OP_HISPARSE_SWAP_IN, C.byref(bt), 0, 0, k, 0)
+    ws = _workspace(n, idx.device, ws)
+    h = hb.c()
+    _check(lib().dsa_hisparse_swap_in(B, idx.data_ptr(), n_sets, k, int(step), C.byref(h), host_pool.data_ptr(),
+                                      hb.device_pool.data_ptr(), _ptr(ws), n, _stream(stream)))

@@ -1,6 +1,7 @@
 // C ABI of the DSA hot path: host-side validation, workspace sizing and launch order.
 // Every check runs before any HIP call, so a rejected call touches neither the GPU nor
-// the HIP runtime (this is what the CPU-only tests exercise).
+// the HIP runtime (this is what the CPU-only tests exercise). The one exception is the
+// swap-in's last check, a pointer query on its host pool, after all the others.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -116,6 +117,7 @@ size_t dsa_workspace_size(int op, const dsa_batch_t* bt, int Hi, int H, int k, i
     case DSA_OP_INDEX_SCORE: return 0;
     case DSA_OP_TOPK: return dsa::topk_workspace_bytes(rows, bt->L_max);
     case DSA_OP_SPARSE_MLA: return (H == 64 || H == 128) ? dsa::sparse_mla_workspace_bytes(rows, H, k, 1) : 0;
+    case DSA_OP_HISPARSE_SWAP_IN: return dsa::hisparse_workspace_bytes(bt->B, bt->Q * k);
     case DSA_OP_FORWARD_SHARED: {
       // scores + top-k state for every query token (the largest case), then the MLA partials
       size_t a = scores_bytes(rows, bt->L_max) + align256(dsa::topk_workspace_bytes(rows, bt->L_max));
@@ -229,6 +231,53 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                                              softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
                who));
   return DSA_OK;
+}
+
+dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
+                                const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
+                                void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "dsa_hisparse_swap_in";
+  if (B < 1 || n_sets < 1) return fail(DSA_ERR_INVALID_ARG, "%s: B=%d n_sets=%d must be >= 1", who, B, n_sets);
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
+  if (step < 0) return fail(DSA_ERR_INVALID_ARG, "%s: step=%d must be >= 0", who, step);
+  if (!hb) return fail(DSA_ERR_INVALID_ARG, "%s: hot buffer is NULL", who);
+  TRY(check_ptr(idx, 4, who, "idx"));
+  TRY(check_ptr(hb->block_table, 4, who, "block_table"));
+  TRY(check_ptr(hb->slot_page, 4, who, "slot_page"));
+  TRY(check_ptr(hb->slot_clock, 4, who, "slot_clock"));
+  TRY(check_ptr(hb->page_clock, 4, who, "page_clock"));
+  if (hb->page_size < 16 || hb->page_size % 16)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: page_size=%d must be a positive multiple of 16", who, hb->page_size);
+  if (hb->max_pages < 1 || hb->n_slots < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: max_pages=%d n_slots=%d must be >= 1", who, hb->max_pages, hb->n_slots);
+  if ((int64_t)n_sets * k > hb->n_slots)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: a step selects up to n_sets*k=%lld pages, more than n_slots=%d", who,
+                (long long)n_sets * k, hb->n_slots);
+  if ((int64_t)B * hb->n_slots >= (1LL << 31) || (int64_t)B * n_sets * k >= (1LL << 31) ||
+      (int64_t)hb->max_pages * hb->page_size > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: sizes beyond the int32 page and position ranges", who);
+  TRY(check_ptr(device_pool, 16, who, "device_pool"));
+  TRY(check_ptr(host_pool, 16, who, "host_pool"));
+  TRY(check_ws(ws, ws_bytes, dsa::hisparse_workspace_bytes(B, n_sets * k), who));
+  // The copy kernel reads host_pool in place: it must be memory the device can address.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_pool) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DSA_ERR_INVALID_ARG, "%s: host_pool is neither pinned host memory nor device memory", who);
+  }
+  const uint16_t* pool_dev = nullptr;
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.hostPointer)
+    pool_dev = (const uint16_t*)((const char*)attr.devicePointer + ((const char*)host_pool - (const char*)attr.hostPointer));
+  else if (attr.type == hipMemoryTypeDevice)
+    pool_dev = host_pool;
+  if (!pool_dev)
+    return fail(DSA_ERR_INVALID_ARG, "%s: host_pool is neither pinned, device-mapped host memory nor device memory", who);
+  g_last_error.clear();
+  const dsa::HostHotBuffer h{hb->block_table, hb->slot_page, hb->slot_clock, hb->page_clock,
+                             hb->max_pages, hb->n_slots, hb->page_size};
+  return launched(dsa::launch_hisparse_swap_in(B, idx, n_sets, k, step, h, pool_dev, device_pool, ws,
+                                               (hipStream_t)stream),
+                  who);
 }
 
 }  // extern "C"

@@ -39,4 +39,17 @@ hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* 
                                     const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
                                     float* const* lse, int n_layers, void* ws, hipStream_t s);
 
+// HiSparse hot buffer: top-k driven swap-in of latent pages from a host pool into per-sequence
+// device slots. Workspace: the copy list (page, slot) of every sequence and its length.
+struct HostHotBuffer {
+  int32_t* block_table;
+  int32_t* slot_page;
+  int32_t* slot_clock;
+  int32_t* page_clock;
+  int max_pages, n_slots, page_size;
+};
+size_t hisparse_workspace_bytes(int B, int cap);
+hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k, int32_t step, const HostHotBuffer& hb,
+                                   const uint16_t* host_pool, uint16_t* device_pool, void* ws, hipStream_t s);
+
 }  // namespace dsa

@@ -149,3 +149,51 @@ def test_workspace_sizes_scale_with_batch():
     mla1 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
     assert mla1 > 0
     assert four - one == 3 * mla1 and eight - one == 7 * mla1 and many == eight
+
+
+# ----------------------------------------------------------------------------- HiSparse swap-in
+def hot(table=A, slot_page=A, slot_clock=A, page_clock=A, max_pages=64, n_slots=4096, page=16):
+    from sparse_attention_lightning_amd._binding import HotBufferT
+    return HotBufferT(table, slot_page, slot_clock, page_clock, max_pages, n_slots, page)
+
+
+def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A, ws=A, ws_bytes=1 << 30):
+    hb = hot() if hb == "default" else hb
+    lib = dsa.lib()
+    return lib.dsa_hisparse_swap_in(B, idx, n_sets, k, step, C.byref(hb) if hb is not None else None, host, dev, ws,
+                                    ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(B=0), INVALID),
+    (dict(n_sets=0), INVALID),
+    (dict(k=0), UNSUPPORTED),
+    (dict(k=2049), UNSUPPORTED),
+    (dict(step=-1), INVALID),
+    (dict(hb=None), INVALID),
+    (dict(idx=None), INVALID),
+    (dict(idx=A + 2), INVALID),
+    (dict(hb=hot(table=None)), INVALID),
+    (dict(hb=hot(slot_page=A + 1)), INVALID),
+    (dict(hb=hot(slot_clock=None)), INVALID),
+    (dict(hb=hot(page_clock=None)), INVALID),
+    (dict(hb=hot(page=8)), UNSUPPORTED),
+    (dict(hb=hot(page=24)), UNSUPPORTED),
+    (dict(hb=hot(max_pages=0)), INVALID),
+    (dict(hb=hot(n_slots=2047)), UNSUPPORTED),             # one step's selected set must fit
+    (dict(n_sets=3, hb=hot(n_slots=6143)), UNSUPPORTED),
+    (dict(dev=None), INVALID),
+    (dict(dev=A + 8), INVALID),
+    (dict(host=None), INVALID),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=A + 64), WORKSPACE),
+    (dict(ws_bytes=16), WORKSPACE),
+])
+def test_swap_in_rejects_before_hip(case, expect):
+    assert call_swap(**case) == expect
+
+
+def test_swap_in_workspace_size():
+    n1 = dsa.workspace_size(dsa.OP_HISPARSE_SWAP_IN, 8, 1, 1, k=2048)
+    n2 = dsa.workspace_size(dsa.OP_HISPARSE_SWAP_IN, 8, 2, 1, k=2048)
+    assert n1 >= 2 * 8 * 2048 * 4 and n2 > n1 and n1 % 256 == 0
