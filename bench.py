@@ -144,7 +144,10 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    batches = [synth.generate(wl, seed=s, device=dev) for s in range(args.rotate)]
+    hot = wl.n_slots > 0
+    # A hot-buffer workload decodes consecutive steps over one cache, its indexer query
+    # drifting from step to step; the others cycle through independent batches.
+    batches = [synth.generate(wl, seed=s, device=dev) for s in range(1 if hot else args.rotate)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     rows_sel = wl.B * (1 if wl.share_first_query else wl.Q)
@@ -167,8 +170,27 @@ def main():
     q_pos = None
     if wl.share_first_query:   # scores + top-k for query token 0 of each sequence only
         q_pos = torch.tensor([[n - wl.Q] for n in wl.lens], dtype=torch.int32, device=dev)
-    ev = {k: [] for k in ("index", "topk", "mla", "group")}
-    # per-batch call arguments, built once (nothing but the three library calls runs in a step)
+    ev = {k: [] for k in ("index", "topk", "mla", "group", "swap")}
+    n_all_steps = args.warmup + args.steps + 3
+    if hot:
+        # HiSparse: the latent pages of every sequence in pinned host memory, logical order;
+        # the device keeps n_slots slots per sequence (state -1: empty before the warm-up)
+        g0 = batches[0]
+        host_pool = g0.latent[0][g0.latent_table[0].long()].cpu().pin_memory()
+        hb = dsa.HotBuffer(
+            block_table=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=dev),
+            slot_page=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=dev),
+            slot_clock=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=dev),
+            page_clock=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=dev),
+            device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=torch.bfloat16, device=dev),
+            page_size=wl.page_size)
+        hot_lat = hb.latent_cache()
+        drift = synth.drift_queries(g0, n_all_steps)
+        copied = torch.zeros((n_all_steps, wl.B), dtype=torch.int32, device=dev)
+        ws_swap = torch.empty(dsa.workspace_size(dsa.OP_HISPARSE_SWAP_IN, wl.B, wl.Q, 1, k=wl.k), dtype=torch.uint8,
+                              device=dev)
+        torch.cuda.synchronize()
+    # per-batch call arguments, built once (nothing but the library calls runs in a step)
     prepared = []
     for g in batches:
         prepared.append({
@@ -210,23 +232,29 @@ def main():
             else:
                 group_call(pr, g)
             return
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             e[0].record(stream)
-        dsa.index_score(pr["qi"], pr["wi"], pr["keys"], g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores, stream=stream)
+        qi = drift[i] if hot else pr["qi"]
+        dsa.index_score(qi, pr["wi"], pr["keys"], g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores, stream=stream)
         if record:
             e[1].record(stream)
         dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
         if record == "all":
             e[2].record(stream)
+        if hot:     # the step's selected pages into the device slots, then attention over them
+            dsa.hisparse_swap_in(idx, i, hb, host_pool, copied=copied[i], ws=ws_swap, stream=stream)
+            if record == "all":
+                e[4].record(stream)
+                ev["swap"].append((e[2], e[4]))
         for layer in range(wl.n_layers):
-            dsa.sparse_mla_fwd(g.q_mla[layer], pr["lats"][layer], idx,
+            dsa.sparse_mla_fwd(g.q_mla[layer], hot_lat if hot else pr["lats"][layer], idx,
                                wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0 if wl.share_first_query else wl.k,
                                out=outs[layer], lse=lses[layer], ws=ws_mla if n_mla else None, stream=stream)
         if record == "all":
             e[3].record(stream)
             ev["topk"].append((e[1], e[2]))
-            ev["mla"].append((e[2], e[3]))
+            ev["mla"].append((e[4] if hot else e[2], e[3]))
         if record:
             ev["index"].append((e[0], e[1]))
 
@@ -241,7 +269,7 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     index_us = sum(a.elapsed_time(b) for a, b in ev["index"]) / len(ev["index"]) * 1e3 if ev["index"] else None
     # stage breakdown, outside the timed region: a few steps with events around every stage
-    ev = {k: [] for k in ("index", "topk", "mla", "group")}
+    ev = {k: [] for k in ("index", "topk", "mla", "group", "swap")}
     for i in range(3):
         step(args.warmup + args.steps + i, "all")
     torch.cuda.synchronize()
@@ -289,6 +317,18 @@ def main():
         "index_tflops": iflops / index_s / 1e12,
         "mla_tflops": mflops * wl.n_layers / (avg["mla"] * 1e-6) / 1e12,
     }
+    if hot:
+        # pages pulled from host memory per timed step (the queries drift, so each step misses a part)
+        per_step = copied[args.warmup:args.warmup + args.steps].sum(dim=1).float().mean().item()
+        page_bytes = wl.page_size * 576 * 2
+        line["kernels_us"]["hisparse_swap_in"] = avg["swap"]
+        line["kernels_us"]["note"] += "; hisparse_swap_in: events around the swap-in in the same 3 steps"
+        line["hot_buffer"] = {
+            "slots_per_sequence": wl.n_slots, "page_tokens": wl.page_size, "pages_per_sequence": wl.max_pages,
+            "pages_copied_per_step": per_step, "bytes_copied_per_step": per_step * page_bytes,
+            "host_read_GBps": per_step * page_bytes / (avg["swap"] * 1e-6) / 1e9,
+            "note": "latent pages read by the copy kernel from pinned host memory; host_read_GBps = bytes copied "
+                    "per timed step / swap-in time of the breakdown steps"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(batches, wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -162,6 +162,7 @@ typedef struct {
  *                memory mapped for the device (hipHostMalloc, torch pin_memory), or device
  *                memory. Checked with hipPointerGetAttributes: DSA_ERR_INVALID_ARG otherwise.
  *   device_pool  [B*n_slots][page_size][576] bf16 device memory
+ *   copied       device [B] int32: pages copied for each sequence in this step, or NULL
  * Afterwards every page holding a selected position is resident. Hits refresh their slot's
  * clock. The missing pages evict as many of the slots this step does not use, least recently
  * used first (never-used slots have clock -1; equal clocks: lower slot first); the i-th missing
@@ -173,7 +174,7 @@ typedef struct {
  * L_max >= 1, 0, 0, k, 0) bytes, 256-byte aligned. */
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
                                 const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
-                                void* ws, size_t ws_bytes, void* stream);
+                                int32_t* copied, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace sizes, from host fields of `batch` only (B, Q, L_max). */
 enum { DSA_OP_INDEX_SCORE = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD_SHARED = 3,

@@ -59,7 +59,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_sparse_mla_fwd.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), P, I, I, F, P, P, P, S, P]
     lib.dsa_forward_shared.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
-    lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, S, P]
+    lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, P, S, P]
     lib.dsa_workspace_size.argtypes = [I, C.POINTER(BatchT), I, I, I, I]
     lib.dsa_workspace_size.restype = S
     lib.dsa_status_str.argtypes = [I]
@@ -230,12 +230,13 @@ class HotBuffer:
         return Cache(self.device_pool, self.block_table, self.page_size)
 
 
-def hisparse_swap_in(idx, step: int, hb: HotBuffer, host_pool, ws=None, stream=None):
-    """idx [B, n_sets, k] int32 from topk; host_pool [B, max_pages, page_size, 576] bf16 pinned."""
+def hisparse_swap_in(idx, step: int, hb: HotBuffer, host_pool, copied=None, ws=None, stream=None):
+    """idx [B, n_sets, k] int32 from topk; host_pool [B, max_pages, page_size, 576] bf16 pinned;
+    copied: optional device [B] int32 that receives the pages copied per sequence."""
     B, n_sets, k = idx.shape
     bt = BatchT(B, n_sets, 1, None, None)
     n = lib().dsa_workspace_size(OP_HISPARSE_SWAP_IN, C.byref(bt), 0, 0, k, 0)
     ws = _workspace(n, idx.device, ws)
     h = hb.c()
     _check(lib().dsa_hisparse_swap_in(B, idx.data_ptr(), n_sets, k, int(step), C.byref(h), host_pool.data_ptr(),
-                                      hb.device_pool.data_ptr(), _ptr(ws), n, _stream(stream)))
+                                      hb.device_pool.data_ptr(), _ptr(copied), _ptr(ws), n, _stream(stream)))

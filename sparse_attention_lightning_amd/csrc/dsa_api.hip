@@ -235,7 +235,7 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
 
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
                                 const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                int32_t* copied, void* ws, size_t ws_bytes, void* stream) {
   const char* who = "dsa_hisparse_swap_in";
   if (B < 1 || n_sets < 1) return fail(DSA_ERR_INVALID_ARG, "%s: B=%d n_sets=%d must be >= 1", who, B, n_sets);
   if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
@@ -258,6 +258,7 @@ dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, i
     return fail(DSA_ERR_UNSUPPORTED, "%s: sizes beyond the int32 page and position ranges", who);
   TRY(check_ptr(device_pool, 16, who, "device_pool"));
   TRY(check_ptr(host_pool, 16, who, "host_pool"));
+  if (copied && !aligned(copied, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: copied misaligned", who);
   TRY(check_ws(ws, ws_bytes, dsa::hisparse_workspace_bytes(B, n_sets * k), who));
   // The copy kernel reads host_pool in place: it must be memory the device can address.
   hipPointerAttribute_t attr;
@@ -275,7 +276,7 @@ dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, i
   g_last_error.clear();
   const dsa::HostHotBuffer h{hb->block_table, hb->slot_page, hb->slot_clock, hb->page_clock,
                              hb->max_pages, hb->n_slots, hb->page_size};
-  return launched(dsa::launch_hisparse_swap_in(B, idx, n_sets, k, step, h, pool_dev, device_pool, ws,
+  return launched(dsa::launch_hisparse_swap_in(B, idx, n_sets, k, step, h, pool_dev, device_pool, copied, ws,
                                                (hipStream_t)stream),
                   who);
 }

@@ -50,6 +50,7 @@ struct HostHotBuffer {
 };
 size_t hisparse_workspace_bytes(int B, int cap);
 hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k, int32_t step, const HostHotBuffer& hb,
-                                   const uint16_t* host_pool, uint16_t* device_pool, void* ws, hipStream_t s);
+                                   const uint16_t* host_pool, uint16_t* device_pool, int32_t* copied, void* ws,
+                                   hipStream_t s);
 
 }  // namespace dsa

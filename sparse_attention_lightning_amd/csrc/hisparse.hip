@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
                                                                int32_t* __restrict__ slot_clock,
                                                                const int32_t* __restrict__ page_clock, int max_pages,
                                                                int n_slots, int cap, int32_t* __restrict__ miss_page,
-                                                               int32_t* __restrict__ victim, int32_t* __restrict__ n_copy) {
+                                                               int32_t* __restrict__ victim, int32_t* __restrict__ n_copy,
+                                                               int32_t* __restrict__ copied) {
   __shared__ PlanLds L;
   const int b = blockIdx.x, tid = threadIdx.x;
   int32_t* bt = block_table + (int64_t)b * max_pages;
@@ -111,7 +112,10 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   }
   if (n_miss > (uint32_t)cap) n_miss = cap;             // the host check rules this out
   if (n_miss == 0) {                                     // workgroup-uniform
-    if (tid == 0) n_copy[b] = 0;
+    if (tid == 0) {
+      n_copy[b] = 0;
+      if (copied) copied[b] = 0;
+    }
     return;
   }
 
@@ -198,7 +202,10 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   // Every miss has a victim when the step selects at most n_slots pages and is later than
   // every step before it (the caller's contract); otherwise only the pairs that exist are made.
   const uint32_t n_pairs = min(n_miss, taken);
-  if (tid == 0) n_copy[b] = (int32_t)n_pairs;
+  if (tid == 0) {
+    n_copy[b] = (int32_t)n_pairs;
+    if (copied) copied[b] = (int32_t)n_pairs;
+  }
   __syncthreads();                                       // the lists are complete
 
   // ---- table updates: the i-th missing page takes the i-th victim in slot order (old pages
@@ -238,7 +245,8 @@ size_t hisparse_workspace_bytes(int B, int cap) {
 }
 
 hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k, int32_t step, const HostHotBuffer& hb,
-                                   const uint16_t* host_pool, uint16_t* device_pool, void* ws, hipStream_t s) {
+                                   const uint16_t* host_pool, uint16_t* device_pool, int32_t* copied, void* ws,
+                                   hipStream_t s) {
   const int cap = n_sets * k;
   const size_t list = ((size_t)B * cap * sizeof(int32_t) + 255) & ~(size_t)255;
   int32_t* miss_page = (int32_t*)ws;
@@ -248,7 +256,7 @@ hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k,
   hipLaunchKernelGGL(hs::hs_mark_kernel, dim3((unsigned)(B * n_sets * chunks)), dim3(256), 0, s, idx, n_sets, k, chunks,
                      step, hb.block_table, hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, hb.page_size);
   hipLaunchKernelGGL(hs::hs_plan_kernel, dim3(B), dim3(hs::kPlanThreads), 0, s, step, hb.block_table, hb.slot_page,
-                     hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, cap, miss_page, victim, n_copy);
+                     hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, cap, miss_page, victim, n_copy, copied);
   hipLaunchKernelGGL(hs::hs_copy_kernel, dim3((unsigned)(B * cap)), dim3(hs::kCopyThreads), 0, s, host_pool, device_pool,
                      cap, miss_page, victim, n_copy, hb.max_pages, hb.n_slots, hb.page_size);
   return hipGetLastError();

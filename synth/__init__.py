@@ -33,7 +33,7 @@ DQK = 576       # latent row: 512 latent + 64 RoPE
 DV = 512        # value part of the latent row
 
 # generator streams
-S_QIDX, S_KEYS, S_W, S_QMLA, S_LATENT, S_TABLE, S_PLANT_POS, S_PLANT_NOISE = 1, 2, 3, 4, 5, 6, 7, 8
+S_QIDX, S_KEYS, S_W, S_QMLA, S_LATENT, S_TABLE, S_PLANT_POS, S_PLANT_NOISE, S_DRIFT = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 @dataclass(frozen=True)
@@ -58,6 +58,8 @@ class Workload:
     share_first_query: int = 0
     L_max: int = 0                       # 0 -> L
     seq_lens: Optional[tuple] = None     # ragged lengths; None -> all L
+    n_slots: int = 0                     # > 0: latent pages live in host memory, n_slots device slots per sequence
+    drift_heads: int = 0                 # indexer query heads redrawn from one decode step to the next
 
     @property
     def lmax(self) -> int:
@@ -85,6 +87,12 @@ WORKLOADS = {
     "verify_b64_q8_32k": Workload("verify_b64_q8_32k", B=64, Q=8, L=32768, page_size=64),
     "verify_b64_q8_32k_draftshare": Workload("verify_b64_q8_32k_draftshare", B=64, Q=8, L=32768, page_size=64,
                                              share_first_query=1),
+    # HiSparse: 1M-token decode with the latent cache in pinned host memory and a device
+    # buffer of 6144 slots of one 16-token page per sequence (the GLM-5.2 inference page gives
+    # 4096-6144 slots and a host : device ratio of 8-10; 65536 pages / 6144 slots = 10.7).
+    # Consecutive decode steps redraw 4 of the 64 indexer query heads.
+    "hisparse_b8_1m_decode": Workload("hisparse_b8_1m_decode", B=8, Q=1, L=1048576, page_size=16,
+                                      n_slots=6144, drift_heads=4),
 }
 
 
@@ -201,3 +209,21 @@ def generate(wl: Workload, seed: int = 0, device="cpu", layers: Optional[int] = 
 def small(name: str, **kw) -> Workload:
     """A scaled-down variant of a named workload (same structure, smaller sizes)."""
     return replace(WORKLOADS[name], **kw)
+
+
+def drift_queries(batch: Batch, n_steps: int, seed: int = 0) -> List[torch.Tensor]:
+    """Indexer queries of n_steps consecutive decode steps: step 0 is the batch's own query;
+    each later step redraws wl.drift_heads heads (chosen at random) of the step before with
+    fresh E4M3FN(N(0,1)) values, so consecutive selected sets overlap without being equal."""
+    wl = batch.wl
+    dev = batch.q_idx.device
+    qs = [batch.q_idx]
+    gsel = _gen(seed, S_DRIFT, 0, "cpu")
+    for t in range(1, n_steps):
+        q = qs[-1].clone()
+        fresh = e4m3_normal((wl.B, wl.Q, wl.drift_heads, DI), _gen(seed, S_DRIFT, t, dev), dev)
+        for b in range(wl.B):
+            heads = torch.randperm(wl.Hi, generator=gsel)[: wl.drift_heads].to(dev)
+            q[b, :, heads] = fresh[b]
+        qs.append(q)
+    return qs

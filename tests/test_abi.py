@@ -157,11 +157,11 @@ def hot(table=A, slot_page=A, slot_clock=A, page_clock=A, max_pages=64, n_slots=
     return HotBufferT(table, slot_page, slot_clock, page_clock, max_pages, n_slots, page)
 
 
-def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A, ws=A, ws_bytes=1 << 30):
+def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A, copied=None, ws=A, ws_bytes=1 << 30):
     hb = hot() if hb == "default" else hb
     lib = dsa.lib()
-    return lib.dsa_hisparse_swap_in(B, idx, n_sets, k, step, C.byref(hb) if hb is not None else None, host, dev, ws,
-                                    ws_bytes, None)
+    return lib.dsa_hisparse_swap_in(B, idx, n_sets, k, step, C.byref(hb) if hb is not None else None, host, dev,
+                                    copied, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -185,6 +185,7 @@ def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A,
     (dict(dev=None), INVALID),
     (dict(dev=A + 8), INVALID),
     (dict(host=None), INVALID),
+    (dict(copied=A + 2), INVALID),
     (dict(ws=None), WORKSPACE),
     (dict(ws=A + 64), WORKSPACE),
     (dict(ws_bytes=16), WORKSPACE),

@@ -75,9 +75,11 @@ def test_swap_in_matches_oracle(B, n_sets, k, ps, max_pages, n_slots, steps, kee
         n_valid = rng.integers(max(1, k // 2), k + 1, size=B)
         idx = random_sets(rng, B, n_sets, k, L, n_valid, prev, keep)
         prev = idx
-        dsa.hisparse_swap_in(torch.from_numpy(idx).to(DEV), step, hb, host)
-        oracle.swap_in(st, idx, step, ps, host_np, dev_np)
+        copied = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        dsa.hisparse_swap_in(torch.from_numpy(idx).to(DEV), step, hb, host, copied=copied)
+        copies = oracle.swap_in(st, idx, step, ps, host_np, dev_np)
         compare(hb, st, dev_np, step)
+        assert copied.cpu().tolist() == [sum(1 for c in copies if c[0] == b) for b in range(B)], step
 
 
 def test_repeated_positions_and_empty_sets():
@@ -126,7 +128,6 @@ def test_attention_over_the_hot_buffer_equals_the_whole_cache():
     """Top-k positions -> swap-in -> sparse MLA through the hot buffer's block table gives the
     bits that sparse MLA over the whole cache gives (the rows are the same, only their place
     in memory differs)."""
-    import synth
     B, Q, L, k, ps, H = 2, 1, 4096, 512, 16, 128
     max_pages, n_slots = L // ps, 512
     gen = torch.Generator().manual_seed(11)
@@ -150,4 +151,3 @@ def test_attention_over_the_hot_buffer_equals_the_whole_cache():
         o2, l2 = dsa.sparse_mla_fwd(q, whole, idx, k, scale, lens, L)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), step
-    del synth
