@@ -8,8 +8,9 @@
 // radix form (topk_radix.hip) for small calls of long rows. The sampled form takes three
 // launches:
 //   sample   one 1024-thread workgroup per row reads a block-strided sample (whole 64-byte
-//            lines, up to 512 blocks of 16 scores) and radix-selects a lower bound tau of the
-//            sample rank that about 2k of the row's scores are expected to reach.
+//            lines, up to 512 blocks of 16 scores, 1024 on rows above 128K) and radix-selects a
+//            lower bound tau of the sample rank that about 2k (2.5k above 128K) of the row's
+//            scores are expected to reach.
 //   gather   chunk workgroups over the whole row append (key, position) of every score >= tau
 //            to the row's candidate list (wave-aggregated atomics; order is irrelevant).
 //   finish   one 1024-thread workgroup per row. If the list holds between k and kTkCap
@@ -728,12 +729,12 @@ namespace sampled {
 
 constexpr int kST = 1024;                  // threads of the per-row sample and finish workgroups
 
-// sample: one 1024-thread workgroup per row; tau for about 2k candidates (rows that fit the
-// candidate list keep every score: tau = 0, below every key).
-template <bool VEC>
+// sample: one 1024-thread workgroup per row; tau for about `target` candidates (rows that fit
+// the candidate list keep every score: tau = 0, below every key).
+template <bool VEC, int NS>
 __global__ __launch_bounds__(kST) void topk_sample_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
-    int Q, int in_Q, int L_max, int k, TkWs ws) {
+    int Q, int in_Q, int L_max, int k, int target, TkWs ws) {
   __shared__ rowsel::SelLds<kST> S;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(kST) void topk_sample_kernel(
   }
   rowsel::Blk<kST> B{S, tid, tid & 63, tid >> 6};
   for (int i = tid; i < 2 * rowsel::kRBins; i += kST) (&S.h.hist[0][0])[i] = 0u;
-  const uint32_t tau = rowsel::sample_tau<kST, rowsel::kRSample, VEC>(B, scores + (int64_t)row * L_max, ri.n, 2 * k);
+  const uint32_t tau = rowsel::sample_tau<kST, NS, VEC>(B, scores + (int64_t)row * L_max, ri.n, target);
   if (tid == 0) { st->tau = tau; st->count = 0; }
 }
 
@@ -792,8 +793,16 @@ template <bool VEC>
 static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
                        hipStream_t s) {
   const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
-  hipLaunchKernelGGL(topk_sample_kernel<VEC>, dim3(rows), dim3(kST), 0, s, scores, bt.seq_lens, bt.q_pos,
-                     bt.Q, bt.in_Q, bt.L_max, k, w);
+  // The candidate count spreads as sqrt(target x sampling stride). Rows above 128K scores take
+  // a denser sample and aim at 2.5k, midway between the bounds k and kTkCap (4k at the largest
+  // k), so that a sample miss (and the exact full-row scan it costs) stays rare at 1M scores
+  // per row.
+  if (bt.L_max > rowsel::kRLongRow)
+    hipLaunchKernelGGL((topk_sample_kernel<VEC, rowsel::kRSampleLong>), dim3(rows), dim3(kST), 0, s, scores,
+                       bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, 5 * k / 2, w);
+  else
+    hipLaunchKernelGGL((topk_sample_kernel<VEC, rowsel::kRSample>), dim3(rows), dim3(kST), 0, s, scores,
+                       bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, 2 * k, w);
   hipLaunchKernelGGL(topk_gather_kernel<VEC>, dim3((unsigned)rows * n_chunks), dim3(kTkThreads), 0, s, scores,
                      bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, bt.L_max, k, n_chunks, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kST), 0, s, scores, bt.seq_lens, bt.q_pos, bt.Q,

@@ -153,3 +153,43 @@ def test_verify_b64_q8_32k(name):
     else:
         for j in (0, 3, 7):
             oracle_check_query(g, wl, 5, j, scores, idx, outs, lses)
+
+
+def test_hisparse_b8_1m_decode():
+    """The hot buffer at the benchmark's size: 8 sequences of 1M tokens, 6144 slots of 16
+    tokens each, the latent cache in pinned host memory, three drifting decode steps. After
+    each step the library's state equals the oracle's on the same selected sets (every table
+    entry), the slots written by the step hold the host bytes of their pages, and sparse MLA
+    over the hot buffer gives the bits of sparse MLA over the whole device cache."""
+    wl = synth.WORKLOADS["hisparse_b8_1m_decode"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    whole = dsa.Cache(g.latent[0], g.latent_table[0], wl.page_size)
+    host = g.latent[0][g.latent_table[0].long()].view(torch.int16).cpu().pin_memory()
+    host_np = host.numpy()
+    hb = dsa.HotBuffer(
+        block_table=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=DEV),
+        slot_page=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=DEV),
+        slot_clock=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=DEV),
+        page_clock=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=DEV),
+        device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=torch.bfloat16, device=DEV),
+        page_size=wl.page_size)
+    st = oracle.HotBufferState.empty(wl.B, wl.max_pages, wl.n_slots)
+    dev_np = np.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=np.int16)
+    for step, q in enumerate(synth.drift_queries(g, 3)):
+        scores = dsa.index_score(q, g.w, keys, g.seq_lens, wl.lmax)
+        idx = dsa.topk(scores, g.seq_lens, wl.k)
+        del scores
+        copied = torch.zeros((wl.B,), dtype=torch.int32, device=DEV)
+        dsa.hisparse_swap_in(idx, step, hb, host, copied=copied)
+        o1, l1 = dsa.sparse_mla_fwd(g.q_mla[0], hb.latent_cache(), idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+        o2, l2 = dsa.sparse_mla_fwd(g.q_mla[0], whole, idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), step
+        copies = oracle.swap_in(st, idx.cpu().numpy(), step, wl.page_size, host_np, dev_np)
+        for name in ("block_table", "slot_page", "slot_clock", "page_clock"):
+            assert np.array_equal(getattr(hb, name).cpu().numpy(), getattr(st, name)), (name, step)
+        assert copied.cpu().tolist() == [sum(1 for c in copies if c[0] == b) for b in range(wl.B)], step
+        pool = hb.device_pool.view(torch.int16)
+        for b, p, s in copies[:: max(1, len(copies) // 64)]:     # a sample of this step's copies
+            assert np.array_equal(pool[b * wl.n_slots + s].cpu().numpy(), host_np[b, p]), (step, b, p)

@@ -327,12 +327,12 @@ def test_forward_shared_many_layers(H):
 @pytest.mark.parametrize("L", [131072, 200000])
 def test_topk_when_the_sample_misses(form, L):
     """Both sampled forms read a block-strided sample of each row: up to 512 blocks of 16
-    scores (the row form takes 1024 on rows above 128K scores), so one block in `stride`. When
+    scores (1024 on rows above 128K scores), so one block in `stride`. When
     exactly those blocks, or exactly the blocks between them, carry the high scores, or every
     score is equal, the candidate list misses or overflows and the exact full-row scan must
     produce the set."""
     rng = np.random.default_rng(21)
-    n_sample = 1024 if (form == "row" and L > 131072) else 512
+    n_sample = 1024 if L > 131072 else 512
     stride = -(-(-(-L // 16)) // n_sample)
     s = (1.0 + rng.random((6, 1, L))).astype(np.float32)
     blk = np.arange(L) // 16
