@@ -85,6 +85,7 @@ def cpu_baseline(batches, wl, budget_s):
     import torch
 
     import oracle
+    import synth
 
     try:
         from threadpoolctl import threadpool_info
@@ -107,7 +108,9 @@ def cpu_baseline(batches, wl, budget_s):
         lats = [oracle.Cache(seq_rows(g.latent[l], g.latent_table[l]).view(np.uint16)) for l in range(len(g.latent))]
         q_idx = g.q_idx[b].cpu().numpy()
         w = g.w[b].cpu().numpy()
-        q_mla = [t[b].view(torch.int16).cpu().numpy().view(np.uint16) for t in g.q_mla]
+        q_src = synth.draft_queries(g, wl.draft_steps) if wl.draft_steps else g.q_mla
+        q_mla = [t[b].view(torch.int16).cpu().numpy().view(np.uint16) for t in q_src]
+        lat_of = (lambda i: lats[0]) if wl.draft_steps else (lambda i: lats[i])
         n = wl.lens[b]
         t0 = time.perf_counter()
         for j in range(rows_per_seq):
@@ -115,11 +118,11 @@ def cpu_baseline(batches, wl, budget_s):
             s = oracle.index_scores(q_idx[j], w[j], keys, 0, p, wl.lmax)
             idx = oracle.select_topk(s.astype(np.float32), p, wl.k)
             users = range(wl.Q) if wl.share_first_query else [j]
-            for layer in range(len(lats)):
+            for c in range(len(q_mla)):          # every layer, or every draft step of an MTP loop
                 for u in users:
-                    oracle.sparse_mla_one(q_mla[layer][u], lats[layer], 0, idx, wl.scale)
+                    oracle.sparse_mla_one(q_mla[c][u], lat_of(c), 0, idx, wl.scale)
         elapsed += time.perf_counter() - t0
-        done_tokens += wl.Q if wl.share_first_query else rows_per_seq
+        done_tokens += (wl.Q if wl.share_first_query else rows_per_seq) * max(1, wl.draft_steps)
         seqs += 1
         if elapsed >= budget_s:
             break
@@ -127,7 +130,7 @@ def cpu_baseline(batches, wl, budget_s):
             "kind": "oracle",
             "sample": f"{seqs} of {wl.B} sequences of {wl.name} (all {rows_per_seq * seqs} query tokens of the "
                       f"sample: index scores over every visible key, top-{wl.k}, sparse MLA over {wl.H} heads x "
-                      f"{len(lats)} layer(s)); {elapsed:.1f} s of oracle time; numpy float64, host threads={threads}, "
+                      f"{len(q_mla)} layer(s) or draft step(s)); {elapsed:.1f} s of oracle time; numpy float64, host threads={threads}, "
                       f"affinity cores={cores}"}
 
 
@@ -192,10 +195,19 @@ def main():
         torch.cuda.synchronize()
     # per-batch call arguments, built once (nothing but the library calls runs in a step)
     prepared = []
+    if wl.draft_steps:      # an MTP draft loop: one latent cache, a query per draft step
+        outs = [torch.empty((wl.B, wl.Q, wl.H, 512), dtype=torch.float32, device=dev) for _ in range(wl.draft_steps)]
+        lses = [torch.empty((wl.B, wl.Q, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.draft_steps)]
     for g in batches:
+        lats = [dsa.Cache(g.latent[layer], g.latent_table[layer], wl.page_size) for layer in range(wl.n_layers)]
+        if wl.draft_steps:
+            mla_calls = [(q, lats[0]) for q in synth.draft_queries(g, wl.draft_steps)]
+        else:
+            mla_calls = [(g.q_mla[layer], lats[layer]) for layer in range(wl.n_layers)]
         prepared.append({
             "keys": dsa.Cache(g.keys, g.key_table, wl.page_size),
-            "lats": [dsa.Cache(g.latent[layer], g.latent_table[layer], wl.page_size) for layer in range(wl.n_layers)],
+            "lats": lats,
+            "mla_calls": mla_calls,
             "qi": g.q_idx[:, :1].contiguous() if wl.share_first_query else g.q_idx,
             "wi": g.w[:, :1].contiguous() if wl.share_first_query else g.w,
             "g": g,
@@ -247,10 +259,11 @@ def main():
             if record == "all":
                 e[4].record(stream)
                 ev["swap"].append((e[2], e[4]))
-        for layer in range(wl.n_layers):
-            dsa.sparse_mla_fwd(g.q_mla[layer], hot_lat if hot else pr["lats"][layer], idx,
+        # every layer of the step (or every draft step of an MTP loop) attends over the one index set
+        for c, (q_mla, lat) in enumerate(pr["mla_calls"]):
+            dsa.sparse_mla_fwd(q_mla, hot_lat if hot else lat, idx,
                                wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0 if wl.share_first_query else wl.k,
-                               out=outs[layer], lse=lses[layer], ws=ws_mla if n_mla else None, stream=stream)
+                               out=outs[c], lse=lses[c], ws=ws_mla if n_mla else None, stream=stream)
         if record == "all":
             e[3].record(stream)
             ev["topk"].append((e[1], e[2]))
@@ -286,7 +299,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    tokens = wl.B * wl.Q
+    tokens = wl.B * wl.Q * max(1, wl.draft_steps)      # an MTP loop yields a draft token per draft step
     value = tokens / (ms_per_step / 1e3)
     ibytes, iflops = index_work(wl)
     mbytes, mflops = mla_work(wl)
@@ -298,13 +311,15 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_profile(args.workload)
     roof["kernel"] = "index_score (lightning indexer scan)"
-    step_bytes = ibytes + mbytes * wl.n_layers
+    n_mla_calls = wl.draft_steps or wl.n_layers
+    step_bytes = ibytes + mbytes * n_mla_calls
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3+bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "L": wl.L, "page_size": wl.page_size, "k": wl.k,
                    "Hi": wl.Hi, "H": wl.H, "n_layers": wl.n_layers, "share_first_query": wl.share_first_query,
+                   "draft_steps": wl.draft_steps, "hot_buffer_slots": wl.n_slots,
                    "planted": wl.planted},
         "roofline": roof,
         "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"],
@@ -315,7 +330,7 @@ def main():
                                 "events around each stage in 3 steps after the timed region")},
         "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "index_tflops": iflops / index_s / 1e12,
-        "mla_tflops": mflops * wl.n_layers / (avg["mla"] * 1e-6) / 1e12,
+        "mla_tflops": mflops * n_mla_calls / (avg["mla"] * 1e-6) / 1e12,
     }
     if hot:
         # pages pulled from host memory per timed step (the queries drift, so each step misses a part)

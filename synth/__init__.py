@@ -33,7 +33,8 @@ DQK = 576       # latent row: 512 latent + 64 RoPE
 DV = 512        # value part of the latent row
 
 # generator streams
-S_QIDX, S_KEYS, S_W, S_QMLA, S_LATENT, S_TABLE, S_PLANT_POS, S_PLANT_NOISE, S_DRIFT = 1, 2, 3, 4, 5, 6, 7, 8, 9
+S_QIDX, S_KEYS, S_W, S_QMLA, S_LATENT, S_TABLE, S_PLANT_POS, S_PLANT_NOISE, S_DRIFT, S_DRAFT = (1, 2, 3, 4, 5, 6, 7, 8,
+                                                                                          9, 10)
 
 
 @dataclass(frozen=True)
@@ -60,6 +61,7 @@ class Workload:
     seq_lens: Optional[tuple] = None     # ragged lengths; None -> all L
     n_slots: int = 0                     # > 0: latent pages live in host memory, n_slots device slots per sequence
     drift_heads: int = 0                 # indexer query heads redrawn from one decode step to the next
+    draft_steps: int = 0                 # > 0: an MTP draft loop of this many sequential steps per index set
 
     @property
     def lmax(self) -> int:
@@ -93,6 +95,11 @@ WORKLOADS = {
     # Consecutive decode steps redraw 4 of the 64 indexer query heads.
     "hisparse_b8_1m_decode": Workload("hisparse_b8_1m_decode", B=8, Q=1, L=1048576, page_size=16,
                                       n_slots=6144, drift_heads=4),
+    # MTP draft loop (GLM-5.2 inference page, MTP section): one MTP layer unrolled 7 times;
+    # KVShare: every draft step reads the main model's cache; IndexShare on MTP: the top-2048
+    # set is computed at step 1 and reused by the next 6 steps. Decode shape of the 128K batch.
+    "mtp_draft_b32_128k_paged": Workload("mtp_draft_b32_128k_paged", B=32, Q=1, L=131072, page_size=64,
+                                         planted=32, draft_steps=7),
 }
 
 
@@ -227,3 +234,11 @@ def drift_queries(batch: Batch, n_steps: int, seed: int = 0) -> List[torch.Tenso
             q[b, :, heads] = fresh[b]
         qs.append(q)
     return qs
+
+
+def draft_queries(batch: Batch, n_steps: int, seed: int = 0) -> List[torch.Tensor]:
+    """MLA queries of the n_steps draft steps of an MTP loop ([B, Q, H, 576] bf16 each, N(0,1)):
+    one shared MTP layer, so one latent cache, and a fresh query per step."""
+    wl = batch.wl
+    dev = batch.q_idx.device
+    return [bf16_normal((wl.B, wl.Q, wl.H, DQK), _gen(seed, S_DRAFT, s, dev), dev) for s in range(n_steps)]

@@ -345,3 +345,22 @@ def test_topk_when_the_sample_misses(form, L):
     for k in (2048, 300):
         got = run_topk(s, [L] * 6, k, form=form)
         assert np.array_equal(got, oracle_topk(s, [L] * 6, k)), k
+
+
+def test_mtp_draft_loop_reuses_the_step1_set():
+    """The MTP draft loop (one shared MTP layer unrolled over 7 steps; IndexShare on MTP: only
+    step 1 scores and selects): one index scan + top-k, then 7 sequential sparse-MLA calls over
+    that set, each with its own query. Every draft step matches the oracle on the step-1 set."""
+    wl = synth.small("mtp_draft_b32_128k_paged", B=2, L=4000, L_max=4032, planted=4, seq_lens=(4000, 2900))
+    cpu, g = gpu_batch(wl)
+    scores = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax)
+    idx = dsa.topk(scores, g.seq_lens, wl.k)
+    o_idx, exact = oracle_idx(cpu, wl)
+    for b in range(wl.B):
+        check_topk_sets(np_(idx)[b, 0], o_idx[b, 0], exact[b, 0], wl.k)
+    qs_cpu = synth.draft_queries(cpu, wl.draft_steps)
+    for s, q in enumerate(qs_cpu):
+        out, lse = dsa.sparse_mla_fwd(q.to(DEV), lat_arg(g), idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+        ref_o, ref_l = oracle.sparse_mla_batch(bits(q), latent_cache(cpu), np_(idx), wl.scale)
+        for b in range(wl.B):
+            check_mla(np_(out)[b, 0], np_(lse)[b, 0], ref_o[b, 0], ref_l[b, 0])
