@@ -20,14 +20,8 @@
 
 namespace dsa {
 
-#ifndef DSA_SCORE_CHUNK
-#define DSA_SCORE_CHUNK 2048
-#endif
-constexpr int kScoreChunk = DSA_SCORE_CHUNK;   // keys per workgroup of the decode form
-#ifndef DSA_DEC_WAVES
-#define DSA_DEC_WAVES 4
-#endif
-constexpr int kDecWaves = DSA_DEC_WAVES;          // waves per workgroup
+constexpr int kScoreChunk = 2048;              // keys per workgroup of the decode form
+constexpr int kDecWaves = 4;                    // waves per workgroup
 
 // XCD-aware work index: consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
 // remap so that each XCD walks a contiguous range of work items (items sharing keys share L2).
@@ -51,24 +45,10 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // integer max for the ReLU, a multiply-add), 8 per matrix-core product of 32 cycles, so every
 // other VALU instruction comes straight out of the matrix-core rate. Tile loads therefore take
 // wave-uniform (scalar) addresses and the reduce-scatter uses lane-swap instructions.
-#ifndef DSA_MQ_TILE
-#define DSA_MQ_TILE 256
-#endif
-#ifndef DSA_MQ_STAGES
-#define DSA_MQ_STAGES 2
-#endif
-#ifndef DSA_MQ_CHUNK
-#define DSA_MQ_CHUNK 4096
-#endif
-#ifndef DSA_MQ_SCHED
-#define DSA_MQ_SCHED 0
-#endif
-#ifndef DSA_MQ_AUX
-#define DSA_MQ_AUX 0                                  // cache policy of the tile loads
-#endif
-constexpr int kMqTile = DSA_MQ_TILE;                 // keys per LDS tile
-constexpr int kMqStages = DSA_MQ_STAGES;
-constexpr int kMqChunk = DSA_MQ_CHUNK;               // keys per workgroup
+constexpr int kMqTile = 256;                         // keys per LDS tile
+constexpr int kMqStages = 2;
+constexpr int kMqChunk = 4096;                       // keys per workgroup
+constexpr int kMqAux = 0;                            // cache policy of the tile loads: default
 constexpr int kMqDma = kMqTile / 8;                  // 1 KB direct-to-LDS loads per tile
 constexpr int kMqWaves = 8;                          // query tokens per workgroup
 static_assert(kMqChunk % kMqTile == 0 && kMqDma % kMqWaves == 0, "tile shape");
@@ -156,7 +136,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
         src = keys.base + ((int64_t)b * L_max + t) * kDi + (off & 127u);
       }
       __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lds + d * 1024),
-                                       16, 0, DSA_MQ_AUX);
+                                       16, 0, kMqAux);
     }
   };
 
@@ -243,14 +223,6 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) sum += wr[m][r] * relu(acc[gi & 1][m][r]);
       part[gi & 3] = sum;
-#if DSA_MQ_SCHED
-      if (gi + 2 < kG) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next-but-one fragment
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one product
-        __builtin_amdgcn_sched_group_barrier(0x002, DSA_MQ_SCHED, 0);         // then VALU
-      }
-#endif
       if ((gi & 3) == 3) {
         const float v = reduce_scatter4(part);        // lane 16c + j: key j of group c
         const int tk = tb + 64 * (gi >> 2) + lane;
@@ -282,13 +254,8 @@ static void launch_multi_rows(const HostBatch& bt, const uint8_t* q, const float
 // of 64 keys and waits on its own load counter only, so no workgroup barrier is involved. Two
 // stages keep LDS at 64 KB per workgroup, two workgroups per CU; the tile loads are marked
 // nontemporal (the keys are read once per step), which measured about 10% faster than cached.
-#ifndef DSA_DEC_STAGES
-#define DSA_DEC_STAGES 2
-#endif
-#ifndef DSA_DEC_AUX
-#define DSA_DEC_AUX 2                                 // cache policy of the tile loads: nontemporal
-#endif
-constexpr int kDecStages = DSA_DEC_STAGES;
+constexpr int kDecStages = 2;
+constexpr int kDecAux = 2;                           // cache policy of the tile loads: nontemporal
 constexpr int kDecTile = 64;                         // keys per ring slot: one reduce-scatter
 
 template <int VM>
@@ -355,7 +322,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void index_score_decode_kernel(
         src = keys.base + ((int64_t)b * L_max + t) * kDi + (off & 127u);
       }
       __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lds + d * 1024),
-                                       16, 0, DSA_DEC_AUX);
+                                       16, 0, kDecAux);
     }
   };
   v8i qa[MT];

@@ -33,28 +33,15 @@ constexpr int kTok = 32;                        // tokens per step
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kSegs = kRowBytes / 128;          // 9 segments of 128 B per row
 constexpr int kTileBytes = kTok * kRowBytes;    // 36 KB per step
-#ifndef DSA_MLA_STAGES
-#define DSA_MLA_STAGES 3
-#endif
-constexpr int kStages = DSA_MLA_STAGES;         // LDS ring depth: rows land kStages - 1 steps ahead
-#ifndef DSA_MLA_FRAG_BATCH
-#define DSA_MLA_FRAG_BATCH 2
-#endif
-constexpr int kFragBatch = DSA_MLA_FRAG_BATCH;  // LDS fragments per read batch
+constexpr int kStages = 3;                      // LDS ring depth: rows land kStages - 1 steps ahead
+constexpr int kFragBatch = 2;                   // LDS fragments per read batch
 constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-#ifndef DSA_MLA_PART_BF16
-#define DSA_MLA_PART_BF16 1
-#endif
 // Split partials: normalised outputs o_s (|o_s| <= the largest value entry, a convex
 // combination) stored as bf16 to halve their traffic, plus fp32 lse_s.
-#if DSA_MLA_PART_BF16
 typedef __bf16 part_t;
-#else
-typedef float part_t;
-#endif
 
 // Per-layer arguments of a launch over up to kMlaMaxLayers layers that share one index set
 // (IndexShare): blockIdx.y picks the layer.
@@ -67,12 +54,8 @@ struct MlaLayers {
 
 constexpr int kMaxSplits = 16;                  // splits per query token, at most
 
-#ifndef DSA_MLA_TARGET_WGS
-#define DSA_MLA_TARGET_WGS 256
-#endif
-#ifndef DSA_MLA_MIN_SPLIT
-#define DSA_MLA_MIN_SPLIT 128
-#endif
+constexpr int kTargetWgs = 256;                 // workgroups a launch aims at (one per CU)
+constexpr int kMinSplit = 128;                  // tokens per split, at least
 
 // Splits per query token: enough workgroups to fill the chip while each split keeps a minimum
 // of tokens. Chosen per layer, so that a launch of several layers gives every layer exactly the
@@ -80,7 +63,7 @@ constexpr int kMaxSplits = 16;                  // splits per query token, at mo
 int sparse_mla_splits(int rows, int H, int k) {
   (void)H;
   int s = 1;
-  while (rows * s < DSA_MLA_TARGET_WGS && (k + 2 * s - 1) / (2 * s) >= DSA_MLA_MIN_SPLIT && s < kMaxSplits) s *= 2;
+  while (rows * s < kTargetWgs && (k + 2 * s - 1) / (2 * s) >= kMinSplit && s < kMaxSplits) s *= 2;
   return s;
 }
 

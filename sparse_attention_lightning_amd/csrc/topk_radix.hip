@@ -25,12 +25,9 @@
 namespace dsa {
 namespace radix {
 
-#ifndef DSA_TOPK_VPT
-#define DSA_TOPK_VPT 4
-#endif
 constexpr int kTopkThreads = 256;
 constexpr int kTopkVec = 4;                                   // floats per load
-constexpr int kTopkVpt = DSA_TOPK_VPT;                        // vector loads per thread
+constexpr int kTopkVpt = 4;                                   // vector loads per thread
 constexpr int kTopkPer = kTopkVec * kTopkVpt;                 // scores per thread
 constexpr int kTopkChunk = kTopkThreads * kTopkPer;           // scores per workgroup
 constexpr int kNB1 = 2048, kNB2 = 2048, kNB3 = 1024;
