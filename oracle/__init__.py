@@ -6,7 +6,7 @@ may import this package. The GPU library and its Python binding never do.
 Pinned functions and what pins them are listed at the top of tests/test_oracle.py.
 """
 from .dsa import (E4M3, Cache, attention_flops, bf16_to_f64, dense_mla_causal, e4m3_to_f64,  # noqa: F401
-                  forward_shared, index_scores, index_scores_batch, indexer_flops, query_positions,
+                  forward_shared, index_scores, index_scores_batch, indexer_flops, latent_values, query_positions,
                   select_topk, sparse_mla, sparse_mla_batch, sparse_mla_one, sparse_to_dense_ratio,
                   topk_batch)
 from .hisparse import HotBufferState, selected_pages, swap_in  # noqa: F401,E402

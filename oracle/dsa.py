@@ -161,17 +161,26 @@ def topk_batch(scores32: np.ndarray, seq_lens, k: int, q_pos=None) -> np.ndarray
 
 
 # ----------------------------------------------------------------------------- step 3
-def sparse_mla(q_bits: np.ndarray, rows_bits: np.ndarray, scale: float):
+def latent_values(rows: np.ndarray, latent_scale: float = 1.0) -> np.ndarray:
+    """Latent rows as float64: bf16 bits (uint16), or E4M3FN codes (uint8) times the cache's
+    scale. The FP8 form reads the inference page's fp8_e4m3 KV-cache option; the pages give
+    no scale convention, so one scale per cache is the reading taken."""
+    if rows.dtype == np.uint8:
+        return e4m3_to_f64(rows) * float(latent_scale)
+    return bf16_to_f64(rows)
+
+
+def sparse_mla(q_bits: np.ndarray, rows_bits: np.ndarray, scale: float, latent_scale: float = 1.0):
     """MQA-mode attention of H query heads over m selected latent rows.
 
-    q_bits [H, 576] bf16 bits, rows_bits [m, 576] bf16 bits (m may be 0).
+    q_bits [H, 576] bf16 bits, rows_bits [m, 576] bf16 bits or E4M3 codes (m may be 0).
     Returns (o [H, 512] float64, lse [H] float64). With no rows: o = 0, lse = -inf.
     """
     H = q_bits.shape[0]
     if rows_bits.shape[0] == 0:
         return np.zeros((H, DV)), np.full(H, -np.inf)
     q = bf16_to_f64(q_bits)
-    c = bf16_to_f64(rows_bits)
+    c = latent_values(rows_bits, latent_scale)
     z = scale * (q @ c.T)                       # [H, m] logits over all 576 dims
     zmax = z.max(axis=1, keepdims=True)
     e = np.exp(z - zmax)
@@ -181,14 +190,15 @@ def sparse_mla(q_bits: np.ndarray, rows_bits: np.ndarray, scale: float):
     return o, lse
 
 
-def sparse_mla_one(q_bits, latent: Cache, b: int, idx_row: np.ndarray, scale: float):
+def sparse_mla_one(q_bits, latent: Cache, b: int, idx_row: np.ndarray, scale: float, latent_scale: float = 1.0):
     """Sparse MLA for one query token: gather the rows named by idx_row (skipping -1)."""
     sel = np.asarray(idx_row)
     sel = sel[sel >= 0]
-    return sparse_mla(q_bits, latent.rows(b, sel), scale)
+    return sparse_mla(q_bits, latent.rows(b, sel), scale, latent_scale)
 
 
-def sparse_mla_batch(q_mla, latent: Cache, idx: np.ndarray, scale: float, idx_q_stride_is_k: bool = True):
+def sparse_mla_batch(q_mla, latent: Cache, idx: np.ndarray, scale: float, idx_q_stride_is_k: bool = True,
+                     latent_scale: float = 1.0):
     """[B, Q, H, 512] outputs and [B, Q, H] lse. idx is [B, Q, k] (one set per query token)
     or, when idx_q_stride_is_k is False, [B, 1, k] shared by all query tokens of a sequence."""
     B, Q, H = q_mla.shape[:3]
@@ -197,7 +207,7 @@ def sparse_mla_batch(q_mla, latent: Cache, idx: np.ndarray, scale: float, idx_q_
     for b in range(B):
         for j in range(Q):
             row = idx[b, j] if idx_q_stride_is_k else idx[b, 0]
-            out[b, j], lse[b, j] = sparse_mla_one(q_mla[b, j], latent, b, row, scale)
+            out[b, j], lse[b, j] = sparse_mla_one(q_mla[b, j], latent, b, row, scale, latent_scale)
     return out, lse
 
 

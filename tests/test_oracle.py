@@ -335,3 +335,27 @@ def test_page_complexity_figures(golden):
     assert oracle.attention_flops(128, 2 * k) == 2 * oracle.attention_flops(128, k)
     assert oracle.attention_flops(128, k) == 2 * 128 * 2048 * 1088
     assert oracle.indexer_flops(64, 1) == 16384
+
+
+# ----------------------------------------------------------------------------- FP8 latent rows
+def test_fp8_latent_rows_equal_bf16_rows_of_their_values():
+    """A latent cache of E4M3 codes with a power-of-two scale is a bf16 cache of the decoded
+    values: every E4M3 value times a power of two is a bf16 value (torch's casts decide), so
+    attention over the codes equals attention over those bf16 rows."""
+    g = torch.Generator().manual_seed(5)
+    codes = (torch.randn((40, 576), generator=g) * 3).to(torch.float8_e4m3fn)
+    q = torch.randn((8, 576), generator=g).to(torch.bfloat16)
+    for s in (1.0, 0.25, 8.0):
+        vals = codes.to(torch.float32) * s
+        as_bf16 = vals.to(torch.bfloat16)
+        assert torch.equal(as_bf16.to(torch.float32), vals)
+        o1, l1 = oracle.sparse_mla(bits(q), codes.view(torch.uint8).numpy(), 0.05, latent_scale=s)
+        o2, l2 = oracle.sparse_mla(bits(q), bits(as_bf16), 0.05)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), s
+
+
+def test_fp8_latent_values_follow_the_code_table():
+    codes = np.arange(256, dtype=np.uint8)
+    ok = ~np.isnan(oracle.e4m3_to_f64(codes))
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.latent_values(codes, 0.5)[ok], 0.5 * ref[ok])
