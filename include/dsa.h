@@ -114,6 +114,20 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H
                               float softmax_scale, float* out, float* lse,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Sparse MLA over an FP8 latent cache (the inference page's KV-cache precision option
+ * fp8_e4m3; "MLA + KV FP8" compression in its HiSparse section). The pages give no scale
+ * convention; here a latent row is 576 OCP E4M3FN codes (576 bytes, half a bf16 row) and one
+ * scale serves the whole cache: the value of a code c is latent_scale x e4m3(c).
+ * Everything else as dsa_sparse_mla_fwd, which it equals on the decoded values: every E4M3
+ * value is exact in bf16, so the products and sums are those of a bf16 cache holding
+ * latent_scale x e4m3(c) when latent_scale is a power of two (and differ only by the rounding
+ * of that product otherwise). latent_scale must be finite and > 0. The workspace is that of
+ * dsa_sparse_mla_fwd. */
+dsa_status dsa_sparse_mla_fwd_fp8(const dsa_batch_t* batch, const uint16_t* q, int H,
+                                  const dsa_cache_t* latent, float latent_scale, const int32_t* idx, int k,
+                                  int idx_q_stride, float softmax_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* IndexShare group ("LLM architecture survey", section 7.2 and Fig. 7-2: every 4 sparse
  * layers share one indexer whose top-k indices the following layers reuse; "GLM-5.2
  * inference deployment", MTP draft + verify: draft steps reuse the step-1 indices).

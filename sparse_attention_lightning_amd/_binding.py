@@ -18,7 +18,8 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED, OP_HISPARSE_SWAP_IN = range(5)
 
 # every symbol include/dsa.h declares
-EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared", "dsa_hisparse_swap_in",
+EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
+           "dsa_hisparse_swap_in",
            "dsa_workspace_size", "dsa_status_str", "dsa_last_error")
 
 
@@ -57,6 +58,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_index_score.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), P, P]
     lib.dsa_topk.argtypes = [C.POINTER(BatchT), P, I, P, P, S, P]
     lib.dsa_sparse_mla_fwd.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), P, I, I, F, P, P, P, S, P]
+    lib.dsa_sparse_mla_fwd_fp8.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), F, P, I, I, F, P, P, P, S, P]
     lib.dsa_forward_shared.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
     lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, P, S, P]
@@ -66,7 +68,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_status_str.restype = C.c_char_p
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = C.c_char_p
-    for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward_shared", "dsa_hisparse_swap_in"):
+    for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
+                 "dsa_hisparse_swap_in"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -158,8 +161,10 @@ def topk(scores, seq_lens, k: int, q_pos=None, idx=None, ws=None, stream=None):
 
 
 def sparse_mla_fwd(q, latent: Cache, idx, k: int, scale: float, seq_lens, L_max: int, idx_q_stride: Optional[int] = None,
-                   q_pos=None, out=None, lse=None, want_lse: bool = True, ws=None, stream=None):
-    """q [B,Q,H,576] bf16 -> (out [B,Q,H,512] float32, lse [B,Q,H] float32)."""
+                   q_pos=None, out=None, lse=None, want_lse: bool = True, ws=None, stream=None,
+                   latent_scale: Optional[float] = None):
+    """q [B,Q,H,576] bf16 -> (out [B,Q,H,512] float32, lse [B,Q,H] float32). With latent_scale
+    the latent cache holds 576 E4M3 codes per row (uint8), value = latent_scale x code."""
     import torch
     B, Q, H = q.shape[:3]
     if idx_q_stride is None:
@@ -172,8 +177,13 @@ def sparse_mla_fwd(q, latent: Cache, idx, k: int, scale: float, seq_lens, L_max:
     n = lib().dsa_workspace_size(OP_SPARSE_MLA, C.byref(bt), 64, H, k, 1)
     ws = _workspace(n, q.device, ws)
     lc = latent.c()
-    _check(lib().dsa_sparse_mla_fwd(C.byref(bt), q.data_ptr(), H, C.byref(lc), idx.data_ptr(), k, idx_q_stride,
-                                    float(scale), out.data_ptr(), _ptr(lse), _ptr(ws), n, _stream(stream)))
+    if latent_scale is None:
+        _check(lib().dsa_sparse_mla_fwd(C.byref(bt), q.data_ptr(), H, C.byref(lc), idx.data_ptr(), k, idx_q_stride,
+                                        float(scale), out.data_ptr(), _ptr(lse), _ptr(ws), n, _stream(stream)))
+    else:
+        _check(lib().dsa_sparse_mla_fwd_fp8(C.byref(bt), q.data_ptr(), H, C.byref(lc), float(latent_scale),
+                                            idx.data_ptr(), k, idx_q_stride, float(scale), out.data_ptr(), _ptr(lse),
+                                            _ptr(ws), n, _stream(stream)))
     return out, lse
 
 

@@ -175,6 +175,31 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H
                   who);
 }
 
+dsa_status dsa_sparse_mla_fwd_fp8(const dsa_batch_t* batch, const uint16_t* q, int H, const dsa_cache_t* latent,
+                                  float latent_scale, const int32_t* idx, int k, int idx_q_stride,
+                                  float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const char* who = "dsa_sparse_mla_fwd_fp8";
+  TRY(check_batch(batch, who));
+  if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
+  if (idx_q_stride != 0 && idx_q_stride != k)
+    return fail(DSA_ERR_INVALID_ARG, "%s: idx_q_stride=%d must be 0 or k=%d", who, idx_q_stride, k);
+  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  if (!std::isfinite(latent_scale) || !(latent_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "%s: latent_scale must be finite and > 0", who);
+  TRY(check_ptr(q, 16, who, "q"));
+  TRY(check_ptr(idx, 4, who, "idx"));
+  TRY(check_ptr(out, 16, who, "out"));
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse misaligned", who);
+  TRY(check_cache(latent, batch->L_max, who, "latent"));
+  TRY(check_ws(ws, ws_bytes, dsa::sparse_mla_workspace_bytes(batch->B * batch->Q, H, k, 1), who));
+  g_last_error.clear();
+  return launched(dsa::launch_sparse_mla_fp8(host_batch(batch), q, H, host_cache(latent), latent_scale, idx, k,
+                                             idx_q_stride, softmax_scale, out, lse, ws, (hipStream_t)stream),
+                  who);
+}
+
 dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
                               const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
                               const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,

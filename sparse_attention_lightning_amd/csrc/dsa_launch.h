@@ -35,6 +35,10 @@ size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers);
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out,
                              float* lse, void* ws, hipStream_t s);
+// FP8 latent rows: 576 OCP E4M3 codes per token, value = latent_scale x code (latent_scale > 0)
+hipError_t launch_sparse_mla_fp8(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
+                                 float latent_scale, const int32_t* idx, int k, int idx_q_stride, float scale,
+                                 float* out, float* lse, void* ws, hipStream_t s);
 hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
                                     const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
                                     float* const* lse, int n_layers, void* ws, hipStream_t s);

@@ -33,6 +33,14 @@ constexpr int kTok = 32;                        // tokens per step
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kSegs = kRowBytes / 128;          // 9 segments of 128 B per row
 constexpr int kTileBytes = kTok * kRowBytes;    // 36 KB per step
+// FP8 latent rows (576 E4M3 codes): a step's 32 rows land in a staging buffer, 8 rows per
+// wave in 4.5 loads of 1 KB (5 issued, the last half onto a dummy tail), and each wave turns
+// its own rows into the bf16 tile of the next step.
+constexpr int kRowBytes8 = kDqk;                // 576
+constexpr int kChunks8Wave = 8 * kRowBytes8 / 16;   // 288 chunks of 16 B per wave and step
+constexpr int kDma8 = (kChunks8Wave + 63) / 64;     // 5 loads per wave and step
+constexpr int kWaveStage8 = kDma8 * 1024;           // 5 KB per wave
+constexpr int kStageBytes8 = 4 * kWaveStage8;       // 20 KB per step
 constexpr int kStages = 3;                      // LDS ring depth: rows land kStages - 1 steps ahead
 constexpr int kFragBatch = 2;                   // LDS fragments per read batch
 constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the softmax reference
@@ -124,26 +132,11 @@ __device__ __forceinline__ void wait_counts() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
 }
 
-// Wait until this wave's direct-to-LDS loads of one step have landed while `pending` loads
-// (the next step's) may still be in flight.
-__device__ __forceinline__ void wait_step(int pending) {
-  switch (pending) {
-    case 0: wait_counts<0, 15>(); break;
-    case 4: wait_counts<4, 15>(); break;
-    case 5: wait_counts<5, 15>(); break;
-    case 8: wait_counts<8, 15>(); break;
-    case 9: wait_counts<9, 15>(); break;
-    case 10: wait_counts<10, 15>(); break;
-    case 18: wait_counts<18, 15>(); break;
-    default: wait_counts<0, 15>(); break;
-  }
-}
-
-template <int NW, int HT, bool SPLIT>
+template <int NW, int HT, bool SPLIT, bool F8>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, int Q, int H, int splits,
-    int split_len, float scale_log2, part_t* __restrict__ part_o_all, float* __restrict__ part_lse_all,
-    int64_t part_o_stride, int64_t part_lse_stride) {
+    int split_len, float scale_log2, float out_scale, part_t* __restrict__ part_o_all,
+    float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride) {
   // layer blockIdx.y of the launch: its query, latent cache, outputs and partials
   const int layer = blockIdx.y;
   const uint16_t* __restrict__ q = layers.q[layer];
@@ -162,12 +155,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   static_assert(kStages == 3, "three named ring slots");
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[F8 ? 1024 : kTileBytes];      // FP8: two slots
+  __shared__ __attribute__((aligned(1024))) uint8_t stg0[F8 ? kStageBytes8 : 1024];      // FP8 staging
+  __shared__ __attribute__((aligned(1024))) uint8_t stg1[F8 ? kStageBytes8 : 1024];
   auto ring_of = [&](auto slot) -> uint8_t* {
     constexpr int S = decltype(slot)::value;
     if constexpr (S == 0) return ring0;
     else if constexpr (S == 1) return ring1;
     else return ring2;
+  };
+  auto stg_of = [&](auto p) -> uint8_t* {
+    if constexpr (decltype(p)::value == 0) return stg0;
+    else return stg1;
   };
   __shared__ int rowid[kMaxK];
   __shared__ int redo_any;
@@ -242,6 +241,55 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   }
   __syncthreads();
 
+  // FP8 rows of step st into staging buffer p: chunk i = 64 d + lane of the wave's 288 is
+  // 16 bytes of row 8 wave + i / 36; chunks past 288 (half of the last load) and rows of
+  // masked tokens or of steps past the last read row 0 into places nothing reads.
+  auto issue_step8 = [&](int st, auto p) {
+    uint8_t* base = stg_of(p) + wave * kWaveStage8;
+    // the lane's chunk numbers are recomputed at every step rather than kept across the loop,
+    // where they would cost registers the step needs
+    const int ln = (int)opaque_u32((uint32_t)lane);
+#pragma unroll
+    for (int d = 0; d < kDma8; ++d) {
+      const int i = d * 64 + ln;
+      const int rl = i / 36, c = i - 36 * (i / 36);
+      const int r = (i < kChunks8Wave && st < n_steps) ? rowid[st * kTok + 8 * wave + rl] : -1;
+      const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes8 + 16 * c : 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + d * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // this wave's 8 FP8 rows of step st, from staging buffer p into the bf16 tile of `slot`
+  // (masked tokens become zero rows). E4M3 values are exact in bf16: a code converts to fp32,
+  // whose upper half is its bf16 pattern.
+  auto convert8 = [&](int st, auto p, auto slot) {
+    const uint8_t* sb = stg_of(p) + wave * kWaveStage8;
+    uint8_t* tile = ring_of(slot);
+    // two codes of x (bytes 0-1, or 2-3 when `upper`) as two packed bf16
+    auto two = [](uint32_t x, bool upper) -> uint32_t {
+      const float f0 = upper ? __builtin_amdgcn_cvt_f32_fp8(x, 2) : __builtin_amdgcn_cvt_f32_fp8(x, 0);
+      const float f1 = upper ? __builtin_amdgcn_cvt_f32_fp8(x, 3) : __builtin_amdgcn_cvt_f32_fp8(x, 1);
+      return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    };
+    const int ln = (int)opaque_u32((uint32_t)lane);
+#pragma unroll 1
+    for (int e = 0; e < kDma8; ++e) {                // one chunk at a time: few registers live
+      const int i = e * 64 + ln;
+      if (i < kChunks8Wave) {
+        const int rl = i / 36, c = i - 36 * (i / 36);
+        const int row = 8 * wave + rl;
+        v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+        if (rowid[st * kTok + row] >= 0) {
+          const v4i x = *(const v4i*)(sb + 16 * i);      // dims 16c .. 16c + 15
+          lo = (v4i){(int)two(x[0], false), (int)two(x[0], true), (int)two(x[1], false), (int)two(x[1], true)};
+          hi = (v4i){(int)two(x[2], false), (int)two(x[2], true), (int)two(x[3], false), (int)two(x[3], true)};
+        }
+        *(v4i*)(tile + tile_off(row, 2 * c)) = lo;
+        *(v4i*)(tile + tile_off(row, 2 * c + 1)) = hi;
+      }
+    }
+  };
+
   // masked rows this wave landed: overwrite the dummy bytes with zeros
   auto zero_masked = [&](int st, auto slot) {
     if (rowid[st * kTok + my_row] >= 0) return;
@@ -288,19 +336,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     constexpr int kAheadSteps = kStages - 1;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    issue_step(0, I0{});
-    issue_step(1, I1{});
-    // step st in ring slot S = st % 3
-    auto step_body = [&](int st, auto slot) {
-      constexpr int S = decltype(slot)::value;
-      static_assert(kAheadSteps == 2, "one step of loads in flight behind the current one");
-      wait_counts<my_dma, 15>();                       // this step's rows have landed
-      zero_masked(st, slot);
-      wait_counts<63, 0>();                            // LDS writes done before the barrier
-      __builtin_amdgcn_s_barrier();
-      // into step st - 1's slot, which every wave has finished reading
-      issue_step(st + kAheadSteps, std::integral_constant<int, (S + kAheadSteps) % kStages>{});
-      const uint8_t* tile = ring_of(slot);
+    // QK, softmax and PV of step st on a landed bf16 tile
+    auto compute = [&](int st, const uint8_t* tile) {
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
       const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
@@ -424,11 +461,52 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         }
       }
     };
-    // unrolled by the three ring slots, so that every step names its slots statically
-    for (int st = 0; st < n_steps; st += kStages) {
-      step_body(st, I0{});
-      if (st + 1 < n_steps) step_body(st + 1, I1{});
-      if (st + 2 < n_steps) step_body(st + 2, std::integral_constant<int, 2>{});
+    if constexpr (!F8) {
+      issue_step(0, I0{});
+      issue_step(1, I1{});
+      // step st in ring slot S = st % 3
+      auto step_body = [&](int st, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        static_assert(kAheadSteps == 2, "one step of loads in flight behind the current one");
+        wait_counts<my_dma, 15>();                     // this step's rows have landed
+        zero_masked(st, slot);
+        wait_counts<63, 0>();                          // LDS writes done before the barrier
+        __builtin_amdgcn_s_barrier();
+        // into step st - 1's slot, which every wave has finished reading
+        issue_step(st + kAheadSteps, std::integral_constant<int, (S + kAheadSteps) % kStages>{});
+        compute(st, ring_of(slot));
+      };
+      // unrolled by the three ring slots, so that every step names its slots statically
+      for (int st = 0; st < n_steps; st += kStages) {
+        step_body(st, I0{});
+        if (st + 1 < n_steps) step_body(st + 1, I1{});
+        if (st + 2 < n_steps) step_body(st + 2, std::integral_constant<int, 2>{});
+      }
+    } else {
+      // FP8: loads two steps ahead into two staging buffers; each wave converts its rows of step
+      // st + 1 into the other bf16 slot while step st computes, so two bf16 slots suffice.
+      issue_step8(0, I0{});
+      issue_step8(1, I1{});
+      wait_counts<kDma8, 15>();                        // step 0's rows (this wave's) have landed
+      convert8(0, I0{}, I0{});
+      auto step8 = [&](int st, auto p) {               // p = st % 2: staging and bf16 slot of st
+        constexpr int P = decltype(p)::value;
+        using Pn = std::integral_constant<int, 1 - P>;
+        wait_counts<63, 0>();                          // conversion writes done before the barrier
+        __builtin_amdgcn_s_barrier();
+        // staging p held step st, which this wave converted a step ago; bf16 slot 1 - p held step
+        // st - 1, which every wave has finished reading
+        issue_step8(st + 2, p);
+        if (st + 1 < n_steps) {                        // workgroup-uniform
+          wait_counts<kDma8, 15>();                    // step st + 1's rows have landed
+          convert8(st + 1, Pn{}, Pn{});
+        }
+        compute(st, ring_of(p));
+      };
+      for (int st = 0; st < n_steps; st += 2) {
+        step8(st, I0{});
+        if (st + 1 < n_steps) step8(st + 1, I1{});
+      }
     }
     wait_counts<0, 15>();                              // the loads past the last step have landed
     if (pass == 0) {
@@ -447,6 +525,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     for (int r = 0; r < 4; ++r) {
       const float lr = __shfl(l_tot, 4 * g + r, 64);
       inv[r] = lr > 0.f ? 1.f / lr : 0.f;
+      if constexpr (F8) inv[r] *= out_scale;         // the FP8 cache's scale on the values
     }
     const int hb = h0 + 16 * ht;
     if (SPLIT) {
@@ -511,31 +590,34 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
   if (t == 0 && lse_out) lse_out[(int64_t)bq * H + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(den);
 }
 
-template <int NW, int HT>
+template <int NW, int HT, bool F8>
 static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L, const int32_t* idx, int k,
-                       int idx_q_stride, int Q, int H, int split_len, float sl2, part_t* part_o, float* part_lse,
-                       int64_t so, int64_t sl) {
+                       int idx_q_stride, int Q, int H, int split_len, float sl2, float out_scale, part_t* part_o,
+                       float* part_lse, int64_t so, int64_t sl) {
   const dim3 block(NW * 64);
   if (splits == 1)
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
-                       split_len, sl2, nullptr, nullptr, (int64_t)0, (int64_t)0);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
+                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, splits,
-                       split_len, sl2, part_o, part_lse, so, sl);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H,
+                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl);
 }
 
-hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
-                                    const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
-                                    float* const* lse, int n_layers, void* ws, hipStream_t s) {
+// latent_scale > 0: FP8 latent rows (576 E4M3 codes, value = latent_scale x code); 0: bf16 rows
+static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                float latent_scale, const int32_t* idx, int k, int idx_q_stride, float scale,
+                                float* const* out, float* const* lse, int n_layers, void* ws, hipStream_t s) {
   const int rows = bt.B * bt.Q;
-  const float sl2 = scale * kLog2e;
+  const bool f8 = latent_scale > 0.f;
+  const float sl2 = scale * (f8 ? latent_scale : 1.f) * kLog2e;
   for (int l0 = 0; l0 < n_layers; l0 += kMlaMaxLayers) {
     const int nl = std::min(kMlaMaxLayers, n_layers - l0);
     MlaLayers L{};
     for (int i = 0; i < nl; ++i) {
       const HostCache& c = latents[l0 + i];
       L.q[i] = q[l0 + i];
-      L.lat[i] = CacheView{(const uint8_t*)c.base, c.table, c.max_pages, c.page_size, kRowBytes, bt.L_max};
+      L.lat[i] = CacheView{(const uint8_t*)c.base, c.table, c.max_pages, c.page_size, f8 ? kRowBytes8 : kRowBytes,
+                           bt.L_max};
       L.out[i] = out[l0 + i];
       L.lse[i] = lse ? lse[l0 + i] : nullptr;
     }
@@ -554,10 +636,18 @@ hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* 
     }
     const dim3 grid((unsigned)(rows * splits), (unsigned)nl);
     // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64)
-    if (H == 128)
-      launch_mla<4, 2>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, part_o, part_lse, so, sl);
+    if (f8 && H == 128)
+      launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, latent_scale, part_o,
+                             part_lse, so, sl);
+    else if (f8)
+      launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, latent_scale, part_o,
+                             part_lse, so, sl);
+    else if (H == 128)
+      launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, 1.f, part_o,
+                              part_lse, so, sl);
     else
-      launch_mla<4, 1>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, part_o, part_lse, so, sl);
+      launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, 1.f, part_o,
+                              part_lse, so, sl);
     if (splits > 1)
       hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2), (unsigned)nl), dim3(256), 0, s, L,
                          part_o, part_lse, H, splits, so, sl);
@@ -567,12 +657,25 @@ hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* 
   return hipSuccess;
 }
 
+hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                    const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
+                                    float* const* lse, int n_layers, void* ws, hipStream_t s) {
+  return launch_layers(bt, q, H, latents, 0.f, idx, k, idx_q_stride, scale, out, lse, n_layers, ws, s);
+}
+
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out, float* lse,
                              void* ws, hipStream_t s) {
   float* lse_arr[1] = {lse};
-  return launch_sparse_mla_layers(bt, &q, H, &latent, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr, 1,
-                                  ws, s);
+  return launch_layers(bt, &q, H, &latent, 0.f, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr, 1, ws, s);
+}
+
+hipError_t launch_sparse_mla_fp8(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
+                                 float latent_scale, const int32_t* idx, int k, int idx_q_stride, float scale,
+                                 float* out, float* lse, void* ws, hipStream_t s) {
+  float* lse_arr[1] = {lse};
+  return launch_layers(bt, &q, H, &latent, latent_scale, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr,
+                       1, ws, s);
 }
 
 }  // namespace dsa

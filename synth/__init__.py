@@ -62,6 +62,7 @@ class Workload:
     n_slots: int = 0                     # > 0: latent pages live in host memory, n_slots device slots per sequence
     drift_heads: int = 0                 # indexer query heads redrawn from one decode step to the next
     draft_steps: int = 0                 # > 0: an MTP draft loop of this many sequential steps per index set
+    latent_fp8: int = 0                  # 1: latent rows as 576 E4M3FN codes (uint8) instead of bf16
 
     @property
     def lmax(self) -> int:
@@ -98,6 +99,10 @@ WORKLOADS = {
     # MTP draft loop (GLM-5.2 inference page, MTP section): one MTP layer unrolled 7 times;
     # KVShare: every draft step reads the main model's cache; IndexShare on MTP: the top-2048
     # set is computed at step 1 and reused by the next 6 steps. Decode shape of the 128K batch.
+    # The default decode batch over an FP8 latent cache (the inference page's fp8_e4m3 KV option):
+    # rows of 576 E4M3FN(N(0,1)) codes, scale 1.
+    "decode_b32_128k_paged_fp8kv": Workload("decode_b32_128k_paged_fp8kv", B=32, Q=1, L=131072, page_size=64,
+                                            planted=32, latent_fp8=1),
     "mtp_draft_b32_128k_paged": Workload("mtp_draft_b32_128k_paged", B=32, Q=1, L=131072, page_size=64,
                                          planted=32, draft_steps=7),
 }
@@ -205,7 +210,10 @@ def generate(wl: Workload, seed: int = 0, device="cpu", layers: Optional[int] = 
         for layer in range(n_layers):
             s = seed + layer
             batch.q_mla.append(bf16_normal((wl.B, wl.Q, wl.H, DQK), _gen(s, S_QMLA, layer, dev), dev))
-            batch.latent.append(bf16_normal(cache_shape(wl, DQK), _gen(s, S_LATENT, layer, dev), dev))
+            if wl.latent_fp8:
+                batch.latent.append(e4m3_normal(cache_shape(wl, DQK), _gen(s, S_LATENT, layer, dev), dev))
+            else:
+                batch.latent.append(bf16_normal(cache_shape(wl, DQK), _gen(s, S_LATENT, layer, dev), dev))
             if wl.page_size:
                 batch.latent_table.append(key_table if layer == 0 else block_table(wl, s, layer, dev))
             else:

@@ -50,9 +50,12 @@ def key_cache(batch):
 
 
 def latent_cache(batch, layer=0):
+    """The oracle's view of a latent cache: bf16 bits, or E4M3 codes for an FP8 cache."""
     wl = batch.wl
     tab = batch.latent_table[layer]
-    return OCache(bits(batch.latent[layer]), None if tab is None else np_(tab), wl.page_size)
+    lat = batch.latent[layer]
+    data = np_(lat) if lat.dtype == torch.uint8 else bits(lat)
+    return OCache(data, None if tab is None else np_(tab), wl.page_size)
 
 
 def score_tolerance(q_codes, w, key_rows_codes, integer_inputs=False):

@@ -17,7 +17,7 @@ A = 1 << 20          # a fake, well-aligned "device address": never dereferenced
 def header_functions():
     text = open(os.path.join(ROOT, "include", "dsa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():

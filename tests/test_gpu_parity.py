@@ -364,3 +364,41 @@ def test_mtp_draft_loop_reuses_the_step1_set():
         ref_o, ref_l = oracle.sparse_mla_batch(bits(q), latent_cache(cpu), np_(idx), wl.scale)
         for b in range(wl.B):
             check_mla(np_(out)[b, 0], np_(lse)[b, 0], ref_o[b, 0], ref_l[b, 0])
+
+
+# ----------------------------------------------------------------------------- FP8 latent cache
+@pytest.mark.parametrize("name,kw,scale", [
+    ("decode_b32_128k_paged", dict(B=2, L=5000, L_max=5056, planted=4, seq_lens=(5000, 3001)), 1.0),       # split, paged
+    ("decode_tiny_8k", dict(B=2, L=3000, seq_lens=(3000, 1500), H=64), 0.37),                              # contiguous, H=64
+    ("verify_b64_q8_32k", dict(B=2, L=3000, L_max=3008, k=300), 0.5),                                      # many rows, no split
+])
+def test_sparse_mla_fp8_latent_on_oracle_indices(name, kw, scale):
+    """The absolute bar (2e-2) is for values of the workloads' size: scales stay at or below 1."""
+    wl = synth.small(name, latent_fp8=1, **kw)
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl)
+    idx_g = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                  latent_scale=scale)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), idx, wl.scale, latent_scale=scale)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
+
+
+@pytest.mark.parametrize("H", [128, 64])
+def test_sparse_mla_fp8_latent_equals_bf16_cache_of_its_values(H):
+    """With a power-of-two scale the FP8 path gives the bits of the bf16 path over a bf16 cache
+    holding the decoded values (same products, same order)."""
+    wl = synth.small("decode_b32_128k_paged", B=2, L=4000, L_max=4032, planted=4, seq_lens=(4000, 2222), H=H,
+                     latent_fp8=1)
+    cpu, g = gpu_batch(wl)
+    scores = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax)
+    idx = dsa.topk(scores, g.seq_lens, wl.k)
+    as_bf16 = (g.latent[0].view(torch.float8_e4m3fn).to(torch.float32) * 4.0).to(torch.bfloat16)
+    o8, l8 = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx, wl.k, wl.scale, g.seq_lens, wl.lmax, latent_scale=4.0)
+    ob, lb = dsa.sparse_mla_fwd(g.q_mla[0], dsa_cache(as_bf16, g.latent_table[0], wl.page_size), idx, wl.k, wl.scale,
+                                g.seq_lens, wl.lmax)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, ob) and torch.equal(l8, lb)
