@@ -59,7 +59,8 @@ def mla_work(wl):
     """Algorithmic bytes and FLOPs of one sparse-MLA launch (rows gathered once per query token)."""
     rows = wl.B * wl.Q
     sel = sum(min(wl.k, n - wl.Q + j + 1) for n in wl.lens for j in range(wl.Q))
-    byts = sel * 1152 + rows * wl.H * (576 * 2 + 512 * 4 + 4) + rows * wl.k * 4
+    row_bytes = 576 if wl.latent_fp8 else 1152          # E4M3 codes or bf16 per latent row
+    byts = sel * row_bytes + rows * wl.H * (576 * 2 + 512 * 4 + 4) + rows * wl.k * 4
     flops = sel * wl.H * 2 * (576 + 512)
     return byts, flops
 
@@ -105,7 +106,8 @@ def cpu_baseline(batches, wl, budget_s):
                 return data[b:b + 1].cpu().numpy()
             return data[table[b].long()].reshape(1, -1, data.shape[-1]).cpu().numpy()
         keys = oracle.Cache(seq_rows(g.keys, g.key_table))
-        lats = [oracle.Cache(seq_rows(g.latent[l], g.latent_table[l]).view(np.uint16)) for l in range(len(g.latent))]
+        lats = [oracle.Cache(r.view(np.uint16) if r.dtype == np.int16 else r)
+                for r in (seq_rows(g.latent[l], g.latent_table[l]) for l in range(len(g.latent)))]
         q_idx = g.q_idx[b].cpu().numpy()
         w = g.w[b].cpu().numpy()
         q_src = synth.draft_queries(g, wl.draft_steps) if wl.draft_steps else g.q_mla
@@ -120,7 +122,7 @@ def cpu_baseline(batches, wl, budget_s):
             users = range(wl.Q) if wl.share_first_query else [j]
             for c in range(len(q_mla)):          # every layer, or every draft step of an MTP loop
                 for u in users:
-                    oracle.sparse_mla_one(q_mla[c][u], lat_of(c), 0, idx, wl.scale)
+                    oracle.sparse_mla_one(q_mla[c][u], lat_of(c), 0, idx, wl.scale, latent_scale=1.0)
         elapsed += time.perf_counter() - t0
         done_tokens += (wl.Q if wl.share_first_query else rows_per_seq) * max(1, wl.draft_steps)
         seqs += 1
@@ -263,7 +265,8 @@ def main():
         for c, (q_mla, lat) in enumerate(pr["mla_calls"]):
             dsa.sparse_mla_fwd(q_mla, hot_lat if hot else lat, idx,
                                wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0 if wl.share_first_query else wl.k,
-                               out=outs[c], lse=lses[c], ws=ws_mla if n_mla else None, stream=stream)
+                               out=outs[c], lse=lses[c], ws=ws_mla if n_mla else None, stream=stream,
+                               latent_scale=1.0 if wl.latent_fp8 else None)
         if record == "all":
             e[3].record(stream)
             ev["topk"].append((e[1], e[2]))
@@ -319,7 +322,7 @@ def main():
         "vs_baseline": None, "dtype": "fp8e4m3+bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "L": wl.L, "page_size": wl.page_size, "k": wl.k,
                    "Hi": wl.Hi, "H": wl.H, "n_layers": wl.n_layers, "share_first_query": wl.share_first_query,
-                   "draft_steps": wl.draft_steps, "hot_buffer_slots": wl.n_slots,
+                   "draft_steps": wl.draft_steps, "hot_buffer_slots": wl.n_slots, "latent_fp8": wl.latent_fp8,
                    "planted": wl.planted},
         "roofline": roof,
         "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"],
