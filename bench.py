@@ -187,7 +187,7 @@ def main():
             slot_page=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=dev),
             slot_clock=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=dev),
             page_clock=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=dev),
-            device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=torch.bfloat16, device=dev),
+            device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=host_pool.dtype, device=dev),
             page_size=wl.page_size)
         hot_lat = hb.latent_cache()
         drift = synth.drift_queries(g0, n_all_steps)
@@ -338,7 +338,7 @@ def main():
     if hot:
         # pages pulled from host memory per timed step (the queries drift, so each step misses a part)
         per_step = copied[args.warmup:args.warmup + args.steps].sum(dim=1).float().mean().item()
-        page_bytes = wl.page_size * 576 * 2
+        page_bytes = wl.page_size * 576 * host_pool.element_size()
         line["kernels_us"]["hisparse_swap_in"] = avg["swap"]
         line["kernels_us"]["note"] += "; hisparse_swap_in: events around the swap-in in the same 3 steps"
         line["hot_buffer"] = {

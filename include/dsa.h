@@ -166,16 +166,18 @@ typedef struct {
   int32_t max_pages;           /* (host) logical pages per sequence                          */
   int32_t n_slots;             /* (host) device slots per sequence                           */
   int32_t page_size;           /* (host) tokens per page (= per slot), a positive multiple of 16 */
+  int32_t row_bytes;           /* (host) bytes per token row in both pools: 1152 (bf16 latent rows)
+                                  or 576 (E4M3 rows, for dsa_sparse_mla_fwd_fp8)               */
 } dsa_hot_buffer_t;
 
 /* One swap-in step, after dsa_topk of the step (page's three steps: top-K miss detection, LRU
  * eviction, page-table update with an asynchronous host-to-device pull).
  *   idx          [B][n_sets][k] int32 selected positions as dsa_topk writes them (-1 skipped)
  *   step         >= 0, larger than the step of every earlier call on the same state
- *   host_pool    [B][max_pages][page_size][576] bf16, every page of every sequence: pinned host
+ *   host_pool    [B][max_pages][page_size][row_bytes], every page of every sequence: pinned host
  *                memory mapped for the device (hipHostMalloc, torch pin_memory), or device
  *                memory. Checked with hipPointerGetAttributes: DSA_ERR_INVALID_ARG otherwise.
- *   device_pool  [B*n_slots][page_size][576] bf16 device memory
+ *   device_pool  [B*n_slots][page_size][row_bytes] device memory
  *   copied       device [B] int32: pages copied for each sequence in this step, or NULL
  * Afterwards every page holding a selected position is resident. Hits refresh their slot's
  * clock. The missing pages evict as many of the slots this step does not use, least recently
@@ -187,7 +189,7 @@ typedef struct {
  * miss list. ws: dsa_workspace_size(DSA_OP_HISPARSE_SWAP_IN, batch with B, Q = n_sets and any
  * L_max >= 1, 0, 0, k, 0) bytes, 256-byte aligned. */
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
-                                const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
+                                const dsa_hot_buffer_t* hb, const void* host_pool, void* device_pool,
                                 int32_t* copied, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace sizes, from host fields of `batch` only (B, Q, L_max). */

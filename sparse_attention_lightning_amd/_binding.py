@@ -36,7 +36,7 @@ class BatchT(C.Structure):
 class HotBufferT(C.Structure):
     _fields_ = [("block_table", C.c_void_p), ("slot_page", C.c_void_p), ("slot_clock", C.c_void_p),
                 ("page_clock", C.c_void_p), ("max_pages", C.c_int32), ("n_slots", C.c_int32),
-                ("page_size", C.c_int32)]
+                ("page_size", C.c_int32), ("row_bytes", C.c_int32)]
 
 
 class DsaError(RuntimeError):
@@ -222,7 +222,8 @@ class HotBuffer:
     """HiSparse hot buffer of B sequences: device slots of one page each over a latent cache
     kept whole in host memory. Every state tensor is int32 on the device, -1 before the first
     step: block_table [B, max_pages], slot_page [B, n_slots], slot_clock [B, n_slots],
-    page_clock [B, max_pages]. device_pool [B * n_slots, page_size, 576] bf16."""
+    page_clock [B, max_pages]. device_pool [B * n_slots, page_size, 576]: bf16 rows, or uint8
+    E4M3 rows (for sparse_mla_fwd with latent_scale)."""
     block_table: "object"
     slot_page: "object"
     slot_clock: "object"
@@ -233,7 +234,7 @@ class HotBuffer:
     def c(self) -> HotBufferT:
         return HotBufferT(self.block_table.data_ptr(), self.slot_page.data_ptr(), self.slot_clock.data_ptr(),
                           self.page_clock.data_ptr(), self.block_table.shape[1], self.slot_page.shape[1],
-                          self.page_size)
+                          self.page_size, 576 * self.device_pool.element_size())
 
     def latent_cache(self) -> Cache:
         """The latent cache that sparse MLA reads once the step's pages are resident."""
@@ -241,9 +242,12 @@ class HotBuffer:
 
 
 def hisparse_swap_in(idx, step: int, hb: HotBuffer, host_pool, copied=None, ws=None, stream=None):
-    """idx [B, n_sets, k] int32 from topk; host_pool [B, max_pages, page_size, 576] bf16 pinned;
+    """idx [B, n_sets, k] int32 from topk; host_pool [B, max_pages, page_size, 576] pinned, the
+    device pool's dtype (bf16, or uint8 E4M3 codes);
     copied: optional device [B] int32 that receives the pages copied per sequence."""
     B, n_sets, k = idx.shape
+    if host_pool.element_size() != hb.device_pool.element_size():
+        raise ValueError("host_pool and device_pool must hold rows of the same type")
     bt = BatchT(B, n_sets, 1, None, None)
     n = lib().dsa_workspace_size(OP_HISPARSE_SWAP_IN, C.byref(bt), 0, 0, k, 0)
     ws = _workspace(n, idx.device, ws)

@@ -259,7 +259,7 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
 }
 
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
-                                const dsa_hot_buffer_t* hb, const uint16_t* host_pool, uint16_t* device_pool,
+                                const dsa_hot_buffer_t* hb, const void* host_pool, void* device_pool,
                                 int32_t* copied, void* ws, size_t ws_bytes, void* stream) {
   const char* who = "dsa_hisparse_swap_in";
   if (B < 1 || n_sets < 1) return fail(DSA_ERR_INVALID_ARG, "%s: B=%d n_sets=%d must be >= 1", who, B, n_sets);
@@ -273,6 +273,8 @@ dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, i
   TRY(check_ptr(hb->page_clock, 4, who, "page_clock"));
   if (hb->page_size < 16 || hb->page_size % 16)
     return fail(DSA_ERR_UNSUPPORTED, "%s: page_size=%d must be a positive multiple of 16", who, hb->page_size);
+  if (hb->row_bytes != 2 * 576 && hb->row_bytes != 576)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: row_bytes=%d (supported: 1152, 576)", who, hb->row_bytes);
   if (hb->max_pages < 1 || hb->n_slots < 1)
     return fail(DSA_ERR_INVALID_ARG, "%s: max_pages=%d n_slots=%d must be >= 1", who, hb->max_pages, hb->n_slots);
   if ((int64_t)n_sets * k > hb->n_slots)
@@ -291,16 +293,16 @@ dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, i
     (void)hipGetLastError();
     return fail(DSA_ERR_INVALID_ARG, "%s: host_pool is neither pinned host memory nor device memory", who);
   }
-  const uint16_t* pool_dev = nullptr;
+  const void* pool_dev = nullptr;
   if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.hostPointer)
-    pool_dev = (const uint16_t*)((const char*)attr.devicePointer + ((const char*)host_pool - (const char*)attr.hostPointer));
+    pool_dev = (const char*)attr.devicePointer + ((const char*)host_pool - (const char*)attr.hostPointer);
   else if (attr.type == hipMemoryTypeDevice)
     pool_dev = host_pool;
   if (!pool_dev)
     return fail(DSA_ERR_INVALID_ARG, "%s: host_pool is neither pinned, device-mapped host memory nor device memory", who);
   g_last_error.clear();
   const dsa::HostHotBuffer h{hb->block_table, hb->slot_page, hb->slot_clock, hb->page_clock,
-                             hb->max_pages, hb->n_slots, hb->page_size};
+                             hb->max_pages, hb->n_slots, hb->page_size, hb->row_bytes};
   return launched(dsa::launch_hisparse_swap_in(B, idx, n_sets, k, step, h, pool_dev, device_pool, copied, ws,
                                                (hipStream_t)stream),
                   who);

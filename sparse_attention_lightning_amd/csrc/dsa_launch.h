@@ -50,11 +50,11 @@ struct HostHotBuffer {
   int32_t* slot_page;
   int32_t* slot_clock;
   int32_t* page_clock;
-  int max_pages, n_slots, page_size;
+  int max_pages, n_slots, page_size, row_bytes;
 };
 size_t hisparse_workspace_bytes(int B, int cap);
 hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k, int32_t step, const HostHotBuffer& hb,
-                                   const uint16_t* host_pool, uint16_t* device_pool, int32_t* copied, void* ws,
+                                   const void* host_pool, void* device_pool, int32_t* copied, void* ws,
                                    hipStream_t s);
 
 }  // namespace dsa

@@ -221,19 +221,20 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   }
 }
 
-__global__ __launch_bounds__(kCopyThreads) void hs_copy_kernel(const uint16_t* __restrict__ host_pool,
-                                                             uint16_t* __restrict__ device_pool, int cap,
+__global__ __launch_bounds__(kCopyThreads) void hs_copy_kernel(const uint8_t* __restrict__ host_pool,
+                                                             uint8_t* __restrict__ device_pool, int cap,
                                                              const int32_t* __restrict__ miss_page,
                                                              const int32_t* __restrict__ victim,
                                                              const int32_t* __restrict__ n_copy, int max_pages,
-                                                             int n_slots, int page_size) {
+                                                             int n_slots, int page_size, int row_bytes) {
   const int b = blockIdx.x / cap, i = blockIdx.x - b * cap;
   if (i >= n_copy[b]) return;
   const int p = miss_page[(int64_t)b * cap + i], s = victim[(int64_t)b * cap + i];
   if (p < 0 || p >= max_pages || s < 0 || s >= n_slots) return;   // written by the plan; never so
-  const int64_t chunks = (int64_t)page_size * kDqk / 8;          // 16-byte chunks per page
-  const v4i* src = (const v4i*)(host_pool + ((int64_t)b * max_pages + p) * page_size * kDqk);
-  v4i* dst = (v4i*)(device_pool + ((int64_t)b * n_slots + s) * page_size * kDqk);
+  const int64_t page_bytes = (int64_t)page_size * row_bytes;
+  const int64_t chunks = page_bytes / 16;                          // 16-byte chunks per page
+  const v4i* src = (const v4i*)(host_pool + ((int64_t)b * max_pages + p) * page_bytes);
+  v4i* dst = (v4i*)(device_pool + ((int64_t)b * n_slots + s) * page_bytes);
   for (int64_t c = threadIdx.x; c < chunks; c += kCopyThreads) dst[c] = src[c];
 }
 
@@ -245,7 +246,7 @@ size_t hisparse_workspace_bytes(int B, int cap) {
 }
 
 hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k, int32_t step, const HostHotBuffer& hb,
-                                   const uint16_t* host_pool, uint16_t* device_pool, int32_t* copied, void* ws,
+                                   const void* host_pool, void* device_pool, int32_t* copied, void* ws,
                                    hipStream_t s) {
   const int cap = n_sets * k;
   const size_t list = ((size_t)B * cap * sizeof(int32_t) + 255) & ~(size_t)255;
@@ -257,8 +258,9 @@ hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k,
                      step, hb.block_table, hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, hb.page_size);
   hipLaunchKernelGGL(hs::hs_plan_kernel, dim3(B), dim3(hs::kPlanThreads), 0, s, step, hb.block_table, hb.slot_page,
                      hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, cap, miss_page, victim, n_copy, copied);
-  hipLaunchKernelGGL(hs::hs_copy_kernel, dim3((unsigned)(B * cap)), dim3(hs::kCopyThreads), 0, s, host_pool, device_pool,
-                     cap, miss_page, victim, n_copy, hb.max_pages, hb.n_slots, hb.page_size);
+  hipLaunchKernelGGL(hs::hs_copy_kernel, dim3((unsigned)(B * cap)), dim3(hs::kCopyThreads), 0, s,
+                     (const uint8_t*)host_pool, (uint8_t*)device_pool, cap, miss_page, victim, n_copy, hb.max_pages,
+                     hb.n_slots, hb.page_size, hb.row_bytes);
   return hipGetLastError();
 }
 

@@ -96,6 +96,9 @@ WORKLOADS = {
     # Consecutive decode steps redraw 4 of the 64 indexer query heads.
     "hisparse_b8_1m_decode": Workload("hisparse_b8_1m_decode", B=8, Q=1, L=1048576, page_size=16,
                                       n_slots=6144, drift_heads=4),
+    # The same with E4M3 latent rows in both pools: half the bytes over the host link per page.
+    "hisparse_b8_1m_decode_fp8kv": Workload("hisparse_b8_1m_decode_fp8kv", B=8, Q=1, L=1048576, page_size=16,
+                                            n_slots=6144, drift_heads=4, latent_fp8=1),
     # MTP draft loop (GLM-5.2 inference page, MTP section): one MTP layer unrolled 7 times;
     # KVShare: every draft step reads the main model's cache; IndexShare on MTP: the top-2048
     # set is computed at step 1 and reused by the next 6 steps. Decode shape of the 128K batch.

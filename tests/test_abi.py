@@ -152,9 +152,9 @@ def test_workspace_sizes_scale_with_batch():
 
 
 # ----------------------------------------------------------------------------- HiSparse swap-in
-def hot(table=A, slot_page=A, slot_clock=A, page_clock=A, max_pages=64, n_slots=4096, page=16):
+def hot(table=A, slot_page=A, slot_clock=A, page_clock=A, max_pages=64, n_slots=4096, page=16, row_bytes=1152):
     from sparse_attention_lightning_amd._binding import HotBufferT
-    return HotBufferT(table, slot_page, slot_clock, page_clock, max_pages, n_slots, page)
+    return HotBufferT(table, slot_page, slot_clock, page_clock, max_pages, n_slots, page, row_bytes)
 
 
 def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A, copied=None, ws=A, ws_bytes=1 << 30):
@@ -180,6 +180,8 @@ def call_swap(B=2, idx=A, n_sets=1, k=2048, step=0, hb="default", host=A, dev=A,
     (dict(hb=hot(page=8)), UNSUPPORTED),
     (dict(hb=hot(page=24)), UNSUPPORTED),
     (dict(hb=hot(max_pages=0)), INVALID),
+    (dict(hb=hot(row_bytes=1024)), UNSUPPORTED),
+    (dict(hb=hot(row_bytes=0)), UNSUPPORTED),
     (dict(hb=hot(n_slots=2047)), UNSUPPORTED),             # one step's selected set must fit
     (dict(n_sets=3, hb=hot(n_slots=6143)), UNSUPPORTED),
     (dict(dev=None), INVALID),

@@ -17,9 +17,13 @@ DEV = "cuda"
 D = 576
 
 
-def make(B, max_pages, n_slots, ps, seed, pinned=True):
+def make(B, max_pages, n_slots, ps, seed, pinned=True, fp8=False):
+    """Pools of bf16 rows (int16 bit patterns), or of E4M3 rows (uint8 codes) when fp8."""
     g = torch.Generator().manual_seed(seed)
-    host = torch.randint(-32768, 32767, (B, max_pages, ps, D), dtype=torch.int16, generator=g)
+    if fp8:
+        host = torch.randint(0, 256, (B, max_pages, ps, D), dtype=torch.uint8, generator=g)
+    else:
+        host = torch.randint(-32768, 32767, (B, max_pages, ps, D), dtype=torch.int16, generator=g)
     if pinned:
         host = host.pin_memory()
     else:
@@ -28,9 +32,9 @@ def make(B, max_pages, n_slots, ps, seed, pinned=True):
                        slot_page=torch.full((B, n_slots), -1, dtype=torch.int32, device=DEV),
                        slot_clock=torch.full((B, n_slots), -1, dtype=torch.int32, device=DEV),
                        page_clock=torch.full((B, max_pages), -1, dtype=torch.int32, device=DEV),
-                       device_pool=torch.zeros((B * n_slots, ps, D), dtype=torch.int16, device=DEV), page_size=ps)
+                       device_pool=torch.zeros((B * n_slots, ps, D), dtype=host.dtype, device=DEV), page_size=ps)
     st = HotBufferState.empty(B, max_pages, n_slots)
-    dev_np = np.zeros((B * n_slots, ps, D), dtype=np.int16)
+    dev_np = np.zeros((B * n_slots, ps, D), dtype=np.uint8 if fp8 else np.int16)
     return host, hb, st, dev_np
 
 
@@ -59,14 +63,16 @@ def random_sets(rng, B, n_sets, k, L, n_valid, prev=None, keep=0.0):
     return idx
 
 
-@pytest.mark.parametrize("B,n_sets,k,ps,max_pages,n_slots,steps,keep", [
-    (3, 1, 40, 16, 64, 48, 10, 0.5),       # pressure: 40 selected tokens on 48 slots
-    (2, 2, 24, 16, 50, 48, 8, 0.7),        # two index sets per sequence, exactly full buffer
-    (2, 1, 300, 32, 80, 320, 6, 0.8),      # pages of 32 tokens, several tokens per page
-    (1, 1, 2048, 16, 1024, 2048, 4, 0.9),  # one decode row at k = 2048 on the smallest legal buffer
+@pytest.mark.parametrize("B,n_sets,k,ps,max_pages,n_slots,steps,keep,fp8", [
+    (3, 1, 40, 16, 64, 48, 10, 0.5, False),       # pressure: 40 selected tokens on 48 slots
+    (2, 2, 24, 16, 50, 48, 8, 0.7, False),        # two index sets per sequence, exactly full buffer
+    (2, 1, 300, 32, 80, 320, 6, 0.8, False),      # pages of 32 tokens, several tokens per page
+    (1, 1, 2048, 16, 1024, 2048, 4, 0.9, False),  # one decode row at k = 2048 on the smallest legal buffer
+    (3, 1, 40, 16, 64, 48, 10, 0.5, True),        # E4M3 rows (576 bytes): the pressure case
+    (2, 1, 300, 48, 80, 320, 6, 0.8, True),       # E4M3 rows, pages of 48 tokens
 ])
-def test_swap_in_matches_oracle(B, n_sets, k, ps, max_pages, n_slots, steps, keep):
-    host, hb, st, dev_np = make(B, max_pages, n_slots, ps, seed=k)
+def test_swap_in_matches_oracle(B, n_sets, k, ps, max_pages, n_slots, steps, keep, fp8):
+    host, hb, st, dev_np = make(B, max_pages, n_slots, ps, seed=k, fp8=fp8)
     host_np = host.numpy()
     rng = np.random.default_rng(k + B)
     L = max_pages * ps
@@ -112,6 +118,13 @@ def test_host_pool_in_device_memory():
         compare(hb, st, dev_np, step)
 
 
+def test_pool_types_must_match():
+    _, hb, _, _ = make(1, 8, 16, 16, seed=1)
+    host8 = torch.zeros((1, 8, 16, D), dtype=torch.uint8).pin_memory()
+    with pytest.raises(ValueError):
+        dsa.hisparse_swap_in(torch.zeros((1, 1, 4), dtype=torch.int32, device=DEV), 0, hb, host8)
+
+
 def test_pageable_host_memory_is_refused():
     B, ps, max_pages, n_slots, k = 1, 16, 8, 16, 4
     _, hb, _, _ = make(B, max_pages, n_slots, ps, seed=1)
@@ -150,4 +163,34 @@ def test_attention_over_the_hot_buffer_equals_the_whole_cache():
         o1, l1 = dsa.sparse_mla_fwd(q, hb.latent_cache(), idx, k, scale, lens, L)
         o2, l2 = dsa.sparse_mla_fwd(q, whole, idx, k, scale, lens, L)
         torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), step
+
+
+def test_fp8_attention_over_the_hot_buffer_equals_the_whole_cache():
+    """The same over an E4M3 latent cache: the hot buffer moves 576-byte rows and sparse MLA
+    over its block table gives the bits of sparse MLA over the whole FP8 cache."""
+    B, Q, L, k, ps, H = 2, 1, 4096, 512, 16, 64
+    max_pages, n_slots = L // ps, 640
+    gen = torch.Generator().manual_seed(12)
+    codes = torch.randint(0, 256, (B, L, D), dtype=torch.uint8, generator=gen)
+    codes[(codes & 0x7F) == 0x7F] = 0x38            # no NaN codes (0x38 = 1.0)
+    host = codes.view(B, max_pages, ps, D).contiguous().pin_memory()
+    q = (torch.randn((B, Q, H, D), generator=gen) * 0.5).to(torch.bfloat16).to(DEV)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    hb = dsa.HotBuffer(block_table=torch.full((B, max_pages), -1, dtype=torch.int32, device=DEV),
+                       slot_page=torch.full((B, n_slots), -1, dtype=torch.int32, device=DEV),
+                       slot_clock=torch.full((B, n_slots), -1, dtype=torch.int32, device=DEV),
+                       page_clock=torch.full((B, max_pages), -1, dtype=torch.int32, device=DEV),
+                       device_pool=torch.zeros((B * n_slots, ps, D), dtype=torch.uint8, device=DEV), page_size=ps)
+    whole = dsa.Cache(codes.to(DEV), None, 0)
+    rng = np.random.default_rng(4)
+    scale = 1.0 / np.sqrt(D)
+    for step in range(3):
+        scores = torch.from_numpy(rng.standard_normal((B, Q, L)).astype(np.float32)).to(DEV)
+        idx = dsa.topk(scores, lens, k)
+        dsa.hisparse_swap_in(idx, step, hb, host)
+        o1, l1 = dsa.sparse_mla_fwd(q, hb.latent_cache(), idx, k, scale, lens, L, latent_scale=0.02)
+        o2, l2 = dsa.sparse_mla_fwd(q, whole, idx, k, scale, lens, L, latent_scale=0.02)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o1).all()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), step
