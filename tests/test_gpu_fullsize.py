@@ -55,8 +55,10 @@ def check_rows_wellformed(idx, wl, share_first=False):
             assert np.all(np.diff(row[:m]) > 0) and row[0] >= 0 and row[m - 1] <= p
 
 
-def oracle_check_query(g, wl, b, j, scores_gpu, idx_gpu, outs, lses, share_first=False, layers=None):
-    """Oracle for one query token (b, j) of a full-size batch."""
+def oracle_check_query(g, wl, b, j, scores_gpu, idx_gpu, outs, lses, share_first=False, layers=None,
+                       q_mla=None, latent_scale=None):
+    """Oracle for one query token (b, j) of a full-size batch. q_mla: the MLA query of each entry
+    of outs (default: the layers' queries); latent_scale: the scale of an E4M3 latent cache."""
     layers = range(wl.n_layers) if layers is None else layers
     p = wl.lens[b] - wl.Q + j
     keys = seq_cache(g.keys, g.key_table, b)
@@ -70,18 +72,19 @@ def oracle_check_query(g, wl, b, j, scores_gpu, idx_gpu, outs, lses, share_first
     swaps = check_topk_sets(idx_gpu[b, 0 if share_first else j].cpu().numpy(), o_idx, exact, wl.k)
     users = range(wl.Q) if share_first else [j]
     worst = (0.0, 0.0)
+    q_src = g.q_mla if q_mla is None else q_mla
     for layer in layers:
-        lat = seq_cache(g.latent[layer], g.latent_table[layer], b)
-        qm = q_bits(g.q_mla[layer], b)
+        lat = seq_cache(g.latent[min(layer, len(g.latent) - 1)], g.latent_table[min(layer, len(g.latent) - 1)], b)
+        qm = q_bits(q_src[layer], b)
         for u in users:
-            ref_o, ref_l = oracle.sparse_mla_one(qm[u], lat, 0, o_idx, wl.scale)
+            ref_o, ref_l = oracle.sparse_mla_one(qm[u], lat, 0, o_idx, wl.scale, latent_scale=latent_scale)
             e = check_mla(outs[layer][b, u].cpu().numpy(), lses[layer][b, u].cpu().numpy(), ref_o, ref_l)
             worst = (max(worst[0], e[0]), max(worst[1], e[1]))
     print(f"  {wl.name} b={b} j={j}: {swaps} near-threshold swaps, out max abs {worst[0]:.3g} rel L2 {worst[1]:.3g}")
     return swaps
 
 
-def run_path(g, wl, share_first=False):
+def run_path(g, wl, share_first=False, q_mla=None, latent_scale=None):
     keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
     q_pos = None
     qi, wi = g.q_idx, g.w
@@ -91,10 +94,12 @@ def run_path(g, wl, share_first=False):
     scores = dsa.index_score(qi, wi, keys, g.seq_lens, wl.lmax, q_pos=q_pos)
     idx = dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos)
     outs, lses = [], []
-    for layer in range(wl.n_layers):
+    q_src = g.q_mla if q_mla is None else q_mla      # one query per layer, or per draft step on one cache
+    for c in range(len(q_src)):
+        layer = min(c, len(g.latent) - 1)
         lat = dsa.Cache(g.latent[layer], g.latent_table[layer], wl.page_size)
-        o, l = dsa.sparse_mla_fwd(g.q_mla[layer], lat, idx, wl.k, wl.scale, g.seq_lens, wl.lmax,
-                                  idx_q_stride=0 if share_first else wl.k)
+        o, l = dsa.sparse_mla_fwd(q_src[c], lat, idx, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                  idx_q_stride=0 if share_first else wl.k, latent_scale=latent_scale)
         outs.append(o)
         lses.append(l)
     torch.cuda.synchronize()
@@ -113,6 +118,32 @@ def test_decode_b32_128k_paged():
     assert torch.equal(scores, s2) and torch.equal(idx, i2) and torch.equal(outs[0], o2[0])
     for b in (0, 17, 31):
         oracle_check_query(g, wl, b, 0, scores, idx, outs, lses)
+
+
+def test_decode_b32_128k_paged_fp8kv():
+    """The decode batch over an E4M3 latent cache (576 codes per row, scale 1)."""
+    wl = synth.WORKLOADS["decode_b32_128k_paged_fp8kv"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    assert g.latent[0].dtype == torch.uint8
+    scores, idx, outs, lses = run_path(g, wl, latent_scale=1.0)
+    check_rows_wellformed(idx, wl)
+    s2, i2, o2, l2 = run_path(g, wl, latent_scale=1.0)
+    assert torch.equal(idx, i2) and torch.equal(outs[0], o2[0]) and torch.equal(lses[0], l2[0])
+    for b in (0, 31):
+        oracle_check_query(g, wl, b, 0, scores, idx, outs, lses, latent_scale=1.0)
+
+
+def test_mtp_draft_b32_128k_paged():
+    """One MTP draft loop at the decode shape: the index set of the base position serves all 7
+    draft steps over the one latent cache; each step's attention is checked for two sequences."""
+    wl = synth.WORKLOADS["mtp_draft_b32_128k_paged"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    drafts = synth.draft_queries(g, wl.draft_steps)
+    assert len(drafts) == 7 and len(g.latent) == 1
+    scores, idx, outs, lses = run_path(g, wl, q_mla=drafts)
+    check_rows_wellformed(idx, wl)
+    for b in (2, 29):
+        oracle_check_query(g, wl, b, 0, scores, idx, outs, lses, layers=range(7), q_mla=drafts)
 
 
 def test_prefill_4096_at_128k():
@@ -155,41 +186,47 @@ def test_verify_b64_q8_32k(name):
             oracle_check_query(g, wl, 5, j, scores, idx, outs, lses)
 
 
-def test_hisparse_b8_1m_decode():
+@pytest.mark.parametrize("name", ["hisparse_b8_1m_decode", "hisparse_b8_1m_decode_fp8kv"])
+def test_hisparse_b8_1m_decode(name):
     """The hot buffer at the benchmark's size: 8 sequences of 1M tokens, 6144 slots of 16
     tokens each, the latent cache in pinned host memory, three drifting decode steps. After
     each step the library's state equals the oracle's on the same selected sets (every table
     entry), the slots written by the step hold the host bytes of their pages, and sparse MLA
     over the hot buffer gives the bits of sparse MLA over the whole device cache."""
-    wl = synth.WORKLOADS["hisparse_b8_1m_decode"]
+    wl = synth.WORKLOADS[name]
     g = synth.generate(wl, seed=0, device=DEV)
+    fp8 = bool(wl.latent_fp8)
+    scale8 = 1.0 if fp8 else None
+    bits = torch.uint8 if fp8 else torch.int16
     keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
     whole = dsa.Cache(g.latent[0], g.latent_table[0], wl.page_size)
-    host = g.latent[0][g.latent_table[0].long()].view(torch.int16).cpu().pin_memory()
+    host = g.latent[0][g.latent_table[0].long()].view(bits).cpu().pin_memory()
     host_np = host.numpy()
     hb = dsa.HotBuffer(
         block_table=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=DEV),
         slot_page=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=DEV),
         slot_clock=torch.full((wl.B, wl.n_slots), -1, dtype=torch.int32, device=DEV),
         page_clock=torch.full((wl.B, wl.max_pages), -1, dtype=torch.int32, device=DEV),
-        device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=torch.bfloat16, device=DEV),
+        device_pool=torch.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=bits, device=DEV),
         page_size=wl.page_size)
     st = oracle.HotBufferState.empty(wl.B, wl.max_pages, wl.n_slots)
-    dev_np = np.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=np.int16)
+    dev_np = np.zeros((wl.B * wl.n_slots, wl.page_size, 576), dtype=host_np.dtype)
     for step, q in enumerate(synth.drift_queries(g, 3)):
         scores = dsa.index_score(q, g.w, keys, g.seq_lens, wl.lmax)
         idx = dsa.topk(scores, g.seq_lens, wl.k)
         del scores
         copied = torch.zeros((wl.B,), dtype=torch.int32, device=DEV)
         dsa.hisparse_swap_in(idx, step, hb, host, copied=copied)
-        o1, l1 = dsa.sparse_mla_fwd(g.q_mla[0], hb.latent_cache(), idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
-        o2, l2 = dsa.sparse_mla_fwd(g.q_mla[0], whole, idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+        o1, l1 = dsa.sparse_mla_fwd(g.q_mla[0], hb.latent_cache(), idx, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                    latent_scale=scale8)
+        o2, l2 = dsa.sparse_mla_fwd(g.q_mla[0], whole, idx, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                    latent_scale=scale8)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), step
         copies = oracle.swap_in(st, idx.cpu().numpy(), step, wl.page_size, host_np, dev_np)
         for name in ("block_table", "slot_page", "slot_clock", "page_clock"):
             assert np.array_equal(getattr(hb, name).cpu().numpy(), getattr(st, name)), (name, step)
         assert copied.cpu().tolist() == [sum(1 for c in copies if c[0] == b) for b in range(wl.B)], step
-        pool = hb.device_pool.view(torch.int16)
+        pool = hb.device_pool.view(bits)
         for b, p, s in copies[:: max(1, len(copies) // 64)]:     # a sample of this step's copies
             assert np.array_equal(pool[b * wl.n_slots + s].cpu().numpy(), host_np[b, p]), (step, b, p)
