@@ -5,7 +5,8 @@
 //   z_i = scale * q_h . c_i (576 dims), o_h = sum_i softmax(z)_i c_i[0:512], lse_h = log sum exp z.
 //
 // One workgroup = one query token x all H heads (4 waves, one per SIMD, 32 heads each at
-// H = 128) x one split of the selected tokens. Per step of 32 tokens the workgroup gathers the
+// H = 128; or, in launches too small to fill half the chip, 64 of the 128 heads at 16 per
+// wave) x one split of the selected tokens. Per step of 32 tokens the workgroup gathers the
 // 32 rows (1152 B each, through the index list and the block table) into a token-major LDS
 // tile, then each wave runs, for each of its 16-head tiles,
 //   S^T[32 tok x 16 heads] = K_tile . Q^T      (bf16 16x16x32 matrix cores, K = 576)
@@ -136,7 +137,7 @@ template <int NW, int HT, bool SPLIT, bool F8>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, int Q, int H, int splits,
     int split_len, float scale_log2, float out_scale, part_t* __restrict__ part_o_all,
-    float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride) {
+    float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride, int n_hg, int n_units) {
   // layer blockIdx.y of the launch: its query, latent cache, outputs and partials
   const int layer = blockIdx.y;
   const uint16_t* __restrict__ q = layers.q[layer];
@@ -173,10 +174,20 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int split = blockIdx.x % splits;
-  const int bq = blockIdx.x / splits;
+  // unit = (query token, split); with n_hg head groups, the groups of one unit are 8 workgroups
+  // apart, which puts them on one XCD (workgroups are dealt to the 8 XCDs in turn), so that the
+  // second group's gathers of the same rows hit that XCD's L2
+  int unit = blockIdx.x, hg = 0;
+  if (n_hg > 1) {
+    const int grp = blockIdx.x / (8 * n_hg), r = blockIdx.x - grp * 8 * n_hg;
+    hg = r >> 3;
+    unit = grp * 8 + (r & 7);
+  }
+  if (unit >= n_units) return;                         // the grid is padded to whole groups of 8
+  const int split = unit % splits;
+  const int bq = unit / splits;
   const int b = bq / Q, j = bq - b * Q;
-  const int h0 = wave * 16 * HT;                       // this wave's heads: tile ht = h0 + 16 ht ..
+  const int h0 = (hg * NW + wave) * 16 * HT;           // this wave's heads: tile ht = h0 + 16 ht ..
   constexpr int my_dma = kSegs;                        // loads this wave issues per step
 
   const int32_t* irow = idx + (int64_t)b * (idx_q_stride ? (int64_t)Q * k : k) + (int64_t)j * idx_q_stride;
@@ -593,14 +604,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
 template <int NW, int HT, bool F8>
 static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L, const int32_t* idx, int k,
                        int idx_q_stride, int Q, int H, int split_len, float sl2, float out_scale, part_t* part_o,
-                       float* part_lse, int64_t so, int64_t sl) {
+                       float* part_lse, int64_t so, int64_t sl, int n_hg, int units) {
   const dim3 block(NW * 64);
   if (splits == 1)
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
-                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0);
+                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, n_hg, units);
   else
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H,
-                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl);
+                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, n_hg, units);
 }
 
 // latent_scale > 0: FP8 latent rows (576 E4M3 codes, value = latent_scale x code); 0: bf16 rows
@@ -634,20 +645,25 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
       part_o = (part_t*)ws;
       part_lse = (float*)((char*)ws + (size_t)nl * part_o_layer(rows, splits, H));
     }
-    const dim3 grid((unsigned)(rows * splits), (unsigned)nl);
-    // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64)
-    if (f8 && H == 128)
-      launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, latent_scale, part_o,
-                             part_lse, so, sl);
+    // one wave per SIMD: 4 waves x 32 heads (H = 128) or 4 waves x 16 heads (H = 64). When the
+    // splits are already as short as they go and the launch still fills under half the chip, the
+    // 128 heads are dealt to two workgroups of 4 x 16 heads instead (same splits, same results).
+    const int units = rows * splits;
+    const int n_hg = (H == 128 && 2 * units * nl <= kTargetWgs) ? 2 : 1;
+    const dim3 grid(n_hg == 1 ? (unsigned)units : (unsigned)((units + 7) / 8 * 8 * n_hg), (unsigned)nl);
+    const float os = f8 ? latent_scale : 1.f;
+    if (f8 && H == 128 && n_hg == 1)
+      launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o, part_lse,
+                             so, sl, 1, units);
     else if (f8)
-      launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, latent_scale, part_o,
-                             part_lse, so, sl);
-    else if (H == 128)
-      launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, 1.f, part_o,
-                              part_lse, so, sl);
+      launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o, part_lse,
+                             so, sl, n_hg, units);
+    else if (H == 128 && n_hg == 1)
+      launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o,
+                              part_lse, so, sl, 1, units);
     else
-      launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, 1.f, part_o,
-                              part_lse, so, sl);
+      launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o,
+                              part_lse, so, sl, n_hg, units);
     if (splits > 1)
       hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2), (unsigned)nl), dim3(256), 0, s, L,
                          part_o, part_lse, H, splits, so, sl);
