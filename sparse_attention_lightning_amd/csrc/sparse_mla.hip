@@ -203,14 +203,20 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   const int my_row = 8 * wave + (lane >> 3);
   // Steps past the last one load row 0 into a slot that is read no more: every step issues the
   // same loads, so the number of loads in flight is the same on every path.
-  auto issue_step = [&](int st, auto slot) {
+  auto step_row = [&](int st) { return st < n_steps ? rowid[st * kTok + my_row] : -1; };
+  auto row_src = [&](int r) -> const uint8_t* {
+    return lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0) + 16 * ((lane & 7) ^ (my_row & 7));
+  };
+  auto step_src = [&](int st) { return row_src(step_row(st)); };
+  auto issue_seg = [&](const uint8_t* src, auto slot, int sg) {
     uint8_t* base = ring_of(slot) + wave * 1024;
-    const int r = st < n_steps ? rowid[st * kTok + my_row] : -1;
-    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0) + 16 * ((lane & 7) ^ (my_row & 7));
+    __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
+                                     (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128)), 16, 0, 0);
+  };
+  auto issue_step = [&](int st, auto slot) {
+    const uint8_t* src = step_src(st);
 #pragma unroll
-    for (int sg = 0; sg < kSegs; ++sg)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
-                                       (__attribute__((address_space(3))) void*)(base + sg * (kTok * 128)), 16, 0, 0);
+    for (int sg = 0; sg < kSegs; ++sg) issue_seg(src, slot, sg);
   };
 
   // Row index (into the cache's rows) of every token of the split, -1 for masked tokens. The
@@ -348,7 +354,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // QK, softmax and PV of step st on a landed bf16 tile
-    auto compute = [&](int st, const uint8_t* tile) {
+    // seg(sg) issues load segment sg of a later step. Issuing a direct-to-LDS load can hold the
+    // wave for tens of cycles while the memory pipeline takes the previous ones; issued as one
+    // block before the products, the 9 loads of a step took about a sixth of the step with the
+    // matrix cores idle. The QK loop spreads them over its fragment batches instead, so that the
+    // matrix cores run through those holds.
+    auto compute = [&](int st, const uint8_t* tile, auto seg) {
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
       const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
@@ -392,6 +403,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) sacc[ht][f & 1] = mfma_bf16(kc[i], qb[ht][f >> 1], sacc[ht][f & 1]);
           }
+          static_assert(NF / kFragBatch == 2 * kSegs, "one load segment per two K fragment batches");
+          if (bt & 1) seg(bt >> 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < kFragBatch; ++i) kc[i] = kn[i];
@@ -475,6 +488,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     if constexpr (!F8) {
       issue_step(0, I0{});
       issue_step(1, I1{});
+      // the row of step st + 2 is read from LDS a step early, so that its latency is not waited
+      // for right before the loads that need it
+      int row_ahead = step_row(kAheadSteps);
       // step st in ring slot S = st % 3
       auto step_body = [&](int st, auto slot) {
         constexpr int S = decltype(slot)::value;
@@ -484,8 +500,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         wait_counts<63, 0>();                          // LDS writes done before the barrier
         __builtin_amdgcn_s_barrier();
         // into step st - 1's slot, which every wave has finished reading
-        issue_step(st + kAheadSteps, std::integral_constant<int, (S + kAheadSteps) % kStages>{});
-        compute(st, ring_of(slot));
+        const uint8_t* src = row_src(row_ahead);
+        row_ahead = step_row(st + kAheadSteps + 1);
+        using SN = std::integral_constant<int, (S + kAheadSteps) % kStages>;
+        compute(st, ring_of(slot), [&](int sg) { issue_seg(src, SN{}, sg); });
       };
       // unrolled by the three ring slots, so that every step names its slots statically
       for (int st = 0; st < n_steps; st += kStages) {
@@ -512,7 +530,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
           wait_counts<kDma8, 15>();                    // step st + 1's rows have landed
           convert8(st + 1, Pn{}, Pn{});
         }
-        compute(st, ring_of(p));
+        compute(st, ring_of(p), [](int) {});
       };
       for (int st = 0; st < n_steps; st += 2) {
         step8(st, I0{});
