@@ -261,20 +261,22 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   // FP8 rows of step st into staging buffer p: chunk i = 64 d + lane of the wave's 288 is
   // 16 bytes of row 8 wave + i / 36; chunks past 288 (half of the last load) and rows of
   // masked tokens or of steps past the last read row 0 into places nothing reads.
-  auto issue_step8 = [&](int st, auto p) {
+  // load d of this wave's share of step st, into staging buffer p. The lane's chunk numbers
+  // are recomputed at every load rather than kept across the loop, where they would cost
+  // registers the step needs.
+  auto issue_seg8 = [&](int st, auto p, int d) {
     uint8_t* base = stg_of(p) + wave * kWaveStage8;
-    // the lane's chunk numbers are recomputed at every step rather than kept across the loop,
-    // where they would cost registers the step needs
     const int ln = (int)opaque_u32((uint32_t)lane);
+    const int i = d * 64 + ln;
+    const int rl = i / 36, c = i - 36 * (i / 36);
+    const int r = (i < kChunks8Wave && st < n_steps) ? rowid[st * kTok + 8 * wave + rl] : -1;
+    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes8 + 16 * c : 0);
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + d * 1024),
+                                     16, 0, 0);
+  };
+  auto issue_step8 = [&](int st, auto p) {
 #pragma unroll
-    for (int d = 0; d < kDma8; ++d) {
-      const int i = d * 64 + ln;
-      const int rl = i / 36, c = i - 36 * (i / 36);
-      const int r = (i < kChunks8Wave && st < n_steps) ? rowid[st * kTok + 8 * wave + rl] : -1;
-      const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes8 + 16 * c : 0);
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + d * 1024),
-                                       16, 0, 0);
-    }
+    for (int d = 0; d < kDma8; ++d) issue_seg8(st, p, d);
   };
   // this wave's 8 FP8 rows of step st, from staging buffer p into the bf16 tile of `slot`
   // (masked tokens become zero rows). E4M3 values are exact in bf16: a code converts to fp32,
@@ -523,14 +525,16 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         using Pn = std::integral_constant<int, 1 - P>;
         wait_counts<63, 0>();                          // conversion writes done before the barrier
         __builtin_amdgcn_s_barrier();
-        // staging p held step st, which this wave converted a step ago; bf16 slot 1 - p held step
-        // st - 1, which every wave has finished reading
-        issue_step8(st + 2, p);
+        // bf16 slot 1 - p held step st - 1, which every wave has finished reading
         if (st + 1 < n_steps) {                        // workgroup-uniform
-          wait_counts<kDma8, 15>();                    // step st + 1's rows have landed
+          wait_counts<0, 15>();                        // step st + 1's rows have landed
           convert8(st + 1, Pn{}, Pn{});
         }
-        compute(st, ring_of(p), [](int) {});
+        // staging p held step st, which this wave converted a step ago: step st + 2's loads go
+        // there, spread over the QK loop like the bf16 path's
+        compute(st, ring_of(p), [&](int sg) {
+          if (sg < kDma8) issue_seg8(st + 2, p, sg);
+        });
       };
       for (int st = 0; st < n_steps; st += 2) {
         step8(st, I0{});
