@@ -580,32 +580,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   }
 }
 
-// Merge split partials: one workgroup per (query token, 2 heads), 128 threads x 4 dims per head;
-// every split's lse and partial are loaded before the merge, so the loads overlap.
+// Merge split partials: one workgroup per (query token, 4 heads), 64 threads x 8 dims per head
+// (one 16-byte load per split and thread); every split's lse and partial are loaded before the
+// merge, so the loads overlap.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
                                                           const float* __restrict__ part_lse_all, int H, int splits,
                                                           int64_t part_o_stride, int64_t part_lse_stride) {
-  typedef part_t p4 __attribute__((ext_vector_type(4)));
+  typedef part_t p8 __attribute__((ext_vector_type(8)));
   const int layer = blockIdx.y;
   const part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
   const float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
   float* __restrict__ out = layers.out[layer];
   float* __restrict__ lse_out = layers.lse[layer];
-  const int hl = threadIdx.x >> 7, t = threadIdx.x & 127;
-  const int bq = blockIdx.x / (H / 2);
-  const int h = (blockIdx.x - bq * (H / 2)) * 2 + hl;
+  const int hl = threadIdx.x >> 6, t = threadIdx.x & 63;
+  const int bq = blockIdx.x / (H / 4);
+  const int h = (blockIdx.x - bq * (H / 4)) * 4 + hl;
   float ls[kMaxSplits];
-  p4 po[kMaxSplits];
+  p8 po[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     const int64_t ps = (int64_t)bq * splits + s;
     ls[s] = s < splits ? part_lse[ps * H + h] : -INFINITY;
-    if (s < splits) po[s] = *(const p4*)(part_o + (ps * H + h) * kDv + 4 * t);
+    if (s < splits) po[s] = *(const p8*)(part_o + (ps * H + h) * kDv + 8 * t);
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) mx = fmaxf(mx, ls[s]);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float den = 0.f;
   if (mx != -INFINITY) {
 #pragma unroll
@@ -614,12 +615,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
         const float wgt = expf(ls[s] - mx);
         den += wgt;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += wgt * (float)po[s][e];
+        for (int e = 0; e < 8; ++e) acc[e >> 2][e & 3] += wgt * (float)po[s][e];
       }
     }
-    acc *= 1.f / den;
+    const float inv = 1.f / den;
+    acc[0] *= inv;
+    acc[1] *= inv;
   }
-  *(v4f*)(out + ((int64_t)bq * H + h) * kDv + 4 * t) = acc;
+  float* orow = out + ((int64_t)bq * H + h) * kDv + 8 * t;
+  *(v4f*)orow = acc[0];
+  *(v4f*)(orow + 4) = acc[1];
   if (t == 0 && lse_out) lse_out[(int64_t)bq * H + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(den);
 }
 
@@ -687,7 +692,7 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
       launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o,
                               part_lse, so, sl, n_hg, units);
     if (splits > 1)
-      hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 2), (unsigned)nl), dim3(256), 0, s, L,
+      hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 4), (unsigned)nl), dim3(256), 0, s, L,
                          part_o, part_lse, H, splits, so, sl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
