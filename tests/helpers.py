@@ -97,13 +97,14 @@ def check_topk_sets(gpu_idx, oracle_idx, exact_scores, k):
     return int(diff.size)
 
 
-def check_mla(out_gpu, lse_gpu, out_ref, lse_ref):
-    """One query token: out [H, 512], lse [H]."""
+def check_mla(out_gpu, lse_gpu, out_ref, lse_ref, max_abs_bar=MLA_MAX_ABS):
+    """One query token: out [H, 512], lse [H]. max_abs_bar defaults to the bar for outputs of the
+    workloads' scale."""
     og = np.asarray(out_gpu, dtype=np.float64)
     err = np.abs(og - out_ref)
     max_abs = float(err.max())
     rel_l2 = float(np.linalg.norm(og - out_ref) / max(np.linalg.norm(out_ref), 1e-30))
-    assert max_abs <= MLA_MAX_ABS, f"max abs error {max_abs}"
+    assert max_abs <= max_abs_bar, f"max abs error {max_abs}"
     assert rel_l2 <= MLA_REL_L2, f"relative L2 error {rel_l2}"
     if lse_gpu is not None:
         lg = np.asarray(lse_gpu, dtype=np.float64)

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import (bits, check_mla, check_scores, check_topk_sets, dsa_cache, integer_e4m3, key_cache,
+from helpers import (MLA_MAX_ABS, bits, check_mla, check_scores, check_topk_sets, dsa_cache, integer_e4m3, key_cache,
                      latent_cache, np_, positions, score_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -402,3 +402,75 @@ def test_sparse_mla_fp8_latent_equals_bf16_cache_of_its_values(H):
                                 g.seq_lens, wl.lmax)
     torch.cuda.synchronize()
     assert torch.equal(o8, ob) and torch.equal(l8, lb)
+
+
+def e4m3_codes(x):
+    """E4M3FN codes (uint8) of float values (torch's round-to-nearest-even cast)."""
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+@pytest.mark.parametrize("H", [128, 64])
+def test_sparse_mla_fp8_logit_jumps_after_the_first_step(H):
+    """The softmax-reference cases of the bf16 test on an E4M3 cache: a late logit about 30
+    binades above the reference, one beyond the headroom (the split is computed a second time
+    through the FP8 staging and conversion path), and a split whose first step is masked."""
+    gen = torch.Generator().manual_seed(6)
+    B, L, k = 3, 4096, 2048
+    scale = 1.0 / 576 ** 0.5
+    q = torch.randn((B, 1, H, 576), generator=gen).to(torch.bfloat16)
+    codes = e4m3_codes(torch.randn((B, L, 576), generator=gen))
+    idx = torch.arange(k, dtype=torch.int32).repeat(B, 1, 1)
+    codes[0, 2040] = e4m3_codes(q[0, 0, 3].float())                # head 3: logit ~ 24
+    codes[1, 2040] = e4m3_codes(4 * q[1, 0, 5].float())            # head 5: logit ~ 96
+    idx[2, 0, :40] = -1                                            # first step of split 0 masked
+    codes[2, 1000] = e4m3_codes(3 * q[2, 0, 1].float())            # head 1: logit ~ 72
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    out, lse = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(codes.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L,
+                                  latent_scale=1.0)
+    # every E4M3 value is a bf16 value: the bits of the bf16 path over the decoded rows, second
+    # pass included
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float32).to(torch.bfloat16)
+    ob, lb = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(vals.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ob) and torch.equal(lse, lb)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(q), oracle.Cache(codes.numpy()), idx.numpy(), scale, latent_scale=1.0)
+    for b in range(B):
+        # The planted rows carry values up to about 18, and heads they dominate have outputs of that
+        # size, far beyond the workloads' (about 0.04 RMS). P and the split partials are bf16, each
+        # within 2^-9 relative, so the absolute bar scales with the output: 2^-8 of its largest value.
+        bar = max(MLA_MAX_ABS, 2.0 ** -8 * float(np.abs(ref_o[b, 0]).max()))
+        check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0], max_abs_bar=bar)
+
+
+def test_sparse_mla_fp8_shared_index_row_and_empty_sets():
+    wl = synth.small("verify_b64_q8_32k", B=2, Q=4, L=2500, L_max=2560, k=512, latent_fp8=1)
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl, share_first=True)       # [B, 1, k]
+    idx[1, 0, :] = -1                                    # sequence 1: empty set -> out 0, lse -inf
+    idx_g = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax, idx_q_stride=0,
+                                  latent_scale=0.5)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), idx, wl.scale, idx_q_stride_is_k=False,
+                                           latent_scale=0.5)
+    for j in range(wl.Q):
+        check_mla(out[0, j], lse[0, j], ref_o[0, j], ref_l[0, j])
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_sparse_mla_fp8_deterministic_and_paged_equals_contiguous():
+    wl = synth.small("decode_b32_128k_paged", B=3, L=4000, L_max=4032, planted=0, seq_lens=(4000, 3000, 2222),
+                     latent_fp8=1)
+    cpu, g = gpu_batch(wl)
+    idx, _ = oracle_idx(cpu, wl)
+    idx_g = torch.from_numpy(idx).to(DEV)
+    run = lambda cache: dsa.sparse_mla_fwd(g.q_mla[0], cache, idx_g, wl.k, wl.scale, g.seq_lens, wl.lmax,
+                                           latent_scale=1.0)
+    o1, l1 = run(lat_arg(g))
+    o2, l2 = run(lat_arg(g))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    tab = g.latent_table[0].long()
+    contig = g.latent[0][tab].reshape(wl.B, wl.lmax, 576).contiguous()
+    o3, l3 = run(dsa_cache(contig, None, 0))
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
