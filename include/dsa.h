@@ -106,8 +106,11 @@ dsa_status dsa_topk(const dsa_batch_t* batch, const float* scores, int k, int32_
  *           k (one set per query token) or 0 (one set per sequence, shared by its Q tokens)
  *   out     [B][Q][H][512] float         lse [B][Q][H] float, or NULL
  * A query whose set has no valid entry gets out = 0 and lse = -inf.
- * H must be 64 or 128; 1 <= k <= 2048. QK and PV run on bf16 matrix cores with fp32
- * accumulation; softmax weights are rounded to bf16 for PV.
+ * H must be 64 or 128; 1 <= k <= 2048; softmax_scale finite and >= 0 (the kernel takes the
+ * maximum of the raw logits and scales it, which needs a non-negative scale; a negative or
+ * non-finite scale returns DSA_ERR_INVALID_ARG). QK and PV run on bf16 matrix cores with fp32
+ * accumulation; softmax weights are rounded to bf16 for PV and the output is normalised by the
+ * sum of the rounded weights (lse by the sum of the unrounded ones).
  * ws: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes (split partials), 256-byte aligned. */
 dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H,
                               const dsa_cache_t* latent, const int32_t* idx, int k, int idx_q_stride,

@@ -162,7 +162,8 @@ dsa_status dsa_sparse_mla_fwd(const dsa_batch_t* batch, const uint16_t* q, int H
   if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
   if (idx_q_stride != 0 && idx_q_stride != k)
     return fail(DSA_ERR_INVALID_ARG, "%s: idx_q_stride=%d must be 0 or k=%d", who, idx_q_stride, k);
-  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0", who);
   TRY(check_ptr(q, 16, who, "q"));
   TRY(check_ptr(idx, 4, who, "idx"));
   TRY(check_ptr(out, 16, who, "out"));
@@ -185,7 +186,8 @@ dsa_status dsa_sparse_mla_fwd_fp8(const dsa_batch_t* batch, const uint16_t* q, i
   if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
   if (idx_q_stride != 0 && idx_q_stride != k)
     return fail(DSA_ERR_INVALID_ARG, "%s: idx_q_stride=%d must be 0 or k=%d", who, idx_q_stride, k);
-  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0", who);
   if (!std::isfinite(latent_scale) || !(latent_scale > 0.f))
     return fail(DSA_ERR_INVALID_ARG, "%s: latent_scale must be finite and > 0", who);
   TRY(check_ptr(q, 16, who, "q"));
@@ -213,7 +215,8 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
   if (share_first_query != 0 && share_first_query != 1)
     return fail(DSA_ERR_INVALID_ARG, "%s: share_first_query=%d must be 0 or 1", who, share_first_query);
   if (n_layers < 1 || n_layers > 64) return fail(DSA_ERR_INVALID_ARG, "%s: n_layers=%d outside [1, 64]", who, n_layers);
-  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale is not finite", who);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0", who);
   TRY(check_ptr(q_e4m3, 16, who, "q_e4m3"));
   TRY(check_ptr(w, 4, who, "w"));
   TRY(check_ptr(idx_out, 4, who, "idx_out"));

@@ -19,8 +19,9 @@
 // every V fragment also feeds both head tiles. The 32-head output accumulator (256 registers)
 // lives in the matrix-core accumulator registers; it is only ever written by products, which
 // is why the softmax keeps one reference per head instead of rescaling O (see the kernel).
-// The softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV.
-// With several splits, each workgroup writes its normalised partial (o_s, lse_s) and a
+// The softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV, and the output is
+// normalised by the sum of those rounded weights (lse by the sum of the fp32 ones).
+// With several splits, each workgroup writes its normalised partial (o_s, lse_s) in fp32 and a
 // combine kernel merges them: lse = log sum_s exp lse_s, o = sum_s exp(lse_s - lse) o_s.
 #include <algorithm>
 #include <type_traits>
@@ -48,9 +49,9 @@ constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Split partials: normalised outputs o_s (|o_s| <= the largest value entry, a convex
-// combination) stored as bf16 to halve their traffic, plus fp32 lse_s.
-typedef __bf16 part_t;
+// Split partials: normalised outputs o_s and lse_s, both fp32. (bf16 partials lose up to 2^-9
+// of |o_s|, which is more than 2e-2 once outputs reach about 10.)
+typedef float part_t;
 
 // Per-layer arguments of a launch over up to kMlaMaxLayers layers that share one index set
 // (IndexShare): blockIdx.y picks the layer.
@@ -336,7 +337,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   // kRefHeadroom, the split is computed again with m_ref = the exact maximum of its logits,
   // which the first pass records.
   v4f o[HT][kDv / 16];
-  float m_ref[HT], m_max[HT], l_run[HT];
+  // l_run sums the fp32 weights (for lse); l_pv sums the bf16-rounded weights that PV multiplies,
+  // so that the output's numerator and denominator use the same weights: a dominant token's
+  // rounding then cancels instead of scaling the output by up to 1 +- 2^-9.
+  float m_ref[HT], m_max[HT], l_run[HT], l_pv[HT];
   bool redo = false;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) m_max[ht] = -INFINITY;
@@ -351,6 +355,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       for (int nt = 0; nt < kDv / 16; ++nt) o[ht][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
       m_ref[ht] = pass == 0 ? -INFINITY : m_max[ht];
       l_run[ht] = 0.f;
+      l_pv[ht] = 0.f;
     }
     constexpr int kAheadSteps = kStages - 1;
     using I0 = std::integral_constant<int, 0>;
@@ -456,10 +461,17 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         for (int i = 0; i < 8; ++i) {
           // v_exp_f32 directly: its flush of results below 2^-126 to 0 is harmless here
           const float pv = __builtin_amdgcn_exp2f(fmaf(z[i], scale_log2, neg_m));
-          psum += pv;                                  // the denominator sums the fp32 weights
+          psum += pv;
           pa[ht][i] = (__bf16)pv;
         }
         l_run[ht] += psum;
+        // the rounded weights, two per dot-product instruction (products by 1 are exact)
+        const v2bf one2 = {(__bf16)1.f, (__bf16)1.f};
+        float pbsum = l_pv[ht];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2)
+          pbsum = __builtin_amdgcn_fdot2_f32_bf16((v2bf){pa[ht][i], pa[ht][i + 1]}, one2, pbsum, false);
+        l_pv[ht] = pbsum;
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- O += P . V; each V fragment feeds HT products
@@ -552,11 +564,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const float l_tot = sum_xor32(sum_xor16(l_run[ht]));
+    const float lpv_tot = sum_xor32(sum_xor16(l_pv[ht]));
     const float lse_h = (l_tot > 0.f) ? (m_ref[ht] + log2f(l_tot)) * kLn2 : -INFINITY;
     float inv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(l_tot, 4 * g + r, 64);
+      const float lr = __shfl(lpv_tot, 4 * g + r, 64);
       inv[r] = lr > 0.f ? 1.f / lr : 0.f;
       if constexpr (F8) inv[r] *= out_scale;         // the FP8 cache's scale on the values
     }
@@ -581,7 +594,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 }
 
 // Merge split partials: one workgroup per (query token, 4 heads), 64 threads x 8 dims per head
-// (one 16-byte load per split and thread); every split's lse and partial are loaded before the
+// (two 16-byte loads per split and thread); every split's lse and partial are loaded before the
 // merge, so the loads overlap.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
                                                           const float* __restrict__ part_lse_all, int H, int splits,

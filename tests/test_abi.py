@@ -104,12 +104,32 @@ def test_sparse_mla_rejects():
     assert call(stride=5) == INVALID
     assert call(scale=float("nan")) == INVALID
     assert call(scale=float("inf")) == INVALID
+    # the kernel takes the maximum of the raw logits and scales it afterwards: only a
+    # non-negative scale commutes with that maximum
+    assert call(scale=-0.04) == INVALID
+    assert call(scale=-1e-30) == INVALID
     assert call(q=A + 4) == INVALID
     assert call(out=A + 4) == INVALID
     assert call(lse=A + 2) == INVALID
     if need:
         assert call(ws=None) == WORKSPACE
         assert call(n=need - 1) == WORKSPACE
+
+
+def test_sparse_mla_fp8_rejects_scales():
+    lib = dsa.lib()
+    bt = batch(B=1, L=8192)
+    kc = cache()
+    need = dsa.workspace_size(dsa.OP_SPARSE_MLA, 1, 1, 8192, H=128, k=2048)
+
+    def call(scale=0.04, latent_scale=1.0):
+        return lib.dsa_sparse_mla_fwd_fp8(C.byref(bt), A, 128, C.byref(kc), latent_scale, A, 2048, 2048, scale, A, A,
+                                          A, need, None)
+    assert call(scale=-0.04) == INVALID
+    assert call(scale=float("-inf")) == INVALID
+    assert call(latent_scale=0.0) == INVALID
+    assert call(latent_scale=-1.0) == INVALID
+    assert call(latent_scale=float("nan")) == INVALID
 
 
 def test_forward_shared_rejects():
@@ -120,9 +140,11 @@ def test_forward_shared_rejects():
     ptrs = (C.c_void_p * 4)(A, A, A, A)
     need = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 1, 1, 8192, k=2048, n_layers=4)
 
-    def call(share=0, nl=4, qs=ptrs, lats=lat, outs=ptrs, ws=A, n=need, Hi=64, H=128):
-        return lib.dsa_forward_shared(C.byref(bt), A, A, Hi, C.byref(kc), 2048, share, nl, qs, H, lats, 0.04, outs,
+    def call(share=0, nl=4, qs=ptrs, lats=lat, outs=ptrs, ws=A, n=need, Hi=64, H=128, scale=0.04):
+        return lib.dsa_forward_shared(C.byref(bt), A, A, Hi, C.byref(kc), 2048, share, nl, qs, H, lats, scale, outs,
                                       None, A, ws, n, None)
+    assert call(scale=-0.04) == INVALID
+    assert call(scale=float("nan")) == INVALID
     assert call(share=2) == INVALID
     assert call(nl=0) == INVALID
     assert call(qs=None) == INVALID

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import (MLA_MAX_ABS, bits, check_mla, check_scores, check_topk_sets, dsa_cache, integer_e4m3, key_cache,
+from helpers import (bits, check_mla, check_scores, check_topk_sets, dsa_cache, integer_e4m3, key_cache,
                      latent_cache, np_, positions, score_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -51,6 +51,49 @@ def test_index_score_integer_inputs_exact(Hi, page_size):
     torch.cuda.synchronize()
     kc = key_cache(cpu)
     pos = positions(wl)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            p = pos[b][j]
+            exact = oracle.index_scores(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc, b, p, wl.lmax)
+            tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)),
+                                  integer_inputs=True)
+            check_scores(scores[b, j], exact, tol, p)
+
+
+@pytest.mark.parametrize("Q,page_size,L_max,lens", [
+    (1, 16, 5008, (5000, 4099, 1500)),     # decode form over 16-token pages (the hot buffer's page)
+    (1, 32, 5024, (5024, 4099, 1500)),
+    (1, 48, 5040, (5001, 4099, 47)),       # a page size that is not a power of two; a one-page row
+    (1, 0, 5001, (5001, 4099, 1500)),      # contiguous, L_max % 8 != 0: each lane finds its own row
+    (2, 0, 5001, (5001, 4099, 1500)),      # the multi-query form of the same
+    (3, 0, 4093, (4093, 2050, 17)),
+])
+def test_index_score_page_sizes_and_odd_row_strides(Q, page_size, L_max, lens):
+    """Integer-valued inputs (exact products: only the fp32 head sum rounds), then the top-k sets
+    of N(0,1) inputs against the oracle's, on page sizes and row strides the workloads do not use."""
+    wl = synth.Workload("odd", B=3, Q=Q, L=max(lens), Hi=64, page_size=page_size, L_max=L_max, seq_lens=lens,
+                        k=1000)
+    cpu, g = gpu_batch(wl, with_mla=False)
+    pos = positions(wl)
+    kc = key_cache(cpu)
+    # N(0,1) inputs: scores within the truncation bound, sets equal up to near-threshold swaps
+    scores = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax)
+    idx = np_(dsa.topk(scores, g.seq_lens, wl.k))
+    scores = np_(scores)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            p = pos[b][j]
+            exact = oracle.index_scores(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc, b, p, wl.lmax)
+            tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)))
+            check_scores(scores[b, j], exact, tol, p)
+            check_topk_sets(idx[b, j], oracle.select_topk(exact.astype(np.float32), p, wl.k), exact, wl.k)
+    # integer inputs: exact up to the fp32 head sum
+    gen = torch.Generator().manual_seed(12)
+    cpu.q_idx = integer_e4m3(tuple(cpu.q_idx.shape), gen)
+    cpu.keys = integer_e4m3(tuple(cpu.keys.shape), gen)
+    g.q_idx, g.keys = cpu.q_idx.to(DEV), cpu.keys.to(DEV)
+    scores = np_(dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax))
+    kc = key_cache(cpu)
     for b in range(wl.B):
         for j in range(wl.Q):
             p = pos[b][j]
@@ -227,6 +270,36 @@ def test_sparse_mla_logit_jumps_after_the_first_step(H):
     out, lse = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(lat.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L)
     out, lse = np_(out), np_(lse)
     ref_o, ref_l = oracle.sparse_mla_batch(bits(q), oracle.Cache(bits(lat)), idx.numpy(), scale)
+    for b in range(B):
+        check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0])
+
+
+@pytest.mark.parametrize("H", [128, 64])
+def test_sparse_mla_dominant_rows_with_large_values(H):
+    """Rows that dominate a head's softmax and carry values up to about 17, through a launch of
+    16 splits per query token: the output is then about that row. P is rounded to bf16 for PV;
+    normalising by the sum of the rounded weights makes a dominant token's rounding cancel, and
+    fp32 split partials keep the combine exact, so the fixed bars hold at this scale. One planted
+    row opens its split (no second pass), two sit in later steps (second pass), and one split
+    starts with a masked step."""
+    gen = torch.Generator().manual_seed(15)
+    B, L, k = 3, 4096, 2048
+    scale = 1.0 / 576 ** 0.5
+    q = torch.randn((B, 1, H, 576), generator=gen).to(torch.bfloat16)
+    lat = torch.randn((B, L, 576), generator=gen).to(torch.bfloat16)
+    idx = torch.arange(k, dtype=torch.int32).repeat(B, 1, 1)
+    lat[0, 1920] = (5 * q[0, 0, 3].float()).to(torch.bfloat16)    # head 3: logit ~ 120, first token of a split
+    lat[1, 2040] = (5 * q[1, 0, 5].float()).to(torch.bfloat16)    # head 5: logit ~ 120, last step of a split
+    lat[2, 1000] = (4 * q[2, 0, 1].float()).to(torch.bfloat16)    # head 1: logit ~ 96, a middle split
+    idx[2, 0, :40] = -1                                            # first step of split 0 masked
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    # 16 splits per query token: the workspace holds 16 fp32 partials of every head of all 3 tokens
+    assert dsa.workspace_size(dsa.OP_SPARSE_MLA, B, 1, L, H=H, k=k) >= B * 16 * H * 512 * 4
+    out, lse = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(lat.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L)
+    out, lse = np_(out), np_(lse)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(q), oracle.Cache(bits(lat)), idx.numpy(), scale)
+    for b, h in ((0, 3), (1, 5), (2, 1)):
+        assert float(np.abs(ref_o[b, 0, h]).max()) >= 10.0, (b, h)
     for b in range(B):
         check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0])
 
@@ -435,12 +508,11 @@ def test_sparse_mla_fp8_logit_jumps_after_the_first_step(H):
     assert torch.equal(out, ob) and torch.equal(lse, lb)
     out, lse = np_(out), np_(lse)
     ref_o, ref_l = oracle.sparse_mla_batch(bits(q), oracle.Cache(codes.numpy()), idx.numpy(), scale, latent_scale=1.0)
+    # the planted rows dominate their heads, whose outputs reach about 10-16, far beyond the
+    # workloads' scale (about 0.04 RMS); the bars stay the fixed ones
+    assert float(np.abs(ref_o[1, 0, 5]).max()) >= 8.0
     for b in range(B):
-        # The planted rows carry values up to about 18, and heads they dominate have outputs of that
-        # size, far beyond the workloads' (about 0.04 RMS). P and the split partials are bf16, each
-        # within 2^-9 relative, so the absolute bar scales with the output: 2^-8 of its largest value.
-        bar = max(MLA_MAX_ABS, 2.0 ** -8 * float(np.abs(ref_o[b, 0]).max()))
-        check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0], max_abs_bar=bar)
+        check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0])
 
 
 def test_sparse_mla_fp8_shared_index_row_and_empty_sets():
