@@ -149,6 +149,26 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                               float softmax_scale, float* const* out, float* const* lse,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_forward_shared for callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, and harnesses that forbid hipMalloc. Same arguments, results
+ * and errors as dsa_forward_shared, without the workspace: the call uses a scratch array that the
+ * library holds in device memory, DSA_NOALLOC_SCRATCH_BYTES (128 MiB) on each GPU it runs on,
+ * from that GPU's first call until the process ends. It covers, for example, decode at B = 32
+ * and 128K tokens (82 MiB), the 8-position verification batch at B = 64 and 32K (96 MiB) and
+ * one layer at B = 8 and 1M tokens (65 MiB). A call whose dsa_workspace_size(
+ * DSA_OP_FORWARD_SHARED, ...) exceeds it returns DSA_ERR_UNSUPPORTED and launches nothing.
+ * The call itself allocates nothing and calls no allocating routine. Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (on different streams, or from
+ * different host threads) race and give undefined results; serialise them. The scratch keeps the
+ * last call's contents; no result depends on them. The GPU is the one that owns `stream` (the
+ * current device for the NULL stream). */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                                      const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                                      const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                                      float softmax_scale, float* const* out, float* const* lse,
+                                      int32_t* idx_out, void* stream);
+
 /* HiSparse hot buffer ("GLM-5.2 inference deployment" page, HiSparse section: a GPU hot
  * buffer over the KV cache kept whole in pinned host memory, driven by the step's top-K; one
  * slot per KV page; the page gives 4096-6144 device slots and 8-10x that in host memory).

@@ -19,7 +19,7 @@ OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED, OP_HISPARSE_SWAP_IN =
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-           "dsa_hisparse_swap_in",
+           "dsa_forward_shared_noalloc", "dsa_hisparse_swap_in",
            "dsa_workspace_size", "dsa_status_str", "dsa_last_error")
 
 
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_sparse_mla_fwd_fp8.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), F, P, I, I, F, P, P, P, S, P]
     lib.dsa_forward_shared.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
+    lib.dsa_forward_shared_noalloc.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
+                                               C.POINTER(CacheT), F, P, P, P, P]
     lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, P, S, P]
     lib.dsa_workspace_size.argtypes = [I, C.POINTER(BatchT), I, I, I, I]
     lib.dsa_workspace_size.restype = S
@@ -69,7 +71,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = C.c_char_p
     for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-                 "dsa_hisparse_swap_in"):
+                 "dsa_forward_shared_noalloc", "dsa_hisparse_swap_in"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -214,6 +216,29 @@ def forward_shared(q_idx, w, keys: Cache, k: int, q_mla: Sequence, latents: Sequ
     _check(lib().dsa_forward_shared(C.byref(bt), q_idx.data_ptr(), w.data_ptr(), Hi, C.byref(kc), k,
                                     int(share_first_query), nl, qs, H, lats, float(scale), os_, ls, idx.data_ptr(),
                                     _ptr(ws), n, _stream(stream)))
+    return idx, list(zip(outs, lses))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20     # DSA_NOALLOC_SCRATCH_BYTES
+
+
+def forward_shared_noalloc(q_idx, w, keys: Cache, k: int, q_mla: Sequence, latents: Sequence[Cache], scale: float,
+                           seq_lens, L_max: int, outs: List, lses: List, idx, share_first_query: bool = False,
+                           q_pos=None, stream=None):
+    """forward_shared without a workspace: the library's own per-device scratch serves the call,
+    which allocates nothing (outputs are the caller's: outs, lses, idx must be given)."""
+    B, Q, Hi = q_idx.shape[:3]
+    H = q_mla[0].shape[2]
+    nl = len(q_mla)
+    bt = batch_t(B, Q, L_max, seq_lens, q_pos)
+    qs = (C.c_void_p * nl)(*[t.data_ptr() for t in q_mla])
+    lats = (CacheT * nl)(*[c.c() for c in latents])
+    os_ = (C.c_void_p * nl)(*[t.data_ptr() for t in outs])
+    ls = (C.c_void_p * nl)(*[(t.data_ptr() if t is not None else None) for t in lses])
+    kc = keys.c()
+    _check(lib().dsa_forward_shared_noalloc(C.byref(bt), q_idx.data_ptr(), w.data_ptr(), Hi, C.byref(kc), k,
+                                            int(share_first_query), nl, qs, H, lats, float(scale), os_, ls,
+                                            idx.data_ptr(), _stream(stream)))
     return idx, list(zip(outs, lses))
 
 

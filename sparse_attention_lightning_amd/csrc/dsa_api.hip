@@ -8,10 +8,19 @@
 #include <vector>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/dsa.h"
 #include "dsa_launch.h"
+
+// Scratch of the allocation-free entry point (dsa_forward_shared_noalloc): every GPU the library
+// runs on holds one copy of this array until the process ends. Host code never passes the name
+// itself to a kernel or copy: in host code it is a stand-in, not a device address. The device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+constexpr size_t kScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -91,6 +100,36 @@ dsa_status launched(hipError_t e, const char* who) {
   } while (0)
 
 size_t scores_bytes(int rows, int L_max) { return align256((size_t)rows * L_max * sizeof(float)); }
+
+// Device address of `scratch` on the GPU that owns `stream` (the current device for the NULL
+// stream), looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_for_stream(hipStream_t stream, void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: device of the stream: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "%s: device %d beyond %d", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(DSA_ERR_HIP, "%s: hipSetDevice(%d): %s", who, dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    if (e2 != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipSetDevice(%d): %s", who, cur, hipGetErrorString(e2));
+    if (!p || !aligned(p, 256)) return fail(DSA_ERR_HIP, "%s: scratch address %p not 256-byte aligned", who, p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
 
 }  // namespace
 
@@ -202,12 +241,16 @@ dsa_status dsa_sparse_mla_fwd_fp8(const dsa_batch_t* batch, const uint16_t* q, i
                   who);
 }
 
-dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
-                              const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
-                              const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,
-                              float* const* out, float* const* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
-                              void* stream) {
-  const char* who = "dsa_forward_shared";
+}  // extern "C"
+
+namespace {
+
+// Argument checks of an IndexShare group call (everything but the workspace).
+dsa_status check_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                                const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                                const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                                float softmax_scale, float* const* out, float* const* lse, int32_t* idx_out,
+                                const char* who) {
   TRY(check_batch(batch, who));
   if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
   if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
@@ -228,22 +271,24 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
     TRY(check_cache(&latents[l], batch->L_max, who, "latent"));
     if (lse && lse[l] && !aligned(lse[l], 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse[%d] misaligned", who, l);
   }
-  const size_t need = dsa_workspace_size(DSA_OP_FORWARD_SHARED, batch, Hi, H, k, n_layers);
-  TRY(check_ws(ws, ws_bytes, need, who));
-  g_last_error.clear();
+  return DSA_OK;
+}
 
-  const hipStream_t s = (hipStream_t)stream;
+// The launches of an IndexShare group call on a checked workspace of the required size.
+dsa_status run_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                              const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                              const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,
+                              float* const* out, float* const* lse, int32_t* idx_out, void* ws, hipStream_t s,
+                              const char* who) {
   const int rows_all = batch->B * batch->Q;
   dsa::HostBatch sel = host_batch(batch);          // the query tokens that get scores + top-k
   if (share_first_query) sel.Q = 1;                // token 0 of each sequence; inputs keep stride Q
-  const int rows_sel = batch->B * sel.Q;
   char* p = (char*)ws;
   float* scores = (float*)p;
   p += scores_bytes(rows_all, batch->L_max);
   void* topk_ws = p;
   p += align256(dsa::topk_workspace_bytes(rows_all, batch->L_max));
   void* mla_ws = p;
-  (void)rows_sel;
 
   TRY(launched(dsa::launch_index_score(sel, q_e4m3, w, Hi, host_cache(keys), scores, s), who));
   TRY(launched(dsa::launch_topk(sel, scores, k, idx_out, topk_ws, s), who));
@@ -259,6 +304,46 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                                              softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
                who));
   return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                              const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                              const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,
+                              float* const* out, float* const* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* who = "dsa_forward_shared";
+  TRY(check_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                           softmax_scale, out, lse, idx_out, who));
+  const size_t need = dsa_workspace_size(DSA_OP_FORWARD_SHARED, batch, Hi, H, k, n_layers);
+  TRY(check_ws(ws, ws_bytes, need, who));
+  g_last_error.clear();
+  return run_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                            softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream, who);
+}
+
+dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                                      const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                                      const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                                      float softmax_scale, float* const* out, float* const* lse, int32_t* idx_out,
+                                      void* stream) {
+  const char* who = "dsa_forward_shared_noalloc";
+  TRY(check_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                           softmax_scale, out, lse, idx_out, who));
+  const size_t need = dsa_workspace_size(DSA_OP_FORWARD_SHARED, batch, Hi, H, k, n_layers);
+  if (need > kScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "%s: this call needs %zu bytes of scratch, above the %zu bytes the library holds per device; "
+                "call dsa_forward_shared with a workspace of dsa_workspace_size(DSA_OP_FORWARD_SHARED, ...) bytes",
+                who, need, kScratchBytes);
+  void* ws = nullptr;
+  TRY(scratch_for_stream((hipStream_t)stream, &ws, who));
+  g_last_error.clear();
+  return run_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                            softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream, who);
 }
 
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,

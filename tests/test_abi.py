@@ -155,6 +155,36 @@ def test_forward_shared_rejects():
     assert call(n=need - 1) == WORKSPACE
 
 
+def test_forward_shared_noalloc_rejects_before_hip():
+    """The allocation-free group call checks its arguments as dsa_forward_shared does, and refuses
+    a call whose workspace would not fit the library's scratch, all before any HIP call."""
+    lib = dsa.lib()
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    assert "#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert dsa.NOALLOC_SCRATCH_BYTES == 128 << 20
+    kc = cache()
+    lat = (CacheT * 4)(*[cache() for _ in range(4)])
+    ptrs = (C.c_void_p * 4)(A, A, A, A)
+
+    def call(bt, nl=4, share=0, Hi=64, H=128, scale=0.04, outs=ptrs):
+        return lib.dsa_forward_shared_noalloc(C.byref(bt), A, A, Hi, C.byref(kc), 2048, share, nl, ptrs, H, lat,
+                                              scale, outs, None, A, None)
+    # 8 sequences of 1M tokens over 4 layers need about 161 MiB of workspace
+    big = batch(B=8, L=1 << 20)
+    assert dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=4) > dsa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == UNSUPPORTED
+    assert "scratch" in dsa.lib().dsa_last_error().decode()
+    ok = batch(B=1, L=8192)
+    assert call(ok, share=2) == INVALID
+    assert call(ok, nl=0) == INVALID
+    assert call(ok, Hi=16) == UNSUPPORTED
+    assert call(ok, H=32) == UNSUPPORTED
+    assert call(ok, scale=-1.0) == INVALID
+    assert call(ok, outs=(C.c_void_p * 4)(A, A, None, A)) == INVALID
+    assert call(batch(B=0)) == INVALID
+    assert dsa.lib().dsa_last_error().decode().startswith("dsa_forward_shared_noalloc")
+
+
 def test_workspace_sizes_scale_with_batch():
     small = dsa.workspace_size(dsa.OP_TOPK, 1, 1, 8192)
     big = dsa.workspace_size(dsa.OP_TOPK, 32, 1, 131072)
