@@ -35,34 +35,73 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="independent input batches cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-index", action="store_true",
+                    help="skip the prefill indexer figure timed after the decode workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
 def index_work(wl):
-    """Algorithmic bytes and FLOPs of one index-score launch (every key read once per sequence)."""
+    """Algorithmic bytes and FLOPs of one index-score launch (every visible key read once per
+    sequence; with compressed attention the keys are the visible compressed entries)."""
     B, Q, Hi = wl.B, wl.Q, wl.Hi
     rows = 1 if wl.share_first_query else Q
-    keys = sum(wl.lens) * 128
-    scores = B * rows * wl.lmax * 4
+    keys = sum(wl.n_visible(n) for n in wl.lens) * 128
+    scores = B * rows * wl.rows * 4
     qw = B * rows * Hi * (128 + 4)
     table = B * wl.max_pages * 4 if wl.page_size else 0
     flops = 0
     for n in wl.lens:
         for j in range(rows):
-            flops += (n - Q + j + 1) * Hi * 128 * 2
+            flops += wl.n_visible(n, j) * Hi * 128 * 2
     return keys + scores + qw + table, flops
 
 
 def mla_work(wl):
-    """Algorithmic bytes and FLOPs of one sparse-MLA launch (rows gathered once per query token)."""
+    """Algorithmic bytes and FLOPs of one sparse-MLA call (rows gathered once per query token);
+    with compressed attention: the selected compressed rows and the window's raw rows, and the
+    merge of the two partial attentions."""
     rows = wl.B * wl.Q
-    sel = sum(min(wl.k, n - wl.Q + j + 1) for n in wl.lens for j in range(wl.Q))
+    pos = [n - wl.Q + j for n in wl.lens for j in range(wl.Q)]
+    if wl.ratio:
+        sel = sum(min(wl.k, (p + 1) // wl.ratio) + min(wl.window, p + 1) for p in pos)
+        merge = rows * wl.H * (512 * 4 * 3 + 4 * 3) if wl.k and wl.window else 0
+        idx = rows * (wl.k + wl.window) * 4
+    else:
+        sel = sum(min(wl.k, p + 1) for p in pos)
+        merge, idx = 0, rows * wl.k * 4
     row_bytes = 576 if wl.latent_fp8 else 1152          # E4M3 codes or bf16 per latent row
-    byts = sel * row_bytes + rows * wl.H * (576 * 2 + 512 * 4 + 4) + rows * wl.k * 4
+    byts = sel * row_bytes + rows * wl.H * (576 * 2 + 512 * 4 + 4) + idx + merge
     flops = sel * wl.H * 2 * (576 + 512)
     return byts, flops
+
+
+def prefill_index_figure(dsa, synth, torch, dev, warmup=3, reps=10):
+    """FP8 matrix-core rate of the indexer on the prefill chunk (4096 query tokens appended to a
+    126976-token prefix, causal): HIP events on the launch stream around each of `reps` launches
+    of dsa_index_score after `warmup` untimed ones."""
+    wl = synth.WORKLOADS["prefill_4096_at_128k"]
+    g = synth.generate(wl, seed=0, device=dev, with_mla=False)
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    scores = torch.empty((wl.B, wl.Q, wl.lmax), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax, scores=scores, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax, scores=scores, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    _, flops = index_work(wl)
+    del g, scores
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "kernel": "index_score (multi-query form)", "us_per_launch": us,
+            "tflops": flops / us / 1e6, "peak_tflops": FP8_PEAK_TFLOPS, "frac": flops / us / 1e6 / FP8_PEAK_TFLOPS,
+            "flop_per_launch": flops, "launches": reps,
+            "note": "causal pairs x Hi x 128 x 2 FLOP over the mean event-timed launch, after the timed region"}
 
 
 def traffic_from_profile(wl_name):
@@ -108,6 +147,9 @@ def cpu_baseline(batches, wl, budget_s):
         keys = oracle.Cache(seq_rows(g.keys, g.key_table))
         lats = [oracle.Cache(r.view(np.uint16) if r.dtype == np.int16 else r)
                 for r in (seq_rows(g.latent[l], g.latent_table[l]) for l in range(len(g.latent)))]
+        if wl.ratio:
+            win = (oracle.Cache(seq_rows(g.window_latent, g.window_table).view(np.uint16))
+                   if g.window_latent is not None else oracle.Cache(np.zeros((1, 1, 576), dtype=np.uint16)))
         q_idx = g.q_idx[b].cpu().numpy()
         w = g.w[b].cpu().numpy()
         q_src = synth.draft_queries(g, wl.draft_steps) if wl.draft_steps else g.q_mla
@@ -117,6 +159,10 @@ def cpu_baseline(batches, wl, budget_s):
         t0 = time.perf_counter()
         for j in range(rows_per_seq):
             p = n - wl.Q + j
+            if wl.ratio:             # compressed sparse attention: selection, window and attention in one
+                oracle.csa.csa_one(q_idx[j], w[j], keys, lats[0], win, 0, p, wl.ratio, wl.k, wl.window, q_mla[0][j],
+                                   wl.scale, wl.rows)
+                continue
             s = oracle.index_scores(q_idx[j], w[j], keys, 0, p, wl.lmax)
             idx = oracle.select_topk(s.astype(np.float32), p, wl.k)
             users = range(wl.Q) if wl.share_first_query else [j]
@@ -156,7 +202,7 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     rows_sel = wl.B * (1 if wl.share_first_query else wl.Q)
-    scores = torch.empty((wl.B, 1 if wl.share_first_query else wl.Q, wl.lmax), dtype=torch.float32, device=dev)
+    scores = torch.empty((wl.B, 1 if wl.share_first_query else wl.Q, wl.rows), dtype=torch.float32, device=dev)
     idx = torch.empty((wl.B, scores.shape[1], wl.k), dtype=torch.int32, device=dev)
     outs = [torch.empty((wl.B, wl.Q, wl.H, 512), dtype=torch.float32, device=dev) for _ in range(wl.n_layers)]
     lses = [torch.empty((wl.B, wl.Q, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.n_layers)]
@@ -175,6 +221,24 @@ def main():
     q_pos = None
     if wl.share_first_query:   # scores + top-k for query token 0 of each sequence only
         q_pos = torch.tensor([[n - wl.Q] for n in wl.lens], dtype=torch.int32, device=dev)
+    if wl.ratio:
+        # compressed sparse attention: one dsa_csa_forward call per step. The breakdown after the
+        # timed region calls the stages separately: the scan and top-k over the compressed entries
+        # (each query at its last visible one), MLA over the selected compressed rows and over the
+        # window's raw rows (argument lists built here on the host)
+        ws_csa = torch.empty(max(1, dsa.csa_workspace_size(wl.B, wl.Q, wl.lmax, wl.H, wl.ratio, wl.k, wl.window)),
+                             dtype=torch.uint8, device=dev)
+        pos = [[n - wl.Q + j for j in range(wl.Q)] for n in wl.lens]
+        q_pos = torch.tensor([[(p + 1) // wl.ratio - 1 for p in r] for r in pos], dtype=torch.int32, device=dev)
+        if wl.window:
+            win = torch.full((wl.B, wl.Q, wl.window), -1, dtype=torch.int32)
+            for b, r in enumerate(pos):
+                for j, p in enumerate(r):
+                    lo = max(0, p - wl.window + 1)
+                    win[b, j, :p + 1 - lo] = torch.arange(lo, p + 1, dtype=torch.int32)
+            win = win.to(dev)
+        ws_win = torch.empty(max(1, dsa.workspace_size(dsa.OP_SPARSE_MLA, wl.B, wl.Q, wl.lmax, H=wl.H,
+                                                       k=max(wl.window, 1))), dtype=torch.uint8, device=dev)
     ev = {k: [] for k in ("index", "topk", "mla", "group", "swap")}
     n_all_steps = args.warmup + args.steps + 3
     if hot:
@@ -207,6 +271,8 @@ def main():
         else:
             mla_calls = [(g.q_mla[layer], lats[layer]) for layer in range(wl.n_layers)]
         prepared.append({
+            "win": (dsa.Cache(g.window_latent, g.window_table, wl.page_size) if g.window_latent is not None
+                    else None),
             "keys": dsa.Cache(g.keys, g.key_table, wl.page_size),
             "lats": lats,
             "mla_calls": mla_calls,
@@ -220,12 +286,45 @@ def main():
                            share_first_query=bool(wl.share_first_query), outs=outs, lses=lses, idx=idx_fs, ws=ws_fs,
                            stream=stream)
 
+    def csa_call(pr, g):
+        dsa.csa_forward(g.q_idx, g.w, pr["keys"], pr["lats"][0], pr["win"], wl.ratio, wl.k, wl.window, g.q_mla[0],
+                        wl.scale, g.seq_lens, wl.lmax, out=outs[0], lse=lses[0], idx=idx if wl.k else None, ws=ws_csa,
+                        stream=stream)
+
     def step(i, record):
         """One pass of the hot path. record = "index": timing events around the index scan only (an event
         record costs a few microseconds of queue time, so only every fourth timed step carries these two);
         "all": events around every stage."""
         pr = prepared[i % len(prepared)]
         g = pr["g"]
+        if wl.ratio:
+            if record == "all":
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+                e[0].record(stream)
+                if wl.k:
+                    dsa.index_score(g.q_idx, g.w, pr["keys"], g.seq_lens, wl.rows, q_pos=q_pos, scores=scores,
+                                    stream=stream)
+                e[1].record(stream)
+                if wl.k:
+                    dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
+                e[2].record(stream)
+                if wl.k:
+                    dsa.sparse_mla_fwd(g.q_mla[0], pr["lats"][0], idx, wl.k, wl.scale, g.seq_lens, wl.rows,
+                                       out=outs[0], lse=lses[0], ws=ws_mla if n_mla else None, stream=stream)
+                if wl.window:
+                    dsa.sparse_mla_fwd(g.q_mla[0], pr["win"], win, wl.window, wl.scale, g.seq_lens, wl.lmax,
+                                       out=outs[0], lse=lses[0], ws=ws_win, stream=stream)
+                e[3].record(stream)
+                e[4].record(stream)
+                csa_call(pr, g)
+                e[5].record(stream)
+                ev["index"].append((e[0], e[1]))
+                ev["topk"].append((e[1], e[2]))
+                ev["mla"].append((e[2], e[3]))
+                ev["group"].append((e[4], e[5]))
+            else:
+                csa_call(pr, g)
+            return
         if group:
             if record == "all":
                 # breakdown: index scan and top-k as separate calls, then the whole group call; the MLA
@@ -290,7 +389,11 @@ def main():
         step(args.warmup + args.steps + i, "all")
     torch.cuda.synchronize()
     avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items() if v}   # microseconds
-    if group:
+    if wl.ratio:
+        # the merge of the two partial attentions is what the one call spends beyond the stages
+        avg["merge"] = max(0.0, avg["group"] - avg["index"] - avg["topk"] - avg["mla"])
+        avg["mla"] += avg["merge"]
+    elif group:
         avg["mla"] = avg["group"] - avg["index"] - avg["topk"]
     else:
         avg["index"] = index_us
@@ -323,10 +426,13 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "L": wl.L, "page_size": wl.page_size, "k": wl.k,
                    "Hi": wl.Hi, "H": wl.H, "n_layers": wl.n_layers, "share_first_query": wl.share_first_query,
                    "draft_steps": wl.draft_steps, "hot_buffer_slots": wl.n_slots, "latent_fp8": wl.latent_fp8,
-                   "planted": wl.planted},
+                   "planted": wl.planted, "compression_ratio": wl.ratio, "window": wl.window},
         "roofline": roof,
         "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"],
-                       "note": ("one dsa_forward_shared call per timed step (all layers' MLA launched together); "
+                       "note": ("one dsa_csa_forward call per timed step; index_score, topk and sparse_mla (selected "
+                                "compressed rows and window rows, plus the merge: the call minus the stages) from "
+                                "separate calls in 3 steps after the timed region" if wl.ratio else
+                                "one dsa_forward_shared call per timed step (all layers' MLA launched together); "
                                 "index_score and topk: events around separate calls in 3 steps after the timed "
                                 "region; sparse_mla: the group call minus those two" if group else
                                 "index_score: HIP events around the scan in every fourth timed step; topk and sparse_mla: "
@@ -347,6 +453,15 @@ def main():
             "host_read_GBps": per_step * page_bytes / (avg["swap"] * 1e-6) / 1e9,
             "note": "latent pages read by the copy kernel from pinned host memory; host_read_GBps = bytes copied "
                     "per timed step / swap-in time of the breakdown steps"}
+    if not args.workload.startswith("prefill"):
+        # the decode gather: sparse MLA and its split combine, against the HBM peak
+        mla_s = avg["mla"] * 1e-6 / n_mla_calls
+        line["roofline_mla"] = {"bound": "hbm", "achieved": mbytes / mla_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": mbytes / mla_s / 1e9 / HBM_PEAK_GBS, "bytes_per_call": mbytes,
+                                "us_per_call": mla_s * 1e6,
+                                "kernel": "sparse_mla + mla_combine (latent-row gather, one call per layer or draft step)"}
+        if not args.no_prefill_index:
+            line["prefill_index"] = prefill_index_figure(dsa, synth, torch, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(batches, wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

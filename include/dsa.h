@@ -169,6 +169,35 @@ dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q
                                       float softmax_scale, float* const* out, float* const* lse,
                                       int32_t* idx_out, void* stream);
 
+/* Compressed sparse attention ("LLM architecture survey", section 2.3 DeepSeek-V4: CSA compresses
+ * the KV cache along the sequence by 4, runs DSA's sparse selection over the compressed entries
+ * (top-1024 in V4-Pro, top-512 in V4-Flash) and adds a sliding window of the last 128 raw tokens;
+ * HCA compresses by 128 and attends densely, which is this call with k >= the visible entries and
+ * window 0). The compression is a learned map of the model: the compressed caches are inputs.
+ * For query token (b, j) at raw position p:
+ *   - compressed entry c summarises raw tokens ratio*c .. ratio*c + ratio - 1 and is visible once
+ *     its last raw token is: the first n_c = (p + 1) / ratio entries (none before a block is full);
+ *   - lightning-indexer scores of the query (q_e4m3, w, Hi as in dsa_index_score) against those
+ *     n_c compressed keys, and the k best of them as in dsa_topk -> idx_out [B][Q][k] (entry ids,
+ *     ascending, -1 padded);
+ *   - the window: raw tokens max(0, p - window + 1) .. p of the raw latent cache;
+ *   - one MQA-mode softmax (as in dsa_sparse_mla_fwd: q_bf16 [B][Q][H][576], softmax_scale) over
+ *     the selected compressed latent rows and the window's raw rows together; a raw token in the
+ *     window and its compressed block both count. out [B][Q][H][512], lse [B][Q][H] or NULL.
+ * Caches: keys_c (128-byte e4m3 rows) and latent_c (576-bf16 rows) hold L_c = ceil(L_max / ratio)
+ * rows per sequence (contiguous [B][L_c][D] or paged with their own block table and max_pages >=
+ * ceil(L_c / page_size)); latent is the raw latent cache of L_max rows per sequence. Only the
+ * window's raw rows are read.
+ * 1 <= ratio <= L_max; 0 <= k <= 2048; 0 <= window <= 2048, not both 0. With k = 0 (a sliding
+ * window only) q_e4m3, w, keys_c, latent_c and idx_out are not read; with window = 0, latent is not.
+ * ws: dsa_csa_workspace_size(batch, H, ratio, k, window) bytes, 256-byte aligned (0 when the
+ * arguments are out of range). */
+size_t dsa_csa_workspace_size(const dsa_batch_t* batch, int H, int ratio, int k, int window);
+dsa_status dsa_csa_forward(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                           const dsa_cache_t* keys_c, const dsa_cache_t* latent_c, const dsa_cache_t* latent,
+                           int ratio, int k, int window, const uint16_t* q_bf16, int H, float softmax_scale,
+                           float* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
 /* HiSparse hot buffer ("GLM-5.2 inference deployment" page, HiSparse section: a GPU hot
  * buffer over the KV cache kept whole in pinned host memory, driven by the step's top-K; one
  * slot per KV page; the page gives 4096-6144 device slots and 8-10x that in host memory).

@@ -7,5 +7,5 @@ kernels of libdsa.so; this package only marshals torch tensors into the C ABI.
 """
 from ._binding import (Cache, DsaError, EXPORTS, HotBuffer, LIB_PATH, OP_FORWARD_SHARED,  # noqa: F401
                        NOALLOC_SCRATCH_BYTES, OP_HISPARSE_SWAP_IN, OP_INDEX_SCORE, OP_SPARSE_MLA, OP_TOPK,
-                       forward_shared, forward_shared_noalloc,
+                       csa_forward, csa_workspace_size, forward_shared, forward_shared_noalloc,
                        hisparse_swap_in, index_score, lib, load_library, sparse_mla_fwd, topk, workspace_size)

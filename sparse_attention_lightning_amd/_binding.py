@@ -19,7 +19,7 @@ OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED, OP_HISPARSE_SWAP_IN =
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-           "dsa_forward_shared_noalloc", "dsa_hisparse_swap_in",
+           "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_csa_workspace_size", "dsa_hisparse_swap_in",
            "dsa_workspace_size", "dsa_status_str", "dsa_last_error")
 
 
@@ -63,6 +63,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
     lib.dsa_forward_shared_noalloc.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                                C.POINTER(CacheT), F, P, P, P, P]
+    lib.dsa_csa_forward.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), C.POINTER(CacheT),
+                                    C.POINTER(CacheT), I, I, I, P, I, F, P, P, P, P, S, P]
+    lib.dsa_csa_workspace_size.argtypes = [C.POINTER(BatchT), I, I, I, I]
+    lib.dsa_csa_workspace_size.restype = S
     lib.dsa_hisparse_swap_in.argtypes = [I, P, I, I, I, C.POINTER(HotBufferT), P, P, P, P, S, P]
     lib.dsa_workspace_size.argtypes = [I, C.POINTER(BatchT), I, I, I, I]
     lib.dsa_workspace_size.restype = S
@@ -71,7 +75,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = C.c_char_p
     for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-                 "dsa_forward_shared_noalloc", "dsa_hisparse_swap_in"):
+                 "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_hisparse_swap_in"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -240,6 +244,40 @@ def forward_shared_noalloc(q_idx, w, keys: Cache, k: int, q_mla: Sequence, laten
                                             int(share_first_query), nl, qs, H, lats, float(scale), os_, ls,
                                             idx.data_ptr(), _stream(stream)))
     return idx, list(zip(outs, lses))
+
+
+def csa_workspace_size(B: int, Q: int, L_max: int, H: int, ratio: int, k: int, window: int) -> int:
+    bt = BatchT(B, Q, L_max, None, None)
+    return lib().dsa_csa_workspace_size(C.byref(bt), H, ratio, k, window)
+
+
+def csa_forward(q_idx, w, keys_c: Optional[Cache], latent_c: Optional[Cache], latent: Optional[Cache], ratio: int,
+                k: int, window: int, q_mla, scale: float, seq_lens, L_max: int, q_pos=None, out=None, lse=None,
+                idx=None, ws=None, stream=None):
+    """Compressed sparse attention: top-k over the compressed entries (keys_c, latent_c: ceil(L_max /
+    ratio) rows per sequence) plus a window of raw rows (latent), one softmax over both.
+    Returns (idx [B,Q,k] int32 compressed entry ids or None when k == 0, out [B,Q,H,512], lse [B,Q,H])."""
+    import torch
+    B, Q, H = q_mla.shape[:3]
+    dev = q_mla.device
+    if out is None:
+        out = torch.empty((B, Q, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    if idx is None and k > 0:
+        idx = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
+    bt = batch_t(B, Q, L_max, seq_lens, q_pos)
+    n = lib().dsa_csa_workspace_size(C.byref(bt), H, ratio, k, window)
+    ws = _workspace(n, dev, ws)
+    empty = CacheT(None, None, 0, 0)
+    kc = keys_c.c() if keys_c is not None else empty
+    lc = latent_c.c() if latent_c is not None else empty
+    lr = latent.c() if latent is not None else empty
+    Hi = q_idx.shape[2] if q_idx is not None else 64
+    _check(lib().dsa_csa_forward(C.byref(bt), _ptr(q_idx), _ptr(w), Hi, C.byref(kc), C.byref(lc), C.byref(lr), ratio, k,
+                                 window, q_mla.data_ptr(), H, float(scale), out.data_ptr(), _ptr(lse), _ptr(idx),
+                                 _ptr(ws), n, _stream(stream)))
+    return idx, out, lse
 
 
 @dataclass

@@ -346,6 +346,49 @@ dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q
                             softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream, who);
 }
 
+size_t dsa_csa_workspace_size(const dsa_batch_t* bt, int H, int ratio, int k, int window) {
+  if (!bt || bt->B < 1 || bt->Q < 1 || bt->L_max < 1 || (H != 64 && H != 128) || ratio < 1 || k < 0 || window < 0 ||
+      k > kMaxTopK || window > kMaxTopK || (k == 0 && window == 0))
+    return 0;
+  return dsa::csa_workspace_bytes(bt->B, bt->Q, bt->L_max, H, ratio, k, window);
+}
+
+dsa_status dsa_csa_forward(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                           const dsa_cache_t* keys_c, const dsa_cache_t* latent_c, const dsa_cache_t* latent,
+                           int ratio, int k, int window, const uint16_t* q_bf16, int H, float softmax_scale,
+                           float* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "dsa_csa_forward";
+  TRY(check_batch(batch, who));
+  if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
+  if (ratio < 1 || ratio > batch->L_max) return fail(DSA_ERR_INVALID_ARG, "%s: ratio=%d outside [1, L_max]", who, ratio);
+  if (k < 0 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [0, %d]", who, k, kMaxTopK);
+  if (window < 0 || window > kMaxTopK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: window=%d outside [0, %d]", who, window, kMaxTopK);
+  if (k == 0 && window == 0) return fail(DSA_ERR_INVALID_ARG, "%s: k and window are both 0: nothing to attend", who);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(DSA_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0", who);
+  TRY(check_ptr(q_bf16, 16, who, "q_bf16"));
+  TRY(check_ptr(out, 16, who, "out"));
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse misaligned", who);
+  const int Lc_max = (batch->L_max + ratio - 1) / ratio;
+  if (k > 0) {
+    if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
+    TRY(check_ptr(q_e4m3, 16, who, "q_e4m3"));
+    TRY(check_ptr(w, 4, who, "w"));
+    TRY(check_ptr(idx_out, 4, who, "idx_out"));
+    TRY(check_cache(keys_c, Lc_max, who, "compressed keys"));
+    TRY(check_cache(latent_c, Lc_max, who, "compressed latent"));
+  }
+  if (window > 0) TRY(check_cache(latent, batch->L_max, who, "latent"));
+  TRY(check_ws(ws, ws_bytes, dsa::csa_workspace_bytes(batch->B, batch->Q, batch->L_max, H, ratio, k, window), who));
+  g_last_error.clear();
+  const dsa::HostCache none{nullptr, nullptr, 0, 0};
+  return launched(dsa::launch_csa(host_batch(batch), q_e4m3, w, Hi, k > 0 ? host_cache(keys_c) : none,
+                                  k > 0 ? host_cache(latent_c) : none, window > 0 ? host_cache(latent) : none, ratio,
+                                  k, window, q_bf16, H, softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream),
+                  who);
+}
+
 dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, int k, int32_t step,
                                 const dsa_hot_buffer_t* hb, const void* host_pool, void* device_pool,
                                 int32_t* copied, void* ws, size_t ws_bytes, void* stream) {

@@ -43,6 +43,14 @@ hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* 
                                     const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
                                     float* const* lse, int n_layers, void* ws, hipStream_t s);
 
+// Compressed sparse attention: the DSA kernels over compressed caches plus a raw sliding window,
+// merged by log-sum-exp. Workspace layout owned by csa.hip.
+size_t csa_workspace_bytes(int B, int Q, int L_max, int H, int ratio, int k, int window);
+hipError_t launch_csa(const HostBatch& bt, const uint8_t* q_e4m3, const float* w, int Hi, const HostCache& keys_c,
+                      const HostCache& latent_c, const HostCache& latent, int ratio, int k, int window,
+                      const uint16_t* q_bf16, int H, float scale, float* out, float* lse, int32_t* idx_out, void* ws,
+                      hipStream_t s);
+
 // HiSparse hot buffer: top-k driven swap-in of latent pages from a host pool into per-sequence
 // device slots. Workspace: the copy list (page, slot) of every sequence and its length.
 struct HostHotBuffer {

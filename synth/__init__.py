@@ -35,6 +35,7 @@ DV = 512        # value part of the latent row
 # generator streams
 S_QIDX, S_KEYS, S_W, S_QMLA, S_LATENT, S_TABLE, S_PLANT_POS, S_PLANT_NOISE, S_DRIFT, S_DRAFT = (1, 2, 3, 4, 5, 6, 7, 8,
                                                                                           9, 10)
+S_WINDOW, S_WINDOW_TABLE = 11, 12
 
 
 @dataclass(frozen=True)
@@ -63,6 +64,9 @@ class Workload:
     drift_heads: int = 0                 # indexer query heads redrawn from one decode step to the next
     draft_steps: int = 0                 # > 0: an MTP draft loop of this many sequential steps per index set
     latent_fp8: int = 0                  # 1: latent rows as 576 E4M3FN codes (uint8) instead of bf16
+    ratio: int = 0                       # > 0: compressed sparse attention; keys and latent rows are compressed
+                                         # entries, one per `ratio` raw tokens (ceil(L_max / ratio) per sequence)
+    window: int = 0                      # raw tokens of the sliding window (compressed sparse attention)
 
     @property
     def lmax(self) -> int:
@@ -77,8 +81,24 @@ class Workload:
         return 1.0 / math.sqrt(DQK)
 
     @property
+    def rows(self) -> int:
+        """Rows per sequence of the key and latent caches: raw tokens, or compressed entries."""
+        return -(-self.lmax // self.ratio) if self.ratio else self.lmax
+
+    @property
     def max_pages(self) -> int:
+        """Pages per sequence of the key and latent caches."""
+        return -(-self.rows // self.page_size) if self.page_size else 0
+
+    @property
+    def max_pages_raw(self) -> int:
+        """Pages per sequence of the raw latent cache that a sliding window reads."""
         return -(-self.lmax // self.page_size) if self.page_size else 0
+
+    def n_visible(self, n: int, j: int = None) -> int:
+        """Rows of a sequence of n raw tokens visible to its query token j (the last by default)."""
+        p = n - self.Q + (self.Q - 1 if j is None else j)
+        return (p + 1) // self.ratio if self.ratio else p + 1
 
 
 # The five workloads of the DSA hot path, at full size.
@@ -108,6 +128,15 @@ WORKLOADS = {
                                             planted=32, latent_fp8=1),
     "mtp_draft_b32_128k_paged": Workload("mtp_draft_b32_128k_paged", B=32, Q=1, L=131072, page_size=64,
                                          planted=32, draft_steps=7),
+    # Compressed sparse attention (architecture survey, DeepSeek-V4): compressed entries of 4 raw
+    # tokens (keys and latent rows drawn like the uncompressed ones; the compression map is the
+    # model's), top-1024 (V4-Pro) or top-512 (V4-Flash) of them, and a 128-token raw window.
+    "csa_pro_decode_b32_128k": Workload("csa_pro_decode_b32_128k", B=32, Q=1, L=131072, page_size=64, planted=32,
+                                        k=1024, ratio=4, window=128),
+    "csa_flash_decode_b8_1m": Workload("csa_flash_decode_b8_1m", B=8, Q=1, L=1048576, page_size=64, planted=32,
+                                       k=512, ratio=4, window=128),
+    # HCA: compressed by 128, dense attention over every visible compressed entry, no window.
+    "hca_decode_b32_128k": Workload("hca_decode_b32_128k", B=32, Q=1, L=131072, page_size=64, k=1024, ratio=128),
 }
 
 
@@ -148,6 +177,12 @@ def block_table(wl: Workload, seed: int, layer: int, device) -> torch.Tensor:
 def cache_shape(wl: Workload, dim: int):
     if wl.page_size:
         return (wl.B * wl.max_pages, wl.page_size, dim)
+    return (wl.B, wl.rows, dim)
+
+
+def raw_cache_shape(wl: Workload, dim: int):
+    if wl.page_size:
+        return (wl.B * wl.max_pages_raw, wl.page_size, dim)
     return (wl.B, wl.lmax, dim)
 
 
@@ -162,13 +197,16 @@ class Batch:
     q_mla: List[torch.Tensor] = field(default_factory=list)     # per layer [B, Q, H, 576] bf16
     latent: List[torch.Tensor] = field(default_factory=list)    # per layer contiguous or pool, bf16
     latent_table: List[Optional[torch.Tensor]] = field(default_factory=list)
-    planted_pos: Optional[torch.Tensor] = None                   # [B, planted] int64
+    planted_pos: Optional[torch.Tensor] = None                   # [B, planted] int64 (rows of the key cache)
+    window_latent: Optional[torch.Tensor] = None                 # compressed attention: the raw latent cache
+    window_table: Optional[torch.Tensor] = None                  # [B, max_pages_raw] int32 or None
 
     def to(self, device) -> "Batch":
         mv = lambda t: None if t is None else t.to(device)
         return Batch(self.wl, mv(self.seq_lens), mv(self.q_idx), mv(self.w), mv(self.keys), mv(self.key_table),
                      [mv(t) for t in self.q_mla], [mv(t) for t in self.latent],
-                     [mv(t) for t in self.latent_table], mv(self.planted_pos))
+                     [mv(t) for t in self.latent_table], mv(self.planted_pos), mv(self.window_latent),
+                     mv(self.window_table))
 
 
 def token_slot(table: Optional[torch.Tensor], page_size: int, b: int, t: torch.Tensor):
@@ -197,7 +235,7 @@ def generate(wl: Workload, seed: int = 0, device="cpu", layers: Optional[int] = 
 
     if wl.planted:
         gp = _gen(seed, S_PLANT_POS, 0, "cpu")
-        pos = torch.stack([torch.randperm(wl.lens[b], generator=gp)[: wl.planted] for b in range(wl.B)])
+        pos = torch.stack([torch.randperm(wl.n_visible(wl.lens[b]), generator=gp)[: wl.planted] for b in range(wl.B)])
         batch.planted_pos = pos.to(dev)
         # key = e4m3(2 * g_hat + 0.25 * eps) with g = sum_h w_h q_h (query token 0), |g_hat| = sqrt(128)
         qd = q_idx[:, 0].view(torch.float8_e4m3fn).to(torch.float32)          # [B, Hi, 128]
@@ -221,6 +259,12 @@ def generate(wl: Workload, seed: int = 0, device="cpu", layers: Optional[int] = 
                 batch.latent_table.append(key_table if layer == 0 else block_table(wl, s, layer, dev))
             else:
                 batch.latent_table.append(None)
+        if wl.ratio and wl.window:
+            batch.window_latent = bf16_normal(raw_cache_shape(wl, DQK), _gen(seed, S_WINDOW, 0, dev), dev)
+            if wl.page_size:
+                n_pages = wl.B * wl.max_pages_raw
+                perm = torch.randperm(n_pages, generator=_gen(seed, S_WINDOW_TABLE, 0, "cpu"), dtype=torch.int64)
+                batch.window_table = perm.to(torch.int32).view(wl.B, wl.max_pages_raw).to(dev)
     return batch
 
 
