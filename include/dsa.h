@@ -190,6 +190,8 @@ dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q
  * window's raw rows are read.
  * 1 <= ratio <= L_max; 0 <= k <= 2048; 0 <= window <= 2048, not both 0. With k = 0 (a sliding
  * window only) q_e4m3, w, keys_c, latent_c and idx_out are not read; with window = 0, latent is not.
+ * With k >= L_c every visible entry is selected whatever its score, so the scores are not computed
+ * (q_e4m3, w and keys_c are then not read; HCA).
  * ws: dsa_csa_workspace_size(batch, H, ratio, k, window) bytes, 256-byte aligned (0 when the
  * arguments are out of range). */
 size_t dsa_csa_workspace_size(const dsa_batch_t* batch, int H, int ratio, int k, int window);

@@ -19,14 +19,21 @@
 
 namespace dsa {
 
+// idx_all (when k covers every compressed row a sequence can have): the selection keeps every
+// visible entry whatever the scores, so it is written directly, 0 .. n_c - 1 then -1, and the
+// scan and top-k are skipped.
 __global__ __launch_bounds__(256) void csa_prep_kernel(const int32_t* __restrict__ seq_lens,
                                                        const int32_t* __restrict__ q_pos, int Q, int ratio,
-                                                       int window, int32_t* __restrict__ qpos_c,
-                                                       int32_t* __restrict__ idx_w) {
+                                                       int window, int k, int32_t* __restrict__ qpos_c,
+                                                       int32_t* __restrict__ idx_w, int32_t* __restrict__ idx_all) {
   const int row = blockIdx.x;
   const int b = row / Q, j = row - b * Q;
   const int p = query_pos(seq_lens, q_pos, Q, b, j);
   if (threadIdx.x == 0 && qpos_c) qpos_c[row] = (p + 1) / ratio - 1;
+  if (idx_all) {
+    const int n_c = (p + 1) / ratio;
+    for (int i = threadIdx.x; i < k; i += blockDim.x) idx_all[(int64_t)row * k + i] = i < n_c ? i : -1;
+  }
   if (idx_w) {
     const int start = max(0, p - window + 1);
     const int cnt = p - start + 1;
@@ -74,7 +81,7 @@ static CsaWs csa_carve(void* ws, int rows, int Lc_max, int H, int k, int window,
   CsaWs w{};
   char* p = (char*)ws;
   auto take = [&](size_t n) { char* q = p; p += a256(n); return (void*)q; };
-  if (k > 0) {
+  if (k > 0 && k < Lc_max) {                         // a selection that needs the scores
     w.scores = (float*)take((size_t)rows * Lc_max * sizeof(float));
     w.topk = take(topk_workspace_bytes(rows, Lc_max));
     w.qpos_c = (int32_t*)take((size_t)rows * sizeof(int32_t));
@@ -108,8 +115,9 @@ hipError_t launch_csa(const HostBatch& bt, const uint8_t* q_e4m3, const float* w
   const int Lc_max = (bt.L_max + ratio - 1) / ratio;
   size_t total = 0;
   const CsaWs W = csa_carve(ws, rows, Lc_max, H, k, window, &total);
-  hipLaunchKernelGGL(csa_prep_kernel, dim3(rows), dim3(256), 0, s, bt.seq_lens, bt.q_pos, bt.Q, ratio, window,
-                     W.qpos_c, W.idx_w);
+  const bool keep_all = k >= Lc_max;                 // e.g. HCA: every visible entry, no scores needed
+  hipLaunchKernelGGL(csa_prep_kernel, dim3(rows), dim3(256), 0, s, bt.seq_lens, bt.q_pos, bt.Q, ratio, window, k,
+                     W.qpos_c, W.idx_w, (k > 0 && keep_all) ? idx_out : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool both = k > 0 && window > 0;
@@ -117,8 +125,10 @@ hipError_t launch_csa(const HostBatch& bt, const uint8_t* q_e4m3, const float* w
     // the compressed caches, addressed like any cache of Lc_max rows per sequence, with each
     // query at its last visible compressed entry
     const HostBatch bc{bt.B, bt.Q, Lc_max, bt.seq_lens, W.qpos_c, bt.Q};
-    if ((e = launch_index_score(bc, q_e4m3, w, Hi, keys_c, W.scores, s)) != hipSuccess) return e;
-    if ((e = launch_topk(bc, W.scores, k, idx_out, W.topk, s)) != hipSuccess) return e;
+    if (!keep_all) {
+      if ((e = launch_index_score(bc, q_e4m3, w, Hi, keys_c, W.scores, s)) != hipSuccess) return e;
+      if ((e = launch_topk(bc, W.scores, k, idx_out, W.topk, s)) != hipSuccess) return e;
+    }
     if ((e = launch_sparse_mla(bc, q_bf16, H, latent_c, idx_out, k, k, scale, both ? W.o_c : out,
                                both ? W.lse_c : lse, W.mla, s)) != hipSuccess)
       return e;

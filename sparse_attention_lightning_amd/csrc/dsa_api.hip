@@ -372,18 +372,20 @@ dsa_status dsa_csa_forward(const dsa_batch_t* batch, const uint8_t* q_e4m3, cons
   if (lse && !aligned(lse, 4)) return fail(DSA_ERR_INVALID_ARG, "%s: lse misaligned", who);
   const int Lc_max = (batch->L_max + ratio - 1) / ratio;
   if (k > 0) {
-    if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
-    TRY(check_ptr(q_e4m3, 16, who, "q_e4m3"));
-    TRY(check_ptr(w, 4, who, "w"));
+    if (k < Lc_max) {                                // the selection reads the scores
+      if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
+      TRY(check_ptr(q_e4m3, 16, who, "q_e4m3"));
+      TRY(check_ptr(w, 4, who, "w"));
+      TRY(check_cache(keys_c, Lc_max, who, "compressed keys"));
+    }
     TRY(check_ptr(idx_out, 4, who, "idx_out"));
-    TRY(check_cache(keys_c, Lc_max, who, "compressed keys"));
     TRY(check_cache(latent_c, Lc_max, who, "compressed latent"));
   }
   if (window > 0) TRY(check_cache(latent, batch->L_max, who, "latent"));
   TRY(check_ws(ws, ws_bytes, dsa::csa_workspace_bytes(batch->B, batch->Q, batch->L_max, H, ratio, k, window), who));
   g_last_error.clear();
   const dsa::HostCache none{nullptr, nullptr, 0, 0};
-  return launched(dsa::launch_csa(host_batch(batch), q_e4m3, w, Hi, k > 0 ? host_cache(keys_c) : none,
+  return launched(dsa::launch_csa(host_batch(batch), q_e4m3, w, Hi, (k > 0 && k < Lc_max) ? host_cache(keys_c) : none,
                                   k > 0 ? host_cache(latent_c) : none, window > 0 ? host_cache(latent) : none, ratio,
                                   k, window, q_bf16, H, softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream),
                   who);

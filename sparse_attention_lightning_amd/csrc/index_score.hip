@@ -189,45 +189,68 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
     __builtin_amdgcn_s_barrier();
     // the slot of tile tt + kAhead was last read in tile tt - 1, which every wave has finished
     if (tt + kAhead < n_tiles) issue_tile(tt + kAhead);
-    const uint8_t* tile = ring[tt % kMqStages];
     const int tb = t0 + tt * kMqTile;
-    auto frag = [&](int gi) {
-      const uint8_t* gp = tile + gi * 16 * 128;
-      const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
-      return (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    };
     // Software pipeline over the tile's groups: the products of group gi + 1 share a scheduling
     // region with the epilogue of group gi (issued a full group earlier, so no epilogue
     // instruction waits on a product in flight), and B fragments are read two groups ahead.
     // Keys after pmax inside the last tile are computed on valid rows and stored as -inf.
-    v4f acc[2][MT];
-    v8i bk_next = frag(1);
-    {
-      const v8i bk0 = frag(0);
+    // An interior tile (every key at or before this wave's query and inside the chunk) stores its
+    // scores with no bound checks, from a wave-uniform base; the tile's branch is taken once.
+    auto run_tile = [&](auto interior_c, auto slot_c) {
+      constexpr bool kInterior = decltype(interior_c)::value;
+      const uint8_t* tile = ring[decltype(slot_c)::value];
+      float* const stile = srow + tb + lane;
+      auto frag = [&](int gi) {
+        const uint8_t* gp = tile + gi * 16 * 128;
+        const v4i lo4 = *(const v4i*)(gp + b_lo), hi4 = *(const v4i*)(gp + b_hi);
+        return (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      };
+      v4f acc[2][MT];
+      v8i bk_next = frag(1);
+      {
+        const v8i bk0 = frag(0);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[0][m] = mfma_fp8(qa[m], bk0, zero);
-    }
-    float part[4];
-#pragma unroll
-    for (int gi = 0; gi < kG; ++gi) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (gi + 1 < kG) {
-        const v8i bk_after = frag(gi + 2 < kG ? gi + 2 : gi + 1);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[(gi + 1) & 1][m] = mfma_fp8(qa[m], bk_next, zero);
-        bk_next = bk_after;
+        for (int m = 0; m < MT; ++m) acc[0][m] = mfma_fp8(qa[m], bk0, zero);
       }
-      float sum = 0.f;
+      float part[4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int gi = 0; gi < kG; ++gi) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (gi + 1 < kG) {
+          const v8i bk_after = frag(gi + 2 < kG ? gi + 2 : gi + 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sum += wr[m][r] * relu(acc[gi & 1][m][r]);
-      part[gi & 3] = sum;
-      if ((gi & 3) == 3) {
-        const float v = reduce_scatter4(part);        // lane 16c + j: key j of group c
-        const int tk = tb + 64 * (gi >> 2) + lane;
-        if (live && tk < t1) srow[tk] = (tk <= pq) ? v : -INFINITY;
+          for (int m = 0; m < MT; ++m) acc[(gi + 1) & 1][m] = mfma_fp8(qa[m], bk_next, zero);
+          bk_next = bk_after;
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum += wr[m][r] * relu(acc[gi & 1][m][r]);
+        part[gi & 3] = sum;
+        if ((gi & 3) == 3) {
+          const float v = reduce_scatter4(part);      // lane 16c + j: key j of group c
+          if constexpr (kInterior) {
+            stile[64 * (gi >> 2)] = v;
+          } else {
+            const int tk = tb + 64 * (gi >> 2) + lane;
+            if (live && tk < t1) srow[tk] = (tk <= pq) ? v : -INFINITY;
+          }
+        }
       }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using Yes = std::true_type;
+    using No = std::false_type;
+    static_assert(kMqStages == 2, "two ring slots");
+    const bool interior = tb + kMqTile - 1 <= pq && tb + kMqTile <= t1;     // wave-uniform
+    if (tt & 1) {
+      if (interior) run_tile(Yes{}, I1{});
+      else run_tile(No{}, I1{});
+    } else {
+      if (interior) run_tile(Yes{}, I0{});
+      else run_tile(No{}, I0{});
     }
   }
 }

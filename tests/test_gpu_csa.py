@@ -145,6 +145,22 @@ def test_csa_ratio_one_without_window_is_the_dsa_path():
     assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def test_hca_keeps_every_entry_without_indexer_inputs():
+    """When k covers every compressed row (HCA), the selection keeps every visible entry whatever
+    the scores: the call needs no indexer inputs and gives the same bits without them."""
+    wl = synth.small("hca_decode_b32_128k", B=3, L=40000, L_max=40064, seq_lens=(40000, 20000, 130), k=320)
+    g = synth.generate(wl, seed=4, device=DEV)
+    lat_c = dsa.Cache(g.latent[0], g.latent_table[0], wl.page_size)
+    idx, out, lse = run_gpu(g, wl)
+    idx2, out2, lse2 = dsa.csa_forward(None, None, None, lat_c, None, wl.ratio, wl.k, 0, g.q_mla[0], wl.scale,
+                                       g.seq_lens, wl.lmax)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(lse, lse2)
+    for b in range(wl.B):
+        n_c = wl.n_visible(wl.lens[b])
+        assert np_(idx)[b, 0].tolist() == list(range(n_c)) + [-1] * (wl.k - n_c)
+
+
 def test_csa_rejects_before_hip():
     wl = synth.small("csa_pro_decode_b32_128k", B=1, L=4096, planted=0)
     g = synth.generate(wl, seed=0, device=DEV)
