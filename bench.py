@@ -42,9 +42,17 @@ def parse():
     return ap.parse_args()
 
 
+def scan_runs(wl):
+    """Whether a step runs the indexer scan: compressed attention whose k covers every compressed
+    row (HCA) keeps every visible entry without scores."""
+    return not (wl.ratio and (wl.k == 0 or wl.k >= wl.rows))
+
+
 def index_work(wl):
     """Algorithmic bytes and FLOPs of one index-score launch (every visible key read once per
     sequence; with compressed attention the keys are the visible compressed entries)."""
+    if not scan_runs(wl):
+        return 0, 0
     B, Q, Hi = wl.B, wl.Q, wl.Hi
     rows = 1 if wl.share_first_query else Q
     keys = sum(wl.n_visible(n) for n in wl.lens) * 128
@@ -284,7 +292,7 @@ def main():
     def group_call(pr, g):
         dsa.forward_shared(g.q_idx, g.w, pr["keys"], wl.k, g.q_mla, pr["lats"], wl.scale, g.seq_lens, wl.lmax,
                            share_first_query=bool(wl.share_first_query), outs=outs, lses=lses, idx=idx_fs, ws=ws_fs,
-                           stream=stream)
+                           stream=stream, latent_scales=[1.0] * wl.n_layers if wl.latent_fp8 else None)
 
     def csa_call(pr, g):
         dsa.csa_forward(g.q_idx, g.w, pr["keys"], pr["lats"][0], pr["win"], wl.ratio, wl.k, wl.window, g.q_mla[0],
@@ -301,11 +309,11 @@ def main():
             if record == "all":
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
                 e[0].record(stream)
-                if wl.k:
+                if scan_runs(wl):
                     dsa.index_score(g.q_idx, g.w, pr["keys"], g.seq_lens, wl.rows, q_pos=q_pos, scores=scores,
                                     stream=stream)
                 e[1].record(stream)
-                if wl.k:
+                if scan_runs(wl):
                     dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
                 e[2].record(stream)
                 if wl.k:
@@ -410,14 +418,20 @@ def main():
     ibytes, iflops = index_work(wl)
     mbytes, mflops = mla_work(wl)
     index_s = avg["index"] * 1e-6
-    if args.workload.startswith("prefill"):
+    n_mla_calls = wl.draft_steps or wl.n_layers
+    if not scan_runs(wl):
+        # no scan in the step (every visible compressed entry is kept): the latent gather dominates
+        mla_s = avg["mla"] * 1e-6 / n_mla_calls
+        roof = {"bound": "hbm", "achieved": mbytes / mla_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "traffic": None, "kernel": "sparse_mla (+ combine): latent-row gather"}
+    elif args.workload.startswith("prefill"):
         roof = {"bound": "mfma", "achieved": iflops / index_s / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": ibytes / index_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profile(args.workload)
-    roof["kernel"] = "index_score (lightning indexer scan)"
-    n_mla_calls = wl.draft_steps or wl.n_layers
+    if scan_runs(wl):
+        roof["traffic"] = traffic_from_profile(args.workload)
+        roof["kernel"] = "index_score (lightning indexer scan)"
     step_bytes = ibytes + mbytes * n_mla_calls
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -438,7 +452,7 @@ def main():
                                 "index_score: HIP events around the scan in every fourth timed step; topk and sparse_mla: "
                                 "events around each stage in 3 steps after the timed region")},
         "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "index_tflops": iflops / index_s / 1e12,
+        "index_tflops": iflops / index_s / 1e12 if index_s > 0 else None,
         "mla_tflops": mflops * n_mla_calls / (avg["mla"] * 1e-6) / 1e12,
     }
     if hot:

@@ -149,13 +149,24 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                               float softmax_scale, float* const* out, float* const* lse,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_forward_shared over FP8 latent caches (the inference page's fp8_e4m3 KV-cache option next
+ * to IndexShare): latents[l] holds rows of 576 E4M3 codes whose values are latent_scales[l] x
+ * e4m3(code), as in dsa_sparse_mla_fwd_fp8; each layer then equals dsa_sparse_mla_fwd_fp8 with
+ * that scale, bit for bit. latent_scales: (host) [n_layers], each finite and > 0. Everything
+ * else (workspace included) as dsa_forward_shared. */
+dsa_status dsa_forward_shared_fp8(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                                  const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                                  const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                                  const float* latent_scales, float softmax_scale, float* const* out,
+                                  float* const* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
 /* dsa_forward_shared for callers that cannot allocate device memory: code being captured into a
  * HIP graph, tight serving loops, and harnesses that forbid hipMalloc. Same arguments, results
  * and errors as dsa_forward_shared, without the workspace: the call uses a scratch array that the
  * library holds in device memory, DSA_NOALLOC_SCRATCH_BYTES (128 MiB) on each GPU it runs on,
  * from that GPU's first call until the process ends. It covers, for example, decode at B = 32
- * and 128K tokens (82 MiB), the 8-position verification batch at B = 64 and 32K (96 MiB) and
- * one layer at B = 8 and 1M tokens (65 MiB). A call whose dsa_workspace_size(
+ * and 128K tokens (50 MiB), the 8-position verification batch at B = 64 and 32K (96 MiB) and
+ * the 4-layer group at B = 8 and 1M tokens (65 MiB). A call whose dsa_workspace_size(
  * DSA_OP_FORWARD_SHARED, ...) exceeds it returns DSA_ERR_UNSUPPORTED and launches nothing.
  * The call itself allocates nothing and calls no allocating routine. Every call on one GPU
  * shares that GPU's scratch: calls that overlap in time on one GPU (on different streams, or from

@@ -19,7 +19,7 @@ OP_INDEX_SCORE, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD_SHARED, OP_HISPARSE_SWAP_IN =
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-           "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_csa_workspace_size", "dsa_hisparse_swap_in",
+           "dsa_forward_shared_fp8", "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_csa_workspace_size", "dsa_hisparse_swap_in",
            "dsa_workspace_size", "dsa_status_str", "dsa_last_error")
 
 
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_sparse_mla_fwd_fp8.argtypes = [C.POINTER(BatchT), P, I, C.POINTER(CacheT), F, P, I, I, F, P, P, P, S, P]
     lib.dsa_forward_shared.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                        C.POINTER(CacheT), F, P, P, P, P, S, P]
+    lib.dsa_forward_shared_fp8.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
+                                           C.POINTER(CacheT), P, F, P, P, P, P, S, P]
     lib.dsa_forward_shared_noalloc.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), I, I, I, P, I,
                                                C.POINTER(CacheT), F, P, P, P, P]
     lib.dsa_csa_forward.argtypes = [C.POINTER(BatchT), P, P, I, C.POINTER(CacheT), C.POINTER(CacheT),
@@ -75,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = C.c_char_p
     for name in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_fp8", "dsa_forward_shared",
-                 "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_hisparse_swap_in"):
+                 "dsa_forward_shared_fp8", "dsa_forward_shared_noalloc", "dsa_csa_forward", "dsa_hisparse_swap_in"):
         getattr(lib, name).restype = C.c_int
     return lib
 
@@ -195,9 +197,11 @@ def sparse_mla_fwd(q, latent: Cache, idx, k: int, scale: float, seq_lens, L_max:
 
 def forward_shared(q_idx, w, keys: Cache, k: int, q_mla: Sequence, latents: Sequence[Cache], scale: float,
                    seq_lens, L_max: int, share_first_query: bool = False, q_pos=None,
-                   outs: Optional[List] = None, lses: Optional[List] = None, idx=None, ws=None, stream=None):
+                   outs: Optional[List] = None, lses: Optional[List] = None, idx=None, ws=None, stream=None,
+                   latent_scales: Optional[Sequence[float]] = None):
     """One IndexShare group: scores + top-k once, sparse MLA per layer with the same indices.
-    Returns (idx, [(out, lse) per layer])."""
+    With latent_scales (one per layer) the latent caches hold 576 E4M3 codes per row (uint8),
+    value = latent_scales[l] x code. Returns (idx, [(out, lse) per layer])."""
     import torch
     B, Q, Hi = q_idx.shape[:3]
     H = q_mla[0].shape[2]
@@ -217,9 +221,15 @@ def forward_shared(q_idx, w, keys: Cache, k: int, q_mla: Sequence, latents: Sequ
     os_ = (C.c_void_p * nl)(*[t.data_ptr() for t in outs])
     ls = (C.c_void_p * nl)(*[(t.data_ptr() if t is not None else None) for t in lses])
     kc = keys.c()
-    _check(lib().dsa_forward_shared(C.byref(bt), q_idx.data_ptr(), w.data_ptr(), Hi, C.byref(kc), k,
-                                    int(share_first_query), nl, qs, H, lats, float(scale), os_, ls, idx.data_ptr(),
-                                    _ptr(ws), n, _stream(stream)))
+    if latent_scales is None:
+        _check(lib().dsa_forward_shared(C.byref(bt), q_idx.data_ptr(), w.data_ptr(), Hi, C.byref(kc), k,
+                                        int(share_first_query), nl, qs, H, lats, float(scale), os_, ls, idx.data_ptr(),
+                                        _ptr(ws), n, _stream(stream)))
+    else:
+        sc = (C.c_float * nl)(*[float(x) for x in latent_scales])
+        _check(lib().dsa_forward_shared_fp8(C.byref(bt), q_idx.data_ptr(), w.data_ptr(), Hi, C.byref(kc), k,
+                                            int(share_first_query), nl, qs, H, lats, sc, float(scale), os_, ls,
+                                            idx.data_ptr(), _ptr(ws), n, _stream(stream)))
     return idx, list(zip(outs, lses))
 
 

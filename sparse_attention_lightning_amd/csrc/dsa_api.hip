@@ -279,7 +279,7 @@ dsa_status run_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
                               const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
                               const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents, float softmax_scale,
                               float* const* out, float* const* lse, int32_t* idx_out, void* ws, hipStream_t s,
-                              const char* who) {
+                              const char* who, const float* latent_scales = nullptr) {
   const int rows_all = batch->B * batch->Q;
   dsa::HostBatch sel = host_batch(batch);          // the query tokens that get scores + top-k
   if (share_first_query) sel.Q = 1;                // token 0 of each sequence; inputs keep stride Q
@@ -300,9 +300,14 @@ dsa_status run_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
     lse_l[l] = lse ? lse[l] : nullptr;
   }
   // all layers of the group in one launch (up to 8 at a time): they share the index set
-  TRY(launched(dsa::launch_sparse_mla_layers(host_batch(batch), q_bf16, H, lat.data(), idx_out, k, stride,
-                                             softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
-               who));
+  if (latent_scales)
+    TRY(launched(dsa::launch_sparse_mla_layers_fp8(host_batch(batch), q_bf16, H, lat.data(), latent_scales, idx_out,
+                                                   k, stride, softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
+                 who));
+  else
+    TRY(launched(dsa::launch_sparse_mla_layers(host_batch(batch), q_bf16, H, lat.data(), idx_out, k, stride,
+                                               softmax_scale, out, lse_l.data(), n_layers, mla_ws, s),
+                 who));
   return DSA_OK;
 }
 
@@ -323,6 +328,25 @@ dsa_status dsa_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3, c
   g_last_error.clear();
   return run_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
                             softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream, who);
+}
+
+dsa_status dsa_forward_shared_fp8(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,
+                                  const dsa_cache_t* keys, int k, int share_first_query, int n_layers,
+                                  const uint16_t* const* q_bf16, int H, const dsa_cache_t* latents,
+                                  const float* latent_scales, float softmax_scale, float* const* out,
+                                  float* const* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "dsa_forward_shared_fp8";
+  TRY(check_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                           softmax_scale, out, lse, idx_out, who));
+  if (!latent_scales) return fail(DSA_ERR_INVALID_ARG, "%s: latent_scales is NULL", who);
+  for (int l = 0; l < n_layers; ++l)
+    if (!std::isfinite(latent_scales[l]) || !(latent_scales[l] > 0.f))
+      return fail(DSA_ERR_INVALID_ARG, "%s: latent_scales[%d] must be finite and > 0", who, l);
+  const size_t need = dsa_workspace_size(DSA_OP_FORWARD_SHARED, batch, Hi, H, k, n_layers);
+  TRY(check_ws(ws, ws_bytes, need, who));
+  g_last_error.clear();
+  return run_forward_shared(batch, q_e4m3, w, Hi, keys, k, share_first_query, n_layers, q_bf16, H, latents,
+                            softmax_scale, out, lse, idx_out, ws, (hipStream_t)stream, who, latent_scales);
 }
 
 dsa_status dsa_forward_shared_noalloc(const dsa_batch_t* batch, const uint8_t* q_e4m3, const float* w, int Hi,

@@ -30,7 +30,7 @@ hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t*
 // Sparse MLA (MQA mode). Workspace holds split partials. Layers that share one index set go up
 // to kMlaMaxLayers per launch.
 constexpr int kMlaMaxLayers = 8;
-int sparse_mla_splits(int rows, int H, int k);
+int sparse_mla_splits(int rows, int H, int k, int nl);
 size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers);
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out,
@@ -42,6 +42,11 @@ hipError_t launch_sparse_mla_fp8(const HostBatch& bt, const uint16_t* q, int H, 
 hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
                                     const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
                                     float* const* lse, int n_layers, void* ws, hipStream_t s);
+// FP8 latent rows, one scale per layer's cache (layers sharing a scale are launched together)
+hipError_t launch_sparse_mla_layers_fp8(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                        const float* latent_scales, const int32_t* idx, int k, int idx_q_stride,
+                                        float scale, float* const* out, float* const* lse, int n_layers, void* ws,
+                                        hipStream_t s);
 
 // Compressed sparse attention: the DSA kernels over compressed caches plus a raw sliding window,
 // merged by log-sum-exp. Workspace layout owned by csa.hip.

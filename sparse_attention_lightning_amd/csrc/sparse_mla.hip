@@ -68,13 +68,15 @@ constexpr int kTargetWgs = 256;                 // workgroups a launch aims at (
 constexpr int kMinSplit = 128;                  // tokens per split, at least
 
 // Splits per query token: enough workgroups to fill the chip while each split keeps a minimum
-// of tokens. Workgroups are counted as a one-layer launch makes them: at H = 128, a launch that
-// fills at most half the chip deals the 128 heads to two workgroups (below). At 32 query tokens
-// that gives 4 splits x 2 head groups rather than 8 splits x 1: half the fp32 partials to write
-// and merge (measured: MLA + combine 46.4 against 53.1 us). Chosen per layer, so that a launch of
-// several layers gives every layer exactly the result of a launch of that layer alone.
-int sparse_mla_splits(int rows, int H, int k) {
-  auto wgs = [&](int s) { return (H == 128 && 2 * rows * s <= kTargetWgs) ? 2 * rows * s : rows * s; };
+// of tokens. Workgroups are counted as the launch makes them, over all nl layers it holds: at
+// H = 128, a launch that fills at most half the chip deals the 128 heads to two workgroups
+// (below). At 32 query tokens (or 8 tokens x 4 layers) that gives 4 splits x 2 head groups
+// rather than 8 (16) splits x 1: fewer fp32 partials to write and merge (measured at 32 tokens:
+// MLA + combine 46.4 against 53.1 us). A group of layers may therefore split differently from
+// a launch of one of its layers alone, and round differently within the tolerance.
+int sparse_mla_splits(int rows, int H, int k, int nl) {
+  const int units = rows * nl;
+  auto wgs = [&](int s) { return (H == 128 && 2 * units * s <= kTargetWgs) ? 2 * units * s : units * s; };
   int s = 1;
   while (wgs(s) < kTargetWgs && (k + 2 * s - 1) / (2 * s) >= kMinSplit && s < kMaxSplits) s *= 2;
   return s;
@@ -87,7 +89,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static size_t part_o_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * kDv * sizeof(part_t)); }
 static size_t part_lse_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * sizeof(float)); }
 static size_t launch_ws_bytes(int rows, int H, int k, int nl) {
-  const int s = sparse_mla_splits(rows, H, k);
+  const int s = sparse_mla_splits(rows, H, k, nl);
   if (s == 1) return 0;
   return (size_t)nl * (part_o_layer(rows, s, H) + part_lse_layer(rows, s, H));
 }
@@ -675,7 +677,7 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
       L.out[i] = out[l0 + i];
       L.lse[i] = lse ? lse[l0 + i] : nullptr;
     }
-    const int splits = sparse_mla_splits(rows, H, k);
+    const int splits = sparse_mla_splits(rows, H, k, nl);
     int split_len = (k + splits - 1) / splits;
     split_len = (split_len + kTok - 1) / kTok * kTok;
     part_t* part_o = nullptr;
@@ -720,6 +722,22 @@ hipError_t launch_sparse_mla_layers(const HostBatch& bt, const uint16_t* const* 
                                     const int32_t* idx, int k, int idx_q_stride, float scale, float* const* out,
                                     float* const* lse, int n_layers, void* ws, hipStream_t s) {
   return launch_layers(bt, q, H, latents, 0.f, idx, k, idx_q_stride, scale, out, lse, n_layers, ws, s);
+}
+
+hipError_t launch_sparse_mla_layers_fp8(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
+                                        const float* latent_scales, const int32_t* idx, int k, int idx_q_stride,
+                                        float scale, float* const* out, float* const* lse, int n_layers, void* ws,
+                                        hipStream_t s) {
+  // layers whose caches share a scale go together (the scale is an argument of the launch)
+  for (int l0 = 0; l0 < n_layers;) {
+    int l1 = l0 + 1;
+    while (l1 < n_layers && latent_scales[l1] == latent_scales[l0]) ++l1;
+    hipError_t e = launch_layers(bt, q + l0, H, latents + l0, latent_scales[l0], idx, k, idx_q_stride, scale, out + l0,
+                                 lse ? lse + l0 : nullptr, l1 - l0, ws, s);
+    if (e != hipSuccess) return e;
+    l0 = l1;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,

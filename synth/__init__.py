@@ -128,6 +128,9 @@ WORKLOADS = {
                                             planted=32, latent_fp8=1),
     "mtp_draft_b32_128k_paged": Workload("mtp_draft_b32_128k_paged", B=32, Q=1, L=131072, page_size=64,
                                          planted=32, draft_steps=7),
+    # The IndexShare group over E4M3 latent caches (one scale per layer's cache, 1 here).
+    "indexshare_b8_1m_4layers_fp8kv": Workload("indexshare_b8_1m_4layers_fp8kv", B=8, Q=1, L=1048576, page_size=64,
+                                               n_layers=4, latent_fp8=1),
     # Compressed sparse attention (architecture survey, DeepSeek-V4): compressed entries of 4 raw
     # tokens (keys and latent rows drawn like the uncompressed ones; the compression map is the
     # model's), top-1024 (V4-Pro) or top-512 (V4-Flash) of them, and a 128-token raw window.

@@ -155,6 +155,25 @@ def test_forward_shared_rejects():
     assert call(n=need - 1) == WORKSPACE
 
 
+def test_forward_shared_fp8_rejects_scales():
+    lib = dsa.lib()
+    bt = batch(B=1, L=8192)
+    kc = cache()
+    lat = (CacheT * 2)(cache(), cache())
+    ptrs = (C.c_void_p * 2)(A, A)
+    need = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 1, 1, 8192, k=2048, n_layers=2)
+
+    def call(scales):
+        sc = None if scales is None else (C.c_float * 2)(*scales)
+        return lib.dsa_forward_shared_fp8(C.byref(bt), A, A, 64, C.byref(kc), 2048, 0, 2, ptrs, 128, lat, sc, 0.04,
+                                          ptrs, None, A, A, need, None)
+    assert call(None) == INVALID
+    assert call([1.0, 0.0]) == INVALID
+    assert call([-1.0, 1.0]) == INVALID
+    assert call([1.0, float("inf")]) == INVALID
+    assert dsa.lib().dsa_last_error().decode().startswith("dsa_forward_shared_fp8")
+
+
 def test_forward_shared_noalloc_rejects_before_hip():
     """The allocation-free group call checks its arguments as dsa_forward_shared does, and refuses
     a call whose workspace would not fit the library's scratch, all before any HIP call."""
@@ -169,9 +188,9 @@ def test_forward_shared_noalloc_rejects_before_hip():
     def call(bt, nl=4, share=0, Hi=64, H=128, scale=0.04, outs=ptrs):
         return lib.dsa_forward_shared_noalloc(C.byref(bt), A, A, Hi, C.byref(kc), 2048, share, nl, ptrs, H, lat,
                                               scale, outs, None, A, None)
-    # 8 sequences of 1M tokens over 4 layers need about 161 MiB of workspace
-    big = batch(B=8, L=1 << 20)
-    assert dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=4) > dsa.NOALLOC_SCRATCH_BYTES
+    # 64 sequences x 8 query tokens at 128K keep 256 MiB of scores alone
+    big = batch(B=64, Q=8, L=1 << 17)
+    assert dsa.workspace_size(dsa.OP_FORWARD_SHARED, 64, 8, 1 << 17, n_layers=4) > dsa.NOALLOC_SCRATCH_BYTES
     assert call(big) == UNSUPPORTED
     assert "scratch" in dsa.lib().dsa_last_error().decode()
     ok = batch(B=1, L=8192)
@@ -193,14 +212,15 @@ def test_workspace_sizes_scale_with_batch():
     shared = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 32, 1, 131072)
     assert shared >= 32 * 131072 * 4 + big
     # layers that share an index set are launched together (up to 8), each with its own split
-    # partials: the group's workspace grows with the layer count up to 8 and then stays
-    one = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=1)
-    four = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=4)
-    eight = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=8)
-    many = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=20)
+    # partials, and a launch splits its tokens over all its layers: 8 tokens x 1 layer take 16
+    # splits, 8 x 4 take 4 (the same partial bytes), 8 x 8 take 2; 20 layers go as 8 + 8 + 4
+    P = 8 * 128 * 512 * 4 + 8 * 128 * 4          # fp32 partial and lse of one split of 8 tokens x 128 heads
+    base = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=1) - \
+        dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
     mla1 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
-    assert mla1 > 0
-    assert four - one == 3 * mla1 and eight - one == 7 * mla1 and many == eight
+    assert mla1 == 16 * P
+    for nl, splits in ((4, 4), (8, 2), (20, 2)):
+        assert dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=nl) - base == min(nl, 8) * splits * P
 
 
 # ----------------------------------------------------------------------------- HiSparse swap-in

@@ -166,13 +166,26 @@ def test_indexshare_b8_1m_4layers():
     idx, res = dsa.forward_shared(g.q_idx, g.w, keys, wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax)
     torch.cuda.synchronize()
     check_rows_wellformed(idx, wl)
-    # the group forward equals separate calls with one index set
-    scores, idx2, outs, lses = run_path(g, wl)
-    assert torch.equal(idx, idx2)
-    for layer in range(4):
-        assert torch.equal(res[layer][0], outs[layer]) and torch.equal(res[layer][1], lses[layer])
-    del res
-    oracle_check_query(g, wl, 3, 0, scores, idx, outs, lses)
+    # the group selects what separate stage calls select; its four layers match the oracle
+    scores = dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax)
+    assert torch.equal(idx, dsa.topk(scores, g.seq_lens, wl.k))
+    oracle_check_query(g, wl, 3, 0, scores, idx, [o for o, _ in res], [l for _, l in res])
+
+
+def test_indexshare_b8_1m_4layers_fp8kv():
+    """The 1M-token IndexShare group over four E4M3 latent caches: the group selects what separate
+    stage calls select; one sequence against the oracle in every layer."""
+    wl = synth.WORKLOADS["indexshare_b8_1m_4layers_fp8kv"]
+    g = synth.generate(wl, seed=0, device=DEV)
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    lats = [dsa.Cache(g.latent[l], g.latent_table[l], wl.page_size) for l in range(4)]
+    idx, res = dsa.forward_shared(g.q_idx, g.w, keys, wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax,
+                                  latent_scales=[1.0] * 4)
+    torch.cuda.synchronize()
+    check_rows_wellformed(idx, wl)
+    scores = dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax)
+    assert torch.equal(idx, dsa.topk(scores, g.seq_lens, wl.k))
+    oracle_check_query(g, wl, 6, 0, scores, idx, [o for o, _ in res], [l for _, l in res], latent_scale=1.0)
 
 
 @pytest.mark.parametrize("name", ["verify_b64_q8_32k", "verify_b64_q8_32k_draftshare"])

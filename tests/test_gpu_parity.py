@@ -374,23 +374,26 @@ def test_forward_shared_small(share_first):
 
 
 @pytest.mark.parametrize("H", [128, 64])
-def test_forward_shared_many_layers(H):
-    """Ten layers share one index set: the library launches their MLA eight layers at a time
-    (two launches here). Every layer equals a separate sparse-MLA call bit for bit and matches
-    the oracle."""
-    wl = synth.small("indexshare_b8_1m_4layers", B=2, L=3000, L_max=3008, seq_lens=(3000, 2345), n_layers=10, H=H)
+@pytest.mark.parametrize("B,n_layers", [(2, 10), (8, 4)])
+def test_forward_shared_many_layers(H, B, n_layers):
+    """Layers that share one index set: the library launches their MLA eight layers at a time
+    (ten layers: two launches) and splits each launch's tokens over all its layers. Every layer
+    matches the oracle on the GPU's set, and the group is deterministic."""
+    lens = tuple(3000 - 97 * b for b in range(B))
+    wl = synth.small("indexshare_b8_1m_4layers", B=B, L=3000, L_max=3008, seq_lens=lens, n_layers=n_layers, H=H)
     cpu, g = gpu_batch(wl)
     lats = [lat_arg(g, l) for l in range(wl.n_layers)]
     idx, res = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax)
+    idx2, res2 = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
     o_idx, exact = oracle_idx(cpu, wl)
     idx_np = np_(idx)
     for b in range(wl.B):
         check_topk_sets(idx_np[b, 0], o_idx[b, 0], exact[b, 0], wl.k)
     for layer in range(wl.n_layers):
-        out, lse = dsa.sparse_mla_fwd(g.q_mla[layer], lats[layer], idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
-        assert torch.equal(res[layer][0], out) and torch.equal(res[layer][1], lse), layer
-    for layer in (0, 8, 9):                                # one layer of each launch, and the last
-        ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[layer]), latent_cache(cpu, layer), o_idx, wl.scale)
+        assert torch.equal(res[layer][0], res2[layer][0]) and torch.equal(res[layer][1], res2[layer][1]), layer
+        ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[layer]), latent_cache(cpu, layer), idx_np, wl.scale)
         out_l, lse_l = np_(res[layer][0]), np_(res[layer][1])
         for b in range(wl.B):
             check_mla(out_l[b, 0], lse_l[b, 0], ref_o[b, 0], ref_l[b, 0])
@@ -513,6 +516,44 @@ def test_sparse_mla_fp8_logit_jumps_after_the_first_step(H):
     assert float(np.abs(ref_o[1, 0, 5]).max()) >= 8.0
     for b in range(B):
         check_mla(out[b, 0], lse[b, 0], ref_o[b, 0], ref_l[b, 0])
+
+
+@pytest.mark.parametrize("share_first", [False, True])
+def test_forward_shared_fp8_layers(share_first):
+    """The IndexShare group over E4M3 latent caches, one scale per layer: layers sharing a scale go
+    in one launch (here two launches: scales 0.5, 0.5, 2.0). Every layer matches the oracle on
+    the GPU's set; with a power-of-two scale the group equals its bf16 form over the decoded values
+    bit for bit (same launches, same products)."""
+    base = "verify_b64_q8_32k_draftshare" if share_first else "indexshare_b8_1m_4layers"
+    wl = synth.small(base, B=2, Q=3 if share_first else 1, L=4000, L_max=4032, seq_lens=(4000, 2900), n_layers=3,
+                     latent_fp8=1, page_size=64)
+    cpu, g = gpu_batch(wl)
+    scales = [0.5, 0.5, 2.0]
+    lats = [lat_arg(g, l) for l in range(wl.n_layers)]
+    idx, res = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla, lats, wl.scale, g.seq_lens, wl.lmax,
+                                  share_first_query=share_first, latent_scales=scales)
+    o_idx, exact = oracle_idx(cpu, wl, share_first=share_first)
+    idx_np = np_(idx)
+    for b in range(wl.B):
+        for j in range(idx_np.shape[1]):
+            check_topk_sets(idx_np[b, j], o_idx[b, j], exact[b, j], wl.k)
+    for layer in range(wl.n_layers):
+        out, lse = np_(res[layer][0]), np_(res[layer][1])
+        ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[layer]), latent_cache(cpu, layer), idx_np, wl.scale,
+                                               idx_q_stride_is_k=not share_first, latent_scale=scales[layer])
+        for b in range(wl.B):
+            for j in range(wl.Q):
+                check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
+    # the bf16 group over the decoded values (same scales grouping: layers 0-1, then layer 2)
+    dec = [dsa_cache((g.latent[l].view(torch.float8_e4m3fn).to(torch.float32) * scales[l]).to(torch.bfloat16),
+                     g.latent_table[l], wl.page_size) for l in range(wl.n_layers)]
+    _, res_a = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla[:2], dec[:2], wl.scale, g.seq_lens,
+                                  wl.lmax, share_first_query=share_first)
+    _, res_b = dsa.forward_shared(g.q_idx, g.w, keys_arg(g), wl.k, g.q_mla[2:], dec[2:], wl.scale, g.seq_lens,
+                                  wl.lmax, share_first_query=share_first)
+    torch.cuda.synchronize()
+    for layer, (o, l) in enumerate(res_a + res_b):
+        assert torch.equal(res[layer][0], o) and torch.equal(res[layer][1], l), layer
 
 
 def test_sparse_mla_fp8_shared_index_row_and_empty_sets():
