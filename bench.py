@@ -128,19 +128,19 @@ def traffic_from_profile(wl_name):
 
 
 def cpu_baseline(batches, wl, budget_s):
-    """The oracle as it stands, timed on a bounded sample of the same workload on host cores."""
+    """The oracle as it stands, timed on a bounded sample of the same workload on host cores: the
+    plain C reference (OpenMP over keys and heads) for the DSA workloads, the numpy oracle for
+    compressed sparse attention."""
     import numpy as np
     import torch
 
     import oracle
+    from oracle import cref
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     cores = len(os.sched_getaffinity(0))
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    cref.build()
     g = batches[0]
     done_tokens, elapsed, seqs = 0, 0.0, 0
     rows_per_seq = 1 if wl.share_first_query else wl.Q
@@ -171,23 +171,27 @@ def cpu_baseline(batches, wl, budget_s):
                 oracle.csa.csa_one(q_idx[j], w[j], keys, lats[0], win, 0, p, wl.ratio, wl.k, wl.window, q_mla[0][j],
                                    wl.scale, wl.rows)
                 continue
-            s = oracle.index_scores(q_idx[j], w[j], keys, 0, p, wl.lmax)
-            idx = oracle.select_topk(s.astype(np.float32), p, wl.k)
+            s = cref.index_scores(q_idx[j], w[j], keys.data[0], p, wl.lmax)
+            idx = cref.select_topk(s.astype(np.float32), p, wl.k)
+            sel = idx[idx >= 0]
             users = range(wl.Q) if wl.share_first_query else [j]
             for c in range(len(q_mla)):          # every layer, or every draft step of an MTP loop
+                rows = lat_of(c).data[0][sel]
                 for u in users:
-                    oracle.sparse_mla_one(q_mla[c][u], lat_of(c), 0, idx, wl.scale, latent_scale=1.0)
+                    cref.sparse_mla(q_mla[c][u], rows, wl.scale, latent_scale=1.0)
         elapsed += time.perf_counter() - t0
         done_tokens += (wl.Q if wl.share_first_query else rows_per_seq) * max(1, wl.draft_steps)
         seqs += 1
         if elapsed >= budget_s:
             break
-    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": threads if threads > 1 else cores,
+    form = "numpy float64 (compressed sparse attention oracle)" if wl.ratio else \
+        "plain C, float64, OpenMP over keys and heads (oracle/dsa_ref.c)"
+    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{seqs} of {wl.B} sequences of {wl.name} (all {rows_per_seq * seqs} query tokens of the "
                       f"sample: index scores over every visible key, top-{wl.k}, sparse MLA over {wl.H} heads x "
-                      f"{len(q_mla)} layer(s) or draft step(s)); {elapsed:.1f} s of oracle time; numpy float64, host threads={threads}, "
-                      f"affinity cores={cores}"}
+                      f"{len(q_mla)} layer(s) or draft step(s)); {elapsed:.1f} s of oracle time; {form}; "
+                      f"threads={threads}, affinity cores={cores}"}
 
 
 def main():

@@ -1,4 +1,5 @@
-"""CPU oracle of the DSA hot path (plain numpy, float64).
+"""CPU oracle of the DSA hot path: plain numpy in float64 (dsa.py, hisparse.py, csa.py) and the
+same DSA steps as plain C (dsa_ref.c through cref.py), tied to the numpy form by tests.
 
 TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's CPU baseline
 may import this package. The GPU library and its Python binding never do.
