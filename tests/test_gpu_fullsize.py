@@ -188,6 +188,39 @@ def test_indexshare_b8_1m_4layers_fp8kv():
     oracle_check_query(g, wl, 6, 0, scores, idx, [o for o, _ in res], [l for _, l in res], latent_scale=1.0)
 
 
+def test_decode_at_the_16m_token_limit():
+    """One sequence at the longest context the library accepts (L_max = 2^24 tokens, paged by 64):
+    indexer scores at 4096 sampled positions against the oracle, the top-k set bit for bit
+    against the oracle's selection on the GPU's own fp32 scores (the long-row top-k form), the
+    planted tokens in it, and the attention against the oracle on that set."""
+    L = 1 << 24
+    wl = synth.Workload("decode_16m", B=1, Q=1, L=L, page_size=64, planted=16)
+    g = synth.generate(wl, seed=0, device=DEV)
+    scores, idx, outs, lses = run_path(g, wl)
+    check_rows_wellformed(idx, wl)
+    p = L - 1
+    rng = np.random.default_rng(0)
+    t = np.unique(np.concatenate([rng.integers(0, L, 4096), g.planted_pos[0].cpu().numpy(), [0, p]]))
+    key_rows = g.keys[g.key_table[0][torch.from_numpy(t // 64).to(DEV).long()].long(),
+                      torch.from_numpy(t % 64).to(DEV).long()].cpu().numpy()
+    qi, wi = g.q_idx[0, 0].cpu().numpy(), g.w[0, 0].cpu().numpy()
+    sub = oracle.Cache(key_rows[None])
+    exact = oracle.index_scores(qi, wi, sub, 0, t.size - 1, t.size)
+    got = scores[0, 0, torch.from_numpy(t).to(DEV).long()].cpu().numpy()
+    tol = score_tolerance(qi, wi, key_rows)
+    err = np.abs(got.astype(np.float64) - exact)
+    assert np.all(err <= tol), float(err.max())
+    s32 = scores[0, 0].cpu().numpy()
+    assert np.array_equal(idx[0, 0].cpu().numpy(), oracle.select_topk(s32, p, wl.k))
+    assert set(g.planted_pos[0].tolist()) <= set(idx[0, 0].cpu().tolist())
+    sel = idx[0, 0].cpu().numpy()
+    tab = g.latent_table[0][0].long()
+    rows = g.latent[0].view(torch.int16)[tab[torch.from_numpy(sel // 64).to(DEV).long()],
+                                         torch.from_numpy(sel % 64).to(DEV).long()].cpu().numpy().view(np.uint16)
+    ref_o, ref_l = oracle.sparse_mla(q_bits(g.q_mla[0], 0)[0], rows, wl.scale)
+    check_mla(outs[0][0, 0].cpu().numpy(), lses[0][0, 0].cpu().numpy(), ref_o, ref_l)
+
+
 @pytest.mark.parametrize("name", ["verify_b64_q8_32k", "verify_b64_q8_32k_draftshare"])
 def test_verify_b64_q8_32k(name):
     wl = synth.WORKLOADS[name]
