@@ -142,7 +142,7 @@ def cpu_baseline(batches, wl, budget_s):
     threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
     cref.build()
     g = batches[0]
-    done_tokens, elapsed, seqs = 0, 0.0, 0
+    done_tokens, done_rows, elapsed, seqs = 0, 0, 0.0, 0
     rows_per_seq = 1 if wl.share_first_query else wl.Q
     for b in range(wl.B):
         # inputs of sequence b in logical token order (input preparation, not timed)
@@ -164,32 +164,35 @@ def cpu_baseline(batches, wl, budget_s):
         q_mla = [t[b].view(torch.int16).cpu().numpy().view(np.uint16) for t in q_src]
         lat_of = (lambda i: lats[0]) if wl.draft_steps else (lambda i: lats[i])
         n = wl.lens[b]
-        t0 = time.perf_counter()
-        for j in range(rows_per_seq):
+        seqs += 1
+        for j in range(rows_per_seq):        # the budget is checked after every query token
             p = n - wl.Q + j
+            t0 = time.perf_counter()
             if wl.ratio:             # compressed sparse attention: selection, window and attention in one
                 oracle.csa.csa_one(q_idx[j], w[j], keys, lats[0], win, 0, p, wl.ratio, wl.k, wl.window, q_mla[0][j],
                                    wl.scale, wl.rows)
-                continue
-            s = cref.index_scores(q_idx[j], w[j], keys.data[0], p, wl.lmax)
-            idx = cref.select_topk(s.astype(np.float32), p, wl.k)
-            sel = idx[idx >= 0]
-            users = range(wl.Q) if wl.share_first_query else [j]
-            for c in range(len(q_mla)):          # every layer, or every draft step of an MTP loop
-                rows = lat_of(c).data[0][sel]
-                for u in users:
-                    cref.sparse_mla(q_mla[c][u], rows, wl.scale, latent_scale=1.0)
-        elapsed += time.perf_counter() - t0
-        done_tokens += (wl.Q if wl.share_first_query else rows_per_seq) * max(1, wl.draft_steps)
-        seqs += 1
+            else:
+                s = cref.index_scores(q_idx[j], w[j], keys.data[0], p, wl.lmax)
+                idx = cref.select_topk(s.astype(np.float32), p, wl.k)
+                sel = idx[idx >= 0]
+                users = range(wl.Q) if wl.share_first_query else [j]
+                for c in range(len(q_mla)):          # every layer, or every draft step of an MTP loop
+                    rows = lat_of(c).data[0][sel]
+                    for u in users:
+                        cref.sparse_mla(q_mla[c][u], rows, wl.scale, latent_scale=1.0)
+            elapsed += time.perf_counter() - t0
+            done_tokens += (wl.Q if wl.share_first_query else 1) * max(1, wl.draft_steps)
+            done_rows += 1
+            if elapsed >= budget_s:
+                break
         if elapsed >= budget_s:
             break
     form = "numpy float64 (compressed sparse attention oracle)" if wl.ratio else \
         "plain C, float64, OpenMP over keys and heads (oracle/dsa_ref.c)"
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{seqs} of {wl.B} sequences of {wl.name} (all {rows_per_seq * seqs} query tokens of the "
-                      f"sample: index scores over every visible key, top-{wl.k}, sparse MLA over {wl.H} heads x "
+            "sample": f"{done_rows} selections in {seqs} of {wl.B} sequences of {wl.name} ({done_tokens} query or "
+                      f"draft tokens: index scores over every visible key, top-{wl.k}, sparse MLA over {wl.H} heads x "
                       f"{len(q_mla)} layer(s) or draft step(s)); {elapsed:.1f} s of oracle time; {form}; "
                       f"threads={threads}, affinity cores={cores}"}
 

@@ -24,6 +24,7 @@
 // Rows with p + 1 <= k keep every visible token. Results are deterministic: the kept set is
 // defined by score and position alone, never by the order of the appends.
 #include <algorithm>
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 
@@ -359,9 +360,7 @@ static_assert(kRCap >= 2 * kMaxK, "room for about 1.5k candidates plus spread");
 // the sampled form's per-row kernels).
 template <int NT>
 struct SelLds {
-  static constexpr int kWindow = NT * 128; // positions per emission bitmap window (4 words per thread)
   static_assert(kRBins % NT == 0, "whole bins per thread");
-  uint32_t bitmap[kWindow / 32];
   union {
     uint32_t hist[2][kRBins];              // radix levels alternate between two histograms
     sampled::TkLds full;                   // the exact full-row fallback
@@ -535,10 +534,13 @@ __device__ uint32_t sample_tau(Blk<NT>& B, const float* __restrict__ srow, int n
 // Exact top-k of the candidates held in registers (PER per thread; every score of the row that
 // can be among the k largest is a candidate, cnt >= k of them) written to out[0..k) in
 // ascending position order: the k-th largest key T, the ties at T by the lowest positions, then
-// an ordered emission through a bitmap of NT * 128 positions at a time.
-template <int NT, int PER>
+// an ordered emission through an LDS bitmap of WORDS words (32 positions each) at a time. Each
+// window costs two barriers and a block scan, so the caller lends the largest LDS region free
+// by then; its first use comes after the select's last barrier.
+template <int NT, int PER, int WORDS>
 __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&cp)[PER], const bool (&cok)[PER], int n,
-                            int k, int32_t* __restrict__ out) {
+                            int k, int32_t* __restrict__ out, uint32_t* __restrict__ bitmap) {
+  static_assert(WORDS % NT == 0, "whole bitmap words per thread");
   const int tid = B.tid;
   int rem;
   const uint32_t T = B.select(ck, cok, k, true, &rem);
@@ -562,32 +564,31 @@ __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&c
   for (int e = 0; e < PER; ++e)
     keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
   int emitted = 0;
-  constexpr int kWindow = SelLds<NT>::kWindow;
+  constexpr int kWindow = WORDS * 32;
   for (int wbase = 0; wbase < n; wbase += kWindow) {
-    for (int i = tid; i < kWindow / 32; i += NT) B.S.bitmap[i] = 0u;
+    // the window's words that hold positions below n, dealt evenly: thread t owns wd consecutive
+    // words, so the emission order is the position order
+    const int nw = min(WORDS, (n - wbase + 31) >> 5);
+    const int wd = (nw + NT - 1) / NT;
+    for (int i = tid; i < nw; i += NT) bitmap[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int q = cp[e] - wbase;
-      if (keep[e] && q >= 0 && q < kWindow) atomicOr(&B.S.bitmap[q >> 5], 1u << (q & 31));
+      if (keep[e] && q >= 0 && q < kWindow) atomicOr(&bitmap[q >> 5], 1u << (q & 31));
     }
     __syncthreads();
-    constexpr int W = kWindow / 32 / NT;               // words per thread
-    uint32_t words[W], pc = 0;
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      words[e] = B.S.bitmap[tid * W + e];
-      pc += __builtin_popcount(words[e]);
-    }
+    const int w0 = min(tid * wd, nw), w1 = min(w0 + wd, nw);
+    uint32_t pc = 0;
+    for (int i = w0; i < w1; ++i) pc += __builtin_popcount(bitmap[i]);
     uint32_t tot;
     int slot = emitted + (int)B.scan(pc, &tot);
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      uint32_t m = words[e];
+    for (int i = w0; i < w1 && slot < k; ++i) {
+      uint32_t m = bitmap[i];
       while (m) {
         const int bit = __builtin_ctz(m);
         m &= m - 1;
-        if (slot < k) out[slot] = wbase + 32 * (tid * W + e) + bit;
+        if (slot < k) out[slot] = wbase + 32 * i + bit;
         ++slot;
       }
     }
@@ -699,7 +700,10 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
     ck[e] = cok[e] ? R.key[i] : 0u;
     cp[e] = cok[e] ? R.pos[i] : 0;
   }
-  select_emit(B, ck, cp, cok, n, k, out);
+  // the candidate arrays (key, then pos: 2 kRCap words) are free once read into registers: the
+  // emission bitmap takes them, 256K positions per window
+  static_assert(offsetof(RowLds, pos) == offsetof(RowLds, key) + kRCap * sizeof(uint32_t), "key, then pos");
+  select_emit<kRT, kRCPer, 2 * kRCap>(B, ck, cp, cok, n, k, out, R.key);
 }
 
 template <bool VEC>
@@ -756,7 +760,9 @@ __global__ __launch_bounds__(kST) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
   constexpr int PER = kTkCap / kST;
+  constexpr int kEmitWords = 24 * kST;                 // 96 KB: 768K positions per emission window
   __shared__ rowsel::SelLds<kST> S;
+  __shared__ uint32_t emit_bits[kEmitWords];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
@@ -786,7 +792,7 @@ __global__ __launch_bounds__(kST) void topk_finish_kernel(
     cp[e] = (int)c.y;
   }
   __syncthreads();                                     // the zeroed histograms before the first level
-  rowsel::select_emit(B, ck, cp, cok, ri.n, k, out);
+  rowsel::select_emit<kST, PER, kEmitWords>(B, ck, cp, cok, ri.n, k, out, emit_bits);
 }
 
 template <bool VEC>
