@@ -165,8 +165,8 @@ dsa_status dsa_forward_shared_fp8(const dsa_batch_t* batch, const uint8_t* q_e4m
  * and errors as dsa_forward_shared, without the workspace: the call uses a scratch array that the
  * library holds in device memory, DSA_NOALLOC_SCRATCH_BYTES (128 MiB) on each GPU it runs on,
  * from that GPU's first call until the process ends. It covers, for example, decode at B = 32
- * and 128K tokens (50 MiB), the 8-position verification batch at B = 64 and 32K (96 MiB) and
- * the 4-layer group at B = 8 and 1M tokens (65 MiB). A call whose dsa_workspace_size(
+ * and 128K tokens (83 MiB), the 8-position verification batch at B = 64 and 32K (96 MiB) and
+ * the 4-layer group at B = 8 and 1M tokens (97 MiB). A call whose dsa_workspace_size(
  * DSA_OP_FORWARD_SHARED, ...) exceeds it returns DSA_ERR_UNSUPPORTED and launches nothing.
  * The call itself allocates nothing and calls no allocating routine. Every call on one GPU
  * shares that GPU's scratch: calls that overlap in time on one GPU (on different streams, or from

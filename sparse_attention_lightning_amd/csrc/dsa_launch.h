@@ -30,7 +30,7 @@ hipError_t launch_topk(const HostBatch& bt, const float* scores, int k, int32_t*
 // Sparse MLA (MQA mode). Workspace holds split partials. Layers that share one index set go up
 // to kMlaMaxLayers per launch.
 constexpr int kMlaMaxLayers = 8;
-int sparse_mla_splits(int rows, int H, int k, int nl);
+int sparse_mla_splits(int rows, int H, int k, int nl, bool f8);
 size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers);
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out,

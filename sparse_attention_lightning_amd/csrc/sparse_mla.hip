@@ -74,9 +74,14 @@ constexpr int kMinSplit = 128;                  // tokens per split, at least
 // rather than 8 (16) splits x 1: fewer fp32 partials to write and merge (measured at 32 tokens:
 // MLA + combine 46.4 against 53.1 us). A group of layers may therefore split differently from
 // a launch of one of its layers alone, and round differently within the tolerance.
-int sparse_mla_splits(int rows, int H, int k, int nl) {
+// FP8 rows keep one head group per split (the count ignores head groups): two groups would each
+// gather and convert the same E4M3 rows, and 8 splits x 32 heads per wave measured 62 us against
+// 70 us for 4 x 2 at 32 decode rows.
+int sparse_mla_splits(int rows, int H, int k, int nl, bool f8) {
   const int units = rows * nl;
-  auto wgs = [&](int s) { return (H == 128 && 2 * units * s <= kTargetWgs) ? 2 * units * s : units * s; };
+  auto wgs = [&](int s) {
+    return (!f8 && H == 128 && 2 * units * s <= kTargetWgs) ? 2 * units * s : units * s;
+  };
   int s = 1;
   while (wgs(s) < kTargetWgs && (k + 2 * s - 1) / (2 * s) >= kMinSplit && s < kMaxSplits) s *= 2;
   return s;
@@ -88,17 +93,21 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // [rows][splits][H] fp32 lse.
 static size_t part_o_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * kDv * sizeof(part_t)); }
 static size_t part_lse_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * sizeof(float)); }
-static size_t launch_ws_bytes(int rows, int H, int k, int nl) {
-  const int s = sparse_mla_splits(rows, H, k, nl);
+static size_t launch_ws_bytes(int rows, int H, int k, int nl, bool f8) {
+  const int s = sparse_mla_splits(rows, H, k, nl, f8);
   if (s == 1) return 0;
   return (size_t)nl * (part_o_layer(rows, s, H) + part_lse_layer(rows, s, H));
 }
 
 size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers) {
-  // layers go kMlaMaxLayers per launch; the last launch may hold fewer
-  size_t b = launch_ws_bytes(rows, H, k, std::min(n_layers, kMlaMaxLayers));
-  if (n_layers > kMlaMaxLayers && n_layers % kMlaMaxLayers)
-    b = std::max(b, launch_ws_bytes(rows, H, k, n_layers % kMlaMaxLayers));
+  // layers go kMlaMaxLayers per launch; the last launch may hold fewer. One size serves bf16 and
+  // FP8 rows, whose split counts may differ.
+  size_t b = 0;
+  for (const bool f8 : {false, true}) {
+    b = std::max(b, launch_ws_bytes(rows, H, k, std::min(n_layers, kMlaMaxLayers), f8));
+    if (n_layers > kMlaMaxLayers && n_layers % kMlaMaxLayers)
+      b = std::max(b, launch_ws_bytes(rows, H, k, n_layers % kMlaMaxLayers, f8));
+  }
   return b;
 }
 
@@ -677,7 +686,7 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
       L.out[i] = out[l0 + i];
       L.lse[i] = lse ? lse[l0 + i] : nullptr;
     }
-    const int splits = sparse_mla_splits(rows, H, k, nl);
+    const int splits = sparse_mla_splits(rows, H, k, nl, f8);
     int split_len = (k + splits - 1) / splits;
     split_len = (split_len + kTok - 1) / kTok * kTok;
     part_t* part_o = nullptr;

@@ -39,7 +39,7 @@ def both_calls(wl, seed=0, share_first=False):
 
 
 def test_noalloc_group_call_equals_workspace_call_then_a_smaller_one():
-    # the decode batch at its full size (50 MiB of scratch), then a smaller two-layer group
+    # the decode batch at its full size (83 MiB of scratch), then a smaller two-layer group
     big = synth.WORKLOADS["decode_b32_128k_paged"]
     print("noalloc: decode B=32 L=131072", flush=True)
     both_calls(big)
