@@ -95,6 +95,23 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Four consecutive fp32 values from i0 (a multiple of 4) of a row with `lim` >= 1 readable
+// entries. With VEC the row starts 16-byte aligned inside an allocation that is a multiple of 4
+// entries long, so the aligned vector holding entry lim - 1 is readable. The address is clamped
+// into the row instead of guarded by a branch: a branch around each load makes the compiler wait
+// at the join for every load before it, while clamped loads issue back to back. Entries at or
+// past lim hold some in-row value; the caller masks them.
+template <bool VEC>
+__device__ __forceinline__ float4 load4_clamped(const float* __restrict__ row, int i0, int lim) {
+  if (VEC) return *(const float4*)(row + min(i0, (lim - 1) & ~3));
+  float4 x;
+  x.x = row[min(i0 + 0, lim - 1)];
+  x.y = row[min(i0 + 1, lim - 1)];
+  x.z = row[min(i0 + 2, lim - 1)];
+  x.w = row[min(i0 + 3, lim - 1)];
+  return x;
+}
+
 // Wave-inclusive scans by DPP: row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15
 // and 31 carry the row totals across rows (lanes shifted in from outside a row read `id`).
 template <int CTRL, int ROWMASK>

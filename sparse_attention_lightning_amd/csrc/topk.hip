@@ -42,7 +42,7 @@ namespace sampled {
 
 constexpr int kTkThreads = 256;
 constexpr int kTkCap = 8192;               // candidates kept per row (4 x the largest k)
-constexpr int kTkChunk = 4096;             // scores per gather workgroup (16 per thread)
+constexpr int kGatherChunk = 4096;         // scores per gather workgroup (16 per thread)
 constexpr int kTkWindow = 1 << 18;         // positions per bitmap window in the finish step (32 KB)
 static_assert(kTkCap >= 2 * kMaxK, "room for about 2k candidates plus spread");
 
@@ -233,65 +233,69 @@ __device__ uint32_t select_24(TkLds& L, int n, int need, ValFn v, UseFn use) {
 }
 
 // ------------------------------------------------------------------------------------------ gather
+// One workgroup per chunk of kGatherChunk scores. Its score loads go out first, all at once and
+// clamped into the row, so that their latency overlaps that of the row's length and tau. A
+// first pass counts the thread's candidates, one atomic per workgroup reserves their room, and
+// a second pass over the same registers writes them.
 template <bool VEC>
 __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, int n_chunks, TkWs ws) {
+  constexpr int NV = kGatherChunk / (4 * kTkThreads);
   const int row = blockIdx.x / n_chunks, chunk = blockIdx.x - row * n_chunks;
+  const int lo = chunk * kGatherChunk;
+  const float* srow = scores + (int64_t)row * L_max;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float4 x[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) x[v] = load4_clamped<VEC>(srow, lo + 4 * tid + 4 * kTkThreads * v, L_max);
   const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
   if (ri.m == ri.n) return;
-  const int lo = chunk * kTkChunk, hi = min(lo + kTkChunk, ri.n);
+  const int hi = min(lo + kGatherChunk, ri.n);
   if (lo >= hi) return;
   TkRow* st = ws.rows + row;
   const uint32_t tau = st->tau;
-  const float* srow = scores + (int64_t)row * L_max;
-  const int lane = threadIdx.x & 63;
-  uint32_t u[16];
-  int pos[16];
-  int mine = 0;
+  uint32_t mine = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int i0 = lo + 4 * (int)threadIdx.x + 1024 * v;
-    float f[4];
-    if (VEC && i0 + 3 < hi) {
-      const float4 x = *(const float4*)(srow + i0);
-      f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-    } else {
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = lo + 4 * tid + 4 * kTkThreads * v;
+    const float f[4] = {x[v].x, x[v].y, x[v].z, x[v].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = (i0 + e < hi) ? srow[i0 + e] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = float_key(f[e]);
-      if (i0 + e < hi && key >= tau) {
-        u[mine] = key;
-        pos[mine] = i0 + e;
-        ++mine;
-      }
-    }
+    for (int e = 0; e < 4; ++e) mine += (i0 + e < hi && float_key(f[e]) >= tau) ? 1u : 0u;
   }
-  // one atomic per workgroup reserves room for its candidates: wave scans, then the four wave
-  // totals through LDS (the early returns above are workgroup-uniform)
+  // wave scans, then the four wave totals through LDS (the early returns above are
+  // workgroup-uniform)
   __shared__ uint32_t wtot[kTkThreads / 64];
   __shared__ uint32_t wg_base;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan((uint32_t)mine, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  const uint32_t incl = wave_incl_scan(mine, 0u, [](uint32_t a, uint32_t b) { return a + b; });
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     uint32_t t = 0;
 #pragma unroll
     for (int i = 0; i < kTkThreads / 64; ++i) t += wtot[i];
     wg_base = t ? atomicAdd(&st->count, t) : 0u;
   }
   __syncthreads();
-  uint32_t base = wg_base;
+  uint32_t slot = wg_base;
 #pragma unroll
-  for (int i = 0; i < kTkThreads / 64; ++i) base += i < wave ? wtot[i] : 0u;
-  base += incl - (uint32_t)mine;
+  for (int i = 0; i < kTkThreads / 64; ++i) slot += i < wave ? wtot[i] : 0u;
+  slot += incl - mine;
+  if (!mine) return;
   uint2* cand = ws.cand + (int64_t)row * kTkCap;
-  for (int c = 0; c < mine; ++c)
-    if (base + c < (uint32_t)kTkCap) cand[base + c] = make_uint2(u[c], (uint32_t)pos[c]);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = lo + 4 * tid + 4 * kTkThreads * v;
+    const float f[4] = {x[v].x, x[v].y, x[v].z, x[v].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = float_key(f[e]);
+      if (i0 + e < hi && key >= tau) {
+        if (slot < (uint32_t)kTkCap) cand[slot] = make_uint2(key, (uint32_t)(i0 + e));
+        ++slot;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------ finish
@@ -509,14 +513,8 @@ __device__ uint32_t sample_tau(Blk<NT>& B, const float* __restrict__ srow, int n
   for (int e = 0; e < kPer; ++e) {
     const int v = tid + e * NT;
     const int i0 = (v >> 2) * stride * 16 + 4 * (v & 3);
-    float f[4];
-    if (VEC && v < s_blocks * 4 && i0 + 3 < n) {
-      const float4 x = *(const float4*)(srow + i0);
-      f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) f[c] = (v < s_blocks * 4 && i0 + c < n) ? srow[i0 + c] : 0.f;
-    }
+    const float4 x = load4_clamped<VEC>(srow, i0, n);
+    const float f[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       sok[4 * e + c] = v < s_blocks * 4 && i0 + c < n;
@@ -632,20 +630,12 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   auto load = [&](float4 (&d)[kRUnroll], int base) {
 #pragma unroll
     for (int u = 0; u < kRUnroll; ++u) {
-      const int i0 = base + 4 * (tid + u * kRT);
-      if (VEC && i0 + 3 < n) {
-        d[u] = *(const float4*)(srow + i0);
-      } else {
-        d[u].x = i0 + 0 < n ? srow[i0 + 0] : -INFINITY;
-        d[u].y = i0 + 1 < n ? srow[i0 + 1] : -INFINITY;
-        d[u].z = i0 + 2 < n ? srow[i0 + 2] : -INFINITY;
-        d[u].w = i0 + 3 < n ? srow[i0 + 3] : -INFINITY;
-      }
+      d[u] = load4_clamped<VEC>(srow, base + 4 * (tid + u * kRT), n);   // past n: masked below
     }
   };
   load(cur, 0);
   for (int base = 0; base < n; base += kStep) {
-    if (base + kStep < n) load(nxt, base + kStep);
+    load(nxt, base + kStep);                           // the last pass's are clamped and unused
     uint64_t bal[kRUnroll][4];
     uint32_t total = 0;
 #pragma unroll
@@ -773,23 +763,26 @@ __global__ __launch_bounds__(kST) void topk_finish_kernel(
     return;
   }
   rowsel::Blk<kST> B{S, tid, tid & 63, tid >> 6};
+  // every slot of the list is loaded at once, before the count is known (slots past the count
+  // hold stale values and are masked)
+  const uint2* cand = ws.cand + (int64_t)row * kTkCap;
+  uint2 c[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) c[e] = cand[tid + e * kST];
   const int cnt = (int)ws.rows[row].count;
   if (cnt < k || cnt > kTkCap) {                       // the sample missed: exact scan of the row
     finish_full_scan<kST>(scores + (int64_t)row * L_max, ri.n, k, out, S.h.full);
     return;
   }
   for (int i = tid; i < 2 * rowsel::kRBins; i += kST) (&S.h.hist[0][0])[i] = 0u;
-  const uint2* cand = ws.cand + (int64_t)row * kTkCap;
   uint32_t ck[PER];
   int cp[PER];
   bool cok[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int i = tid + e * kST;
-    cok[e] = i < cnt;
-    const uint2 c = cok[e] ? cand[i] : make_uint2(0u, 0u);
-    ck[e] = c.x;
-    cp[e] = (int)c.y;
+    cok[e] = tid + e * kST < cnt;
+    ck[e] = cok[e] ? c[e].x : 0u;
+    cp[e] = cok[e] ? (int)c[e].y : 0;
   }
   __syncthreads();                                     // the zeroed histograms before the first level
   rowsel::select_emit<kST, PER, kEmitWords>(B, ck, cp, cok, ri.n, k, out, emit_bits);
@@ -798,7 +791,7 @@ __global__ __launch_bounds__(kST) void topk_finish_kernel(
 template <bool VEC>
 static void launch_all(const HostBatch& bt, const float* scores, int k, int32_t* idx, TkWs w, int rows,
                        hipStream_t s) {
-  const int n_chunks = (bt.L_max + kTkChunk - 1) / kTkChunk;
+  const int n_chunks = (bt.L_max + kGatherChunk - 1) / kGatherChunk;
   // The candidate count spreads as sqrt(target x sampling stride). Rows above 128K scores take
   // a denser sample and aim at 2.5k, midway between the bounds k and kTkCap (4k at the largest
   // k), so that a sample miss (and the exact full-row scan it costs) stays rare at 1M scores

@@ -151,14 +151,8 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int l
 #pragma unroll
   for (int v = 0; v < kTopkVpt; ++v) {
     const int i0 = lo + kTopkVec * (int)threadIdx.x + kTopkThreads * kTopkVec * v;
-    float f[4];
-    if (VEC && i0 + 3 < hi) {
-      const float4 x = *(const float4*)(srow + i0);
-      f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = (i0 + e < hi) ? srow[i0 + e] : 0.f;
-    }
+    const float4 x = load4_clamped<VEC>(srow, i0, hi);
+    const float f[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       u[4 * v + e] = float_key(f[e]);
