@@ -366,7 +366,7 @@ template <int NT>
 struct SelLds {
   static_assert(kRBins % NT == 0, "whole bins per thread");
   union {
-    uint32_t hist[2][kRBins];              // radix levels alternate between two histograms
+    alignas(16) uint32_t hist[2][kRBins];  // radix levels alternate between two histograms
     sampled::TkLds full;                   // the exact full-row fallback
   } h;
   uint32_t wred[4][NT / 64];               // per-wave partials, rotated over the block steps
@@ -431,14 +431,22 @@ struct Blk {
   // needed from it (two barriers). Thread t owns bins [kRBins - 4(t+1), kRBins - 4t).
   __device__ void find_bin(int need, uint32_t& bin, int& rem) {
     constexpr int PER = kRBins / NT;
+    static_assert(PER % 4 == 0, "whole 16-byte reads of bins");
     const uint32_t* hist = S.h.hist[cur];
     const int top = kRBins - PER * tid;
+    // 16-byte reads: the lanes' bins are PER words apart, which as single-word reads would fall
+    // on a few LDS banks; as 16-byte reads of consecutive lanes they do not conflict
     uint32_t h[PER], mine = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      h[e] = hist[top - 1 - e];
-      mine += h[e];
+    for (int v = 0; v < PER / 4; ++v) {
+      const uint4 x = *(const uint4*)&hist[top - 4 * (v + 1)];
+      h[4 * v + 0] = x.w;
+      h[4 * v + 1] = x.z;
+      h[4 * v + 2] = x.y;
+      h[4 * v + 3] = x.x;
     }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) mine += h[e];
     uint32_t tot;
     uint32_t cum = scan(mine, &tot);
 #pragma unroll
@@ -563,12 +571,16 @@ __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&c
     keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
   int emitted = 0;
   constexpr int kWindow = WORDS * 32;
+  constexpr int WPT = WORDS / NT + 1;                  // bitmap words per thread, at most
   for (int wbase = 0; wbase < n; wbase += kWindow) {
     // the window's words that hold positions below n, dealt evenly: thread t owns wd consecutive
-    // words, so the emission order is the position order
+    // words, so the emission order is the position order. wd is odd, so that the lanes' reads,
+    // wd words apart, fall in distinct LDS banks (an even stride folds them onto a few banks).
     const int nw = min(WORDS, (n - wbase + 31) >> 5);
-    const int wd = (nw + NT - 1) / NT;
-    for (int i = tid; i < nw; i += NT) bitmap[i] = 0u;
+    const int wd = ((nw + NT - 1) / NT) | 1;
+#pragma unroll
+    for (int r = 0; r < WPT; ++r)
+      if (tid + r * NT < nw) bitmap[tid + r * NT] = 0u;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -576,17 +588,27 @@ __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&c
       if (keep[e] && q >= 0 && q < kWindow) atomicOr(&bitmap[q >> 5], 1u << (q & 31));
     }
     __syncthreads();
-    const int w0 = min(tid * wd, nw), w1 = min(w0 + wd, nw);
+    // the thread's words into registers in one burst: every read is issued (clamped into the
+    // bitmap) and the words it does not own are masked, so the reads do not wait one by one
+    const int w0 = tid * wd;
+    uint32_t wv[WPT];
     uint32_t pc = 0;
-    for (int i = w0; i < w1; ++i) pc += __builtin_popcount(bitmap[i]);
+#pragma unroll
+    for (int r = 0; r < WPT; ++r) {
+      const uint32_t x = bitmap[min(w0 + r, WORDS - 1)];
+      wv[r] = (r < wd && w0 + r < nw) ? x : 0u;
+      pc += (uint32_t)__builtin_popcount(wv[r]);
+    }
     uint32_t tot;
     int slot = emitted + (int)B.scan(pc, &tot);
-    for (int i = w0; i < w1 && slot < k; ++i) {
-      uint32_t m = bitmap[i];
+#pragma unroll
+    for (int r = 0; r < WPT; ++r) {
+      uint32_t m = wv[r];
+      const int pos0 = wbase + 32 * (w0 + r);
       while (m) {
         const int bit = __builtin_ctz(m);
         m &= m - 1;
-        if (slot < k) out[slot] = wbase + 32 * i + bit;
+        if (slot < k) out[slot] = pos0 + bit;
         ++slot;
       }
     }
