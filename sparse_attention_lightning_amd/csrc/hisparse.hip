@@ -27,6 +27,7 @@ namespace hs {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanPages = 4;                          // pages per thread and pass of the miss scan (16 measured slower)
 constexpr int kCopyThreads = 256;
 
 struct PlanLds {
@@ -90,25 +91,44 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   int32_t* vs = victim + (int64_t)b * cap;
   int parity = 0;
 
-  // ---- missing pages (selected this step, not resident), ascending
+  // ---- missing pages (selected this step, not resident), ascending: kPlanPages consecutive
+  // pages per thread and pass. Loads are clamped into the sequence's pages (and masked) rather
+  // than branched, and the next pass's go out before this pass's scan, so that the passes do
+  // not wait for memory one after another.
   uint32_t n_miss = 0;
-  for (int base = 0; base < max_pages; base += 4 * kPlanThreads) {
+  int pc_cur[kPlanPages], bt_cur[kPlanPages], pc_nxt[kPlanPages], bt_nxt[kPlanPages];
+  auto load_pages = [&](int base, int (&c)[kPlanPages], int (&t)[kPlanPages]) {
+#pragma unroll
+    for (int e = 0; e < kPlanPages; ++e) {
+      const int p = min(base + kPlanPages * tid + e, max_pages - 1);
+      c[e] = pc[p];
+      t[e] = bt[p];
+    }
+  };
+  load_pages(0, pc_cur, bt_cur);
+  for (int base = 0; base < max_pages; base += kPlanPages * kPlanThreads) {
+    load_pages(base + kPlanPages * kPlanThreads, pc_nxt, bt_nxt);
     uint32_t flags = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int p = base + 4 * tid + e;
-      if (p < max_pages && pc[p] == step && bt[p] < 0) flags |= 1u << e;
+    for (int e = 0; e < kPlanPages; ++e) {
+      const int p = base + kPlanPages * tid + e;
+      if (p < max_pages && pc_cur[e] == step && bt_cur[e] < 0) flags |= 1u << e;
     }
     uint32_t tot;
     uint32_t at = n_miss + block_scan(L, parity, (uint32_t)__builtin_popcount(flags), &tot);
     parity ^= 1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < kPlanPages; ++e)
       if ((flags >> e) & 1) {
-        if (at < (uint32_t)cap) mp[at] = base + 4 * tid + e;
+        if (at < (uint32_t)cap) mp[at] = base + kPlanPages * tid + e;
         ++at;
       }
     n_miss += tot;
+#pragma unroll
+    for (int e = 0; e < kPlanPages; ++e) {
+      pc_cur[e] = pc_nxt[e];
+      bt_cur[e] = bt_nxt[e];
+    }
   }
   if (n_miss > (uint32_t)cap) n_miss = cap;             // the host check rules this out
   if (n_miss == 0) {                                     // workgroup-uniform
@@ -119,24 +139,27 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
     return;
   }
 
-  // ---- victims: the n_miss smallest keys (clock + 1) among slots not used this step, ties to
-  // the lower slot. Radix select of the threshold key T, 8 bits at a time from the top.
-  auto key_of = [&](int s, bool& ok) -> uint32_t {
-    const int c = sc[s];
-    ok = c < step;
-    return (uint32_t)(c + 1);
-  };
+  // ---- victims: the n_miss smallest keys (clock + 1) among slots not used this step (clock
+  // below the step), ties to the lower slot. Radix select of the threshold key T, 8 bits at a
+  // time from the top. Slot clocks are read four per thread at once, clamped into the sequence's
+  // slots and masked.
   uint32_t prefix = 0;
   int need = (int)n_miss;
   if (tid == 0) L.res[0] = L.res[1] = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kPlanThreads) L.hist[i] = 0u;
     __syncthreads();
-    for (int s = tid; s < n_slots; s += kPlanThreads) {
-      bool ok;
-      const uint32_t key = key_of(s, ok);
-      const bool match = shift == 24 || (key >> (shift + 8)) == prefix;
-      if (ok && match) atomicAdd(&L.hist[(key >> shift) & 255u], 1u);
+    for (int s0 = 0; s0 < n_slots; s0 += 4 * kPlanThreads) {
+      int c[4];                                          // four clocks per thread, loaded together
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = sc[min(s0 + e * kPlanThreads + tid, n_slots - 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = (uint32_t)(c[e] + 1);
+        const bool ok = s0 + e * kPlanThreads + tid < n_slots && c[e] < step;
+        const bool match = shift == 24 || (key >> (shift + 8)) == prefix;
+        if (ok && match) atomicAdd(&L.hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (tid < 64) {                                      // wave 0: the bin of the need-th smallest
@@ -167,15 +190,15 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   uint32_t taken = 0, eq_seen = 0;
   for (int base = 0; base < n_slots; base += 4 * kPlanThreads) {
     uint32_t lt = 0, eq = 0;
+    int c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = sc[min(base + 4 * tid + e, n_slots - 1)];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int s = base + 4 * tid + e;
-      if (s < n_slots) {
-        bool ok;
-        const uint32_t key = key_of(s, ok);
-        if (ok && key < T) lt |= 1u << e;
-        if (ok && key == T) eq |= 1u << e;
-      }
+      const uint32_t key = (uint32_t)(c[e] + 1);
+      const bool ok = base + 4 * tid + e < n_slots && c[e] < step;
+      if (ok && key < T) lt |= 1u << e;
+      if (ok && key == T) eq |= 1u << e;
     }
     uint32_t tot_eq;
     uint32_t eq_before = eq_seen + block_scan(L, parity, (uint32_t)__builtin_popcount(eq), &tot_eq);
