@@ -44,7 +44,9 @@ constexpr int kDma8 = (kChunks8Wave + 63) / 64;     // 5 loads per wave and step
 constexpr int kWaveStage8 = kDma8 * 1024;           // 5 KB per wave
 constexpr int kStageBytes8 = 4 * kWaveStage8;       // 20 KB per step
 constexpr int kStages = 3;                      // LDS ring depth: rows land kStages - 1 steps ahead
-constexpr int kFragBatch = 2;                   // LDS fragments per read batch
+constexpr int kFragBatch = 2;                   // LDS fragments per read batch (32 heads per wave) ...
+constexpr int kFragBatchK16 = 4;                // ... and with 16 heads per wave: K fragments
+constexpr int kFragBatchV16 = 4;                //                                  V fragments
 constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -162,6 +164,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
   float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
   constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
+  // fragments per LDS read batch: a batch feeds FB x HT products, enough to cover the latency of
+  // the next batch's reads
+  constexpr int FBK = HT == 1 ? kFragBatchK16 : kFragBatch;
+  constexpr int FBV = HT == 1 ? kFragBatchV16 : kFragBatch;
   // The ring of gathered tiles, as three LDS variables. While a direct-to-LDS load is in flight
   // the compiler makes every LDS read that may alias its destination wait for it (a wait on the
   // vector-memory counter, i.e. for every gather issued so far); reads and loads that name
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
       const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
 
-      // LDS fragment reads go in batches of kFragBatch, double-buffered: batch b + 1 is issued
+      // LDS fragment reads go in batches of FBK, double-buffered: batch b + 1 is issued
       // right after an explicit wait for batch b and lands while batch b's products run. (While a
       // direct-to-LDS load is in flight the compiler waits for all LDS reads at every use, so
       // the distance between a read and its wait is set here, by the order of the code.)
@@ -405,30 +411,32 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
           return lds_v8bf(kb[mt][s2 & 1] + (s2 >> 1) * (kTok * 128));
         };
         constexpr int NF = 2 * (kDqk / 32);
-        static_assert(NF % kFragBatch == 0, "whole batches of K fragments");
-        v8bf kc[kFragBatch], kn[kFragBatch];
+        static_assert(NF % FBK == 0, "whole batches of K fragments");
+        v8bf kc[FBK], kn[FBK];
 #pragma unroll
-        for (int i = 0; i < kFragBatch; ++i) kc[i] = kfrag(i);
+        for (int i = 0; i < FBK; ++i) kc[i] = kfrag(i);
 #pragma unroll
-        for (int bt = 0; bt < NF / kFragBatch; ++bt) {
+        for (int bt = 0; bt < NF / FBK; ++bt) {
           wait_counts<63, 0>();
           __builtin_amdgcn_sched_barrier(0);
-          if (bt + 1 < NF / kFragBatch) {
+          if (bt + 1 < NF / FBK) {
 #pragma unroll
-            for (int i = 0; i < kFragBatch; ++i) kn[i] = kfrag((bt + 1) * kFragBatch + i);
+            for (int i = 0; i < FBK; ++i) kn[i] = kfrag((bt + 1) * FBK + i);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < kFragBatch; ++i) {
-            const int f = bt * kFragBatch + i;
+          for (int i = 0; i < FBK; ++i) {
+            const int f = bt * FBK + i;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) sacc[ht][f & 1] = mfma_bf16(kc[i], qb[ht][f >> 1], sacc[ht][f & 1]);
           }
-          static_assert(NF / kFragBatch == 2 * kSegs, "one load segment per two K fragment batches");
-          if (bt & 1) seg(bt >> 1);
+          // the step's kSegs load segments, spread evenly over the NF / FBK batches
+          constexpr int NB = NF / FBK;
+#pragma unroll
+          for (int sg = bt * kSegs / NB; sg < (bt + 1) * kSegs / NB; ++sg) seg(sg);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < kFragBatch; ++i) kc[i] = kn[i];
+          for (int i = 0; i < FBK; ++i) kc[i] = kn[i];
         }
       }
       // V^T fragments by transpose reads, tokens 4g+e (e<4), 16+4g+(e-4) (e>=4); the first batch
@@ -443,9 +451,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         const v4bf hi = lds_tr_read(vb[1][nt & 3] + (nt >> 2) * (kTok * 128));
         return (v8bf){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
-      v8bf vc[kFragBatch], vn[kFragBatch];
+      v8bf vc[FBV], vn[FBV];
 #pragma unroll
-      for (int i = 0; i < kFragBatch; ++i) vc[i] = vfrag(i);
+      for (int i = 0; i < FBV; ++i) vc[i] = vfrag(i);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax weights of heads h0 + 16 ht + c16 over tokens 16mt + 4g + r. The maximum is
@@ -491,25 +499,25 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
       // ---- O += P . V; each V fragment feeds HT products
       {
         constexpr int NV = kDv / 16;
-        static_assert(NV % kFragBatch == 0, "whole batches of V fragments");
+        static_assert(NV % FBV == 0, "whole batches of V fragments");
 #pragma unroll
-        for (int bt = 0; bt < NV / kFragBatch; ++bt) {
+        for (int bt = 0; bt < NV / FBV; ++bt) {
           wait_counts<63, 0>();
           __builtin_amdgcn_sched_barrier(0);
-          if (bt + 1 < NV / kFragBatch) {
+          if (bt + 1 < NV / FBV) {
 #pragma unroll
-            for (int i = 0; i < kFragBatch; ++i) vn[i] = vfrag((bt + 1) * kFragBatch + i);
+            for (int i = 0; i < FBV; ++i) vn[i] = vfrag((bt + 1) * FBV + i);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < kFragBatch; ++i) {
-            const int nt = bt * kFragBatch + i;
+          for (int i = 0; i < FBV; ++i) {
+            const int nt = bt * FBV + i;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma_bf16(pa[ht], vc[i], o[ht][nt]);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < kFragBatch; ++i) vc[i] = vn[i];
+          for (int i = 0; i < FBV; ++i) vc[i] = vn[i];
         }
       }
     };
