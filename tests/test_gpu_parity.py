@@ -211,6 +211,20 @@ def test_topk_rows_shorter_than_k_and_positions(form):
 
 
 @pytest.mark.parametrize("form", FORMS)
+def test_topk_odd_row_length(form):
+    # L_max % 4 != 0: rows start unaligned, so every form takes its scalar loads (each clamped
+    # into the row); visible lengths end inside and at the row, across chunk and sample edges
+    rng = np.random.default_rng(10)
+    L = 13001
+    s = rng.normal(size=(5, 1, L)).astype(np.float32)
+    s[3, 0, :] = np.round(s[3, 0, :] * 4)                       # ties at the threshold
+    lens = [L, 9999, 4097, 8193, 3]
+    for k in (2048, 1000, 5):
+        got = run_topk(s, lens, k, form=form)
+        assert np.array_equal(got, oracle_topk(s, lens, k)), k
+
+
+@pytest.mark.parametrize("form", FORMS)
 def test_topk_deterministic(form):
     rng = np.random.default_rng(9)
     s = rng.integers(0, 1000, size=(4, 1, 70000)).astype(np.float32)
