@@ -163,7 +163,6 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   float* __restrict__ lse_out = layers.lse[layer];
   part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
   float* __restrict__ part_lse = part_lse_all + layer * part_lse_stride;
-  constexpr int kDmaPerStep = kSegs * kTok / 8;      // 36 loads of 1 KB land one step
   // fragments per LDS read batch: a batch feeds FB x HT products, enough to cover the latency of
   // the next batch's reads
   constexpr int FBK = HT == 1 ? kFragBatchK16 : kFragBatch;

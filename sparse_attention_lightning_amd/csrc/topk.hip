@@ -12,7 +12,8 @@
 //            lower bound tau of the sample rank that about 2k (2.5k above 128K) of the row's
 //            scores are expected to reach.
 //   gather   chunk workgroups over the whole row append (key, position) of every score >= tau
-//            to the row's candidate list (wave-aggregated atomics; order is irrelevant).
+//            to the row's candidate list (one atomic per workgroup reserves its room; order is
+//            irrelevant).
 //   finish   one 1024-thread workgroup per row. If the list holds between k and kTkCap
 //            candidates it contains the exact top-k (all scores >= tau, and tau is at most the
 //            k-th largest); holding them in registers, the workgroup radix-selects the k-th
@@ -43,7 +44,6 @@ namespace sampled {
 constexpr int kTkThreads = 256;
 constexpr int kTkCap = 8192;               // candidates kept per row (4 x the largest k)
 constexpr int kGatherChunk = 4096;         // scores per gather workgroup (16 per thread)
-constexpr int kTkWindow = 1 << 18;         // positions per bitmap window in the finish step (32 KB)
 static_assert(kTkCap >= 2 * kMaxK, "room for about 2k candidates plus spread");
 
 struct TkRow {
