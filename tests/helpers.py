@@ -7,9 +7,17 @@ Tolerances
     rounds: |ds| <= 2^-17 * sum_h |w_h| |d_h|  (64 fp32 additions, 2^-24 each, with margin).
   scores (general E4M3 inputs): the FP8 matrix cores truncate each product of a group of 8 to
     a grid 13 binades below the group's largest product (measured on gfx950: 256 + 2^-5 is
-    kept, 256 + 2^-6 comes back as 256). Per group that is < 8 * 2^-13 * max|p| <= 2^-10 *
-    sum|p|, so |d_gpu - d| <= 2^-10 * sum_i |q_i k_i| per head, and
-    |ds| <= 2^-10 * sum_h |w_h| sum_i |q_hi k_ti| + 2^-16 * sum_h |w_h| |d_h|.
+    kept, 256 + 2^-6 comes back as 256). Both scan kernels feed each lane 16 consecutive dims
+    per 16-byte half of its operand, so a group is 8 consecutive dims [8a, 8a + 8). A product
+    already on its group's grid 2^(e_g - 13) (e_g the binade of the group's largest |product|)
+    loses nothing; any other loses less than one grid step. Per head
+      |d_gpu - d| <= sum_g (off-grid products of g) * 2^(e_g - 13) + 2^-20 * sum_i |q_i k_i|
+    (the second term: the fp32 accumulation of the 16 group sums), and
+    |ds| <= sum_h |w_h| * that + 2^-16 * sum_h |w_h| |d_h| (the fp32 head sum). On N(0,1)
+    inputs about 1.7% of products are off their grid, and the bound is about 1/100 of the
+    coarser 2^-10 * sum_h |w_h| sum_i |q_hi k_ti| that ignores which products lose bits. Rows
+    longer than 2^18 keys take the per-group bound at 2^18 evenly spaced keys and the coarser
+    one at the others (the per-group count costs about 35 s of host time per 1M keys).
   top-k sets: equal, except that tokens whose exact score lies within 1e-3 * |s_k| of the
     exact k-th largest score s_k may swap; the set sizes are equal.
   top-k on identical float32 scores: bit-exact (integer work).
@@ -27,7 +35,11 @@ import torch
 import oracle
 from oracle.dsa import Cache as OCache
 
-SCORE_REL_GENERAL = 2.0 ** -10
+SCORE_FP8_GRID = 13          # binades between a product group's largest product and its grid
+SCORE_REL_COARSE = 2.0 ** -10  # the per-group bound's worst case, relative to sum_i |q_i k_i|
+SCORE_SHARP_ROWS = 1 << 18   # keys per row that take the per-group bound
+SCORE_GROUP = 8              # products per truncation group
+SCORE_REL_ACC = 2.0 ** -20
 SCORE_REL_FP32 = 2.0 ** -16
 SCORE_REL_INT = 2.0 ** -17
 TOPK_SWAP_REL = 1e-3
@@ -58,6 +70,43 @@ def latent_cache(batch, layer=0):
     return OCache(data, None if tab is None else np_(tab), wl.page_size)
 
 
+def _e4m3_binades(codes):
+    """Per E4M3FN code with value m * 2^E (m the integer mantissa, 0..15): the binade of its top
+    bit T = floor(log2 m) + E, of its lowest set bit L = ctz(m) + E, and its mantissa scaled into
+    8..15, a = m * 2^(3 - floor(log2 m)). Zero gets T = -100, L = 100, a = 0."""
+    c = np.asarray(codes, dtype=np.int16)
+    e, f = (c >> 3) & 15, c & 7
+    m = np.where(e == 0, f, f + 8)
+    E = np.where(e == 0, -9, e - 10)
+    lg = np.floor(np.log2(np.maximum(m, 1))).astype(np.int16)
+    ctz = np.array([0, 0, 1, 0, 2, 0, 1, 0, 3, 0, 1, 0, 2, 0, 1, 0], dtype=np.int16)[m]
+    z = m == 0
+    T = np.where(z, -100, lg + E).astype(np.int16)
+    L = np.where(z, 100, ctz + E).astype(np.int16)
+    a = np.where(z, 0, m << (3 - lg)).astype(np.int16)
+    return torch.from_numpy(T), torch.from_numpy(L), torch.from_numpy(a)
+
+
+def _truncation_bound(q_codes, k_codes, aw):
+    """sum_h |w_h| sum_g (off-grid products of g) * 2^(e_g - 13) for every key row (see the
+    module docstring), from the products' binades alone: the product of two codes has its top
+    bit at T_q + T_k (+ 1 when a_q a_k >= 128) and its lowest set bit at L_q + L_k."""
+    Tq, Lq, aq = _e4m3_binades(q_codes)               # [Hi, D]
+    Tk, Lk, ak = _e4m3_binades(k_codes)               # [n, D]
+    Hi, D = Tq.shape
+    G = D // SCORE_GROUP
+    w = torch.as_tensor(aw, dtype=torch.float64)
+    out = torch.empty(Tk.shape[0], dtype=torch.float64)
+    for s in range(0, Tk.shape[0], 2048):
+        top = Tk[s:s + 2048, None, :] + Tq[None, :, :] + (ak[s:s + 2048, None, :] * aq[None, :, :] >= 128)
+        low = Lk[s:s + 2048, None, :] + Lq[None, :, :]
+        g = top.view(-1, Hi, G, SCORE_GROUP).amax(-1, keepdim=True) - SCORE_FP8_GRID
+        off = (low.view(-1, Hi, G, SCORE_GROUP) < g).sum(-1)
+        step = torch.exp2(g.squeeze(-1).to(torch.float64))
+        out[s:s + 2048] = (off.to(torch.float64) * step).sum(-1) @ w
+    return out.numpy()
+
+
 def score_tolerance(q_codes, w, key_rows_codes, integer_inputs=False):
     """Per-token tolerance of GPU scores for one query (see module docstring)."""
     q = oracle.e4m3_to_f64(q_codes)
@@ -67,8 +116,15 @@ def score_tolerance(q_codes, w, key_rows_codes, integer_inputs=False):
     mag = np.abs(d) @ aw
     if integer_inputs:
         return SCORE_REL_INT * mag
-    l1 = np.abs(k) @ np.abs(q).T
-    return SCORE_REL_GENERAL * (l1 @ aw) + SCORE_REL_FP32 * mag
+    l1 = (np.abs(k) @ np.abs(q).T) @ aw
+    n = k.shape[0]
+    if n <= SCORE_SHARP_ROWS:
+        trunc = _truncation_bound(q_codes, key_rows_codes, aw)
+    else:
+        trunc = SCORE_REL_COARSE * l1
+        pick = np.unique(np.linspace(0, n - 1, SCORE_SHARP_ROWS).astype(np.int64))
+        trunc[pick] = _truncation_bound(q_codes, np.asarray(key_rows_codes)[pick], aw)
+    return trunc + SCORE_REL_ACC * l1 + SCORE_REL_FP32 * mag
 
 
 def check_scores(gpu_row, exact_row, tol, p):
