@@ -21,8 +21,10 @@
 // is why the softmax keeps one reference per head instead of rescaling O (see the kernel).
 // The softmax runs in the log2 domain in fp32; P is rounded to bf16 for PV, and the output is
 // normalised by the sum of those rounded weights (lse by the sum of the fp32 ones).
-// With several splits, each workgroup writes its normalised partial (o_s, lse_s) in fp32 and a
-// combine kernel merges them: lse = log sum_s exp lse_s, o = sum_s exp(lse_s - lse) o_s.
+// With several splits, each workgroup writes its partial in fp32 as it stands in the
+// accumulators, with lse_s and the factor f_s that normalises it (1 / its weight sum, times the
+// cache scale for E4M3 rows), and a combine kernel merges them: lse = log sum_s exp lse_s,
+// o = sum_s exp(lse_s - lse) f_s o_s.
 #include <algorithm>
 #include <type_traits>
 
@@ -51,8 +53,8 @@ constexpr float kRefHeadroom = 64.f;            // log2 headroom of P above the 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Split partials: normalised outputs o_s and lse_s, both fp32. (bf16 partials lose up to 2^-9
-// of |o_s|, which is more than 2e-2 once outputs reach about 10.)
+// Split partials: unnormalised outputs o_s, with lse_s and the normalising factor f_s, all fp32.
+// (bf16 partials lose up to 2^-9 of |o_s|, which is more than 2e-2 once outputs reach about 10.)
 typedef float part_t;
 
 // Per-layer arguments of a launch over up to kMlaMaxLayers layers that share one index set
@@ -92,9 +94,9 @@ int sparse_mla_splits(int rows, int H, int k, int nl, bool f8) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Split partials of one launch of nl layers: per layer [rows][splits][H][512] part_t, then
-// [rows][splits][H] fp32 lse.
+// [rows][splits][H] fp32 lse followed by [rows][splits][H] fp32 normalising factors.
 static size_t part_o_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * kDv * sizeof(part_t)); }
-static size_t part_lse_layer(int rows, int splits, int H) { return align256((size_t)rows * splits * H * sizeof(float)); }
+static size_t part_lse_layer(int rows, int splits, int H) { return align256(2 * (size_t)rows * splits * H * sizeof(float)); }
 static size_t launch_ws_bytes(int rows, int H, int k, int nl, bool f8) {
   const int s = sparse_mla_splits(rows, H, k, nl, f8);
   if (s == 1) return 0;
@@ -154,7 +156,8 @@ template <int NW, int HT, bool SPLIT, bool F8>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, int Q, int H, int splits,
     int split_len, float scale_log2, float out_scale, part_t* __restrict__ part_o_all,
-    float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride, int n_hg, int n_units) {
+    float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride, int64_t nrm_off, int n_hg,
+    int n_units) {
   // layer blockIdx.y of the launch: its query, latent cache, outputs and partials
   const int layer = blockIdx.y;
   const uint16_t* __restrict__ q = layers.q[layer];
@@ -587,23 +590,29 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const float l_tot = sum_xor32(sum_xor16(l_run[ht]));
     const float lpv_tot = sum_xor32(sum_xor16(l_pv[ht]));
     const float lse_h = (l_tot > 0.f) ? (m_ref[ht] + log2f(l_tot)) * kLn2 : -INFINITY;
-    float inv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(lpv_tot, 4 * g + r, 64);
-      inv[r] = lr > 0.f ? 1.f / lr : 0.f;
-      if constexpr (F8) inv[r] *= out_scale;         // the FP8 cache's scale on the values
-    }
     const int hb = h0 + 16 * ht;
     if (SPLIT) {
+      // the partial as the accumulators hold it; the combine applies the factor
       const int64_t ps = (int64_t)bq * splits + split;
       part_t* pbase = part_o + (ps * H + hb) * kDv;
-      if (g == 0) part_lse[ps * H + hb + c16] = lse_h;
+      if (g == 0) {
+        float f = lpv_tot > 0.f ? 1.f / lpv_tot : 0.f;
+        if constexpr (F8) f *= out_scale;             // the FP8 cache's scale on the values
+        part_lse[ps * H + hb + c16] = lse_h;
+        part_lse[nrm_off + ps * H + hb + c16] = f;
+      }
 #pragma unroll
       for (int nt = 0; nt < kDv / 16; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pbase[(4 * g + r) * kDv + 16 * nt + c16] = (part_t)(o[ht][nt][r] * inv[r]);
+        for (int r = 0; r < 4; ++r) pbase[(4 * g + r) * kDv + 16 * nt + c16] = (part_t)o[ht][nt][r];
     } else {
+      float inv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float lr = __shfl(lpv_tot, 4 * g + r, 64);
+        inv[r] = lr > 0.f ? 1.f / lr : 0.f;
+        if constexpr (F8) inv[r] *= out_scale;       // the FP8 cache's scale on the values
+      }
       float* obase = out + ((int64_t)bq * H + hb) * kDv;
       if (g == 0 && lse_out) lse_out[(int64_t)bq * H + hb + c16] = lse_h;
 #pragma unroll
@@ -619,7 +628,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 // merge, so the loads overlap.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
                                                           const float* __restrict__ part_lse_all, int H, int splits,
-                                                          int64_t part_o_stride, int64_t part_lse_stride) {
+                                                          int64_t part_o_stride, int64_t part_lse_stride,
+                                                          int64_t nrm_off) {
   typedef part_t p8 __attribute__((ext_vector_type(8)));
   const int layer = blockIdx.y;
   const part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
@@ -629,12 +639,13 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
   const int hl = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int bq = blockIdx.x / (H / 4);
   const int h = (blockIdx.x - bq * (H / 4)) * 4 + hl;
-  float ls[kMaxSplits];
+  float ls[kMaxSplits], nr[kMaxSplits];
   p8 po[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     const int64_t ps = (int64_t)bq * splits + s;
     ls[s] = s < splits ? part_lse[ps * H + h] : -INFINITY;
+    nr[s] = s < splits ? part_lse[nrm_off + ps * H + h] : 0.f;
     if (s < splits) po[s] = *(const p8*)(part_o + (ps * H + h) * kDv + 8 * t);
   }
   float mx = -INFINITY;
@@ -648,8 +659,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
       if (s < splits) {
         const float wgt = expf(ls[s] - mx);
         den += wgt;
+        const float c = wgt * nr[s];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e >> 2][e & 3] += wgt * (float)po[s][e];
+        for (int e = 0; e < 8; ++e) acc[e >> 2][e & 3] += c * (float)po[s][e];
       }
     }
     const float inv = 1.f / den;
@@ -667,12 +679,13 @@ static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L,
                        int idx_q_stride, int Q, int H, int split_len, float sl2, float out_scale, part_t* part_o,
                        float* part_lse, int64_t so, int64_t sl, int n_hg, int units) {
   const dim3 block(NW * 64);
+  const int64_t nrm_off = (int64_t)units * H;          // the factors follow the units' lse
   if (splits == 1)
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
-                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, n_hg, units);
+                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, (int64_t)0, n_hg, units);
   else
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H,
-                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, n_hg, units);
+                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, nrm_off, n_hg, units);
 }
 
 // latent_scale > 0: FP8 latent rows (576 E4M3 codes, value = latent_scale x code); 0: bf16 rows
@@ -727,7 +740,7 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
                               part_lse, so, sl, n_hg, units);
     if (splits > 1)
       hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 4), (unsigned)nl), dim3(256), 0, s, L,
-                         part_o, part_lse, H, splits, so, sl);
+                         part_o, part_lse, H, splits, so, sl, (int64_t)units * H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

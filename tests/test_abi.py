@@ -215,7 +215,7 @@ def test_workspace_sizes_scale_with_batch():
     # partials, and a launch splits its tokens over all its layers: 8 tokens x 1 layer take 16
     # splits; bf16 rows at 8 x 4 take 4 splits x 2 head groups, FP8 rows 8 splits x 1 group, and
     # the size covers the larger (8 x 4: 8 splits, 8 x 8: 4); 20 layers go as 8 + 8 + 4
-    P = 8 * 128 * 512 * 4 + 8 * 128 * 4          # fp32 partial and lse of one split of 8 tokens x 128 heads
+    P = 8 * 128 * 512 * 4 + 2 * 8 * 128 * 4      # fp32 partial, lse and factor of one split of 8 tokens x 128 heads
     base = dsa.workspace_size(dsa.OP_FORWARD_SHARED, 8, 1, 1 << 20, n_layers=1) - \
         dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
     mla1 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 8, 1, 1 << 20)
