@@ -2,16 +2,15 @@
 // compressed along the sequence by 4, DSA's top-k selection over the compressed entries, and a
 // sliding window of the last 128 raw tokens; HCA compresses by 128 and attends densely).
 //
-// The path reuses the DSA kernels on the compressed caches and adds two small kernels:
+// The path reuses the DSA kernels on the compressed caches and adds one small kernel:
 //   csa_prep_kernel   per query token at raw position p: the position of its last visible
 //                     compressed entry, (p + 1) / ratio - 1 (an entry is visible once its last
 //                     raw token is; -1 when none is), and the window's index list
 //                     max(0, p - window + 1) .. p, padded with -1;
-//   (indexer scan, top-k and sparse MLA over the compressed caches with those positions;
-//    sparse MLA over the raw latent cache with the window lists)
-//   csa_merge_kernel  one softmax over both sets, from the two partial attentions by their
-//                     log-sum-exp: lse = log(e^lse_c + e^lse_w),
-//                     o = e^(lse_c - lse) o_c + e^(lse_w - lse) o_w.
+//   (indexer scan and top-k over the compressed keys with those positions; then one sparse MLA
+//    launch over the union of the two lists, the selected compressed rows of the compressed
+//    latent cache and the window's rows of the raw latent cache, in one softmax: its splits run
+//    over the two lists one after the other, and its combine merges them)
 #include <algorithm>
 
 #include "dsa_device.h"
@@ -41,29 +40,6 @@ __global__ __launch_bounds__(256) void csa_prep_kernel(const int32_t* __restrict
   }
 }
 
-// In place: out holds the window's attention (o_w) on entry and the merged result on exit.
-// One thread per 4 dims of one (query token, head).
-__global__ __launch_bounds__(256) void csa_merge_kernel(const float* __restrict__ o_c, const float* __restrict__ lse_c,
-                                                        const float* __restrict__ lse_w, float* __restrict__ out,
-                                                        float* __restrict__ lse, int64_t n_heads) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rh = t >> 7;                         // 128 threads x 4 dims per head
-  if (rh >= n_heads) return;
-  const float lc = lse_c[rh], lw = lse_w[rh];
-  const float m = fmaxf(lc, lw);
-  v4f r = {0.f, 0.f, 0.f, 0.f};
-  float l = -INFINITY;
-  if (m != -INFINITY) {
-    const float wc = expf(lc - m), ww = expf(lw - m);
-    const float inv = 1.f / (wc + ww);
-    const v4f a = *(const v4f*)(o_c + t * 4), c = *(const v4f*)(out + t * 4);
-    r = (wc * inv) * a + (ww * inv) * c;
-    l = m + logf(wc + ww);
-  }
-  *(v4f*)(out + t * 4) = r;
-  if (lse && (t & 127) == 0) lse[rh] = l;
-}
-
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct CsaWs {
@@ -71,9 +47,6 @@ struct CsaWs {
   void* topk;
   int32_t* qpos_c;
   int32_t* idx_w;
-  float* o_c;
-  float* lse_c;
-  float* lse_w;
   void* mla;
 };
 
@@ -87,14 +60,7 @@ static CsaWs csa_carve(void* ws, int rows, int Lc_max, int H, int k, int window,
     w.qpos_c = (int32_t*)take((size_t)rows * sizeof(int32_t));
   }
   if (window > 0) w.idx_w = (int32_t*)take((size_t)rows * window * sizeof(int32_t));
-  if (k > 0 && window > 0) {
-    w.o_c = (float*)take((size_t)rows * H * kDv * sizeof(float));
-    w.lse_c = (float*)take((size_t)rows * H * sizeof(float));
-    w.lse_w = (float*)take((size_t)rows * H * sizeof(float));
-  }
-  size_t mla = 0;
-  if (k > 0) mla = std::max(mla, sparse_mla_workspace_bytes(rows, H, k, 1));
-  if (window > 0) mla = std::max(mla, sparse_mla_workspace_bytes(rows, H, window, 1));
+  const size_t mla = sparse_mla_workspace_bytes(rows, H, k + window, 1);
   w.mla = mla ? take(mla) : nullptr;
   *total = (size_t)(p - (char*)ws);
   return w;
@@ -120,32 +86,18 @@ hipError_t launch_csa(const HostBatch& bt, const uint8_t* q_e4m3, const float* w
                      W.qpos_c, W.idx_w, (k > 0 && keep_all) ? idx_out : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool both = k > 0 && window > 0;
-  if (k > 0) {
-    // the compressed caches, addressed like any cache of Lc_max rows per sequence, with each
-    // query at its last visible compressed entry
-    const HostBatch bc{bt.B, bt.Q, Lc_max, bt.seq_lens, W.qpos_c, bt.Q};
-    if (!keep_all) {
-      if ((e = launch_index_score(bc, q_e4m3, w, Hi, keys_c, W.scores, s)) != hipSuccess) return e;
-      if ((e = launch_topk(bc, W.scores, k, idx_out, W.topk, s)) != hipSuccess) return e;
-    }
-    if ((e = launch_sparse_mla(bc, q_bf16, H, latent_c, idx_out, k, k, scale, both ? W.o_c : out,
-                               both ? W.lse_c : lse, W.mla, s)) != hipSuccess)
-      return e;
+  if (k == 0)                                        // the window alone
+    return launch_sparse_mla(bt, q_bf16, H, latent, W.idx_w, window, window, scale, out, lse, W.mla, s);
+  // the compressed caches, addressed like any cache of Lc_max rows per sequence, with each query
+  // at its last visible compressed entry
+  const HostBatch bc{bt.B, bt.Q, Lc_max, bt.seq_lens, W.qpos_c, bt.Q};
+  if (!keep_all) {
+    if ((e = launch_index_score(bc, q_e4m3, w, Hi, keys_c, W.scores, s)) != hipSuccess) return e;
+    if ((e = launch_topk(bc, W.scores, k, idx_out, W.topk, s)) != hipSuccess) return e;
   }
-  if (window > 0) {
-    if ((e = launch_sparse_mla(bt, q_bf16, H, latent, W.idx_w, window, window, scale, out, both ? W.lse_w : lse,
-                               W.mla, s)) != hipSuccess)
-      return e;
-  }
-  if (both) {
-    const int64_t n_heads = (int64_t)rows * H;
-    const int64_t threads = n_heads * (kDv / 4);
-    hipLaunchKernelGGL(csa_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, W.o_c, W.lse_c,
-                       W.lse_w, out, lse, n_heads);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (window == 0) return launch_sparse_mla(bc, q_bf16, H, latent_c, idx_out, k, k, scale, out, lse, W.mla, s);
+  return launch_sparse_mla_union(bc, q_bf16, H, latent_c, idx_out, k, k, latent, bt.L_max, W.idx_w, window, window,
+                                 scale, out, lse, W.mla, s);
 }
 
 }  // namespace dsa

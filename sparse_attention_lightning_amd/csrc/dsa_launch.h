@@ -35,6 +35,12 @@ size_t sparse_mla_workspace_bytes(int rows, int H, int k, int n_layers);
 hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                              const int32_t* idx, int k, int idx_q_stride, float scale, float* out,
                              float* lse, void* ws, hipStream_t s);
+// One softmax over the union of two index lists: idx (k entries per query token) over latent
+// (bt.L_max rows per sequence) and idx2 (k2 entries) over latent2 (L_max2 rows per sequence).
+hipError_t launch_sparse_mla_union(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
+                                   const int32_t* idx, int k, int idx_q_stride, const HostCache& latent2, int L_max2,
+                                   const int32_t* idx2, int k2, int idx2_q_stride, float scale, float* out, float* lse,
+                                   void* ws, hipStream_t s);
 // FP8 latent rows: 576 OCP E4M3 codes per token, value = latent_scale x code (latent_scale > 0)
 hipError_t launch_sparse_mla_fp8(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
                                  float latent_scale, const int32_t* idx, int k, int idx_q_stride, float scale,
@@ -48,8 +54,8 @@ hipError_t launch_sparse_mla_layers_fp8(const HostBatch& bt, const uint16_t* con
                                         float scale, float* const* out, float* const* lse, int n_layers, void* ws,
                                         hipStream_t s);
 
-// Compressed sparse attention: the DSA kernels over compressed caches plus a raw sliding window,
-// merged by log-sum-exp. Workspace layout owned by csa.hip.
+// Compressed sparse attention: the DSA scan and top-k over compressed caches, then one attention
+// over the selected compressed rows and a raw sliding window. Workspace layout owned by csa.hip.
 size_t csa_workspace_bytes(int B, int Q, int L_max, int H, int ratio, int k, int window);
 hipError_t launch_csa(const HostBatch& bt, const uint8_t* q_e4m3, const float* w, int Hi, const HostCache& keys_c,
                       const HostCache& latent_c, const HostCache& latent, int ratio, int k, int window,

@@ -57,6 +57,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (bf16 partials lose up to 2^-9 of |o_s|, which is more than 2e-2 once outputs reach about 10.)
 typedef float part_t;
 
+// The second index list of a union launch: compressed sparse attention attends, in one softmax,
+// over the selected compressed rows (the first list, over the layer's cache) and the window's raw
+// rows (this list, over its own cache). k = 0 in every other launch.
+struct MlaSecond {
+  CacheView lat;
+  const int32_t* idx;
+  int k, idx_q_stride;
+};
+
 // Per-layer arguments of a launch over up to kMlaMaxLayers layers that share one index set
 // (IndexShare): blockIdx.y picks the layer.
 struct MlaLayers {
@@ -88,6 +97,7 @@ int sparse_mla_splits(int rows, int H, int k, int nl, bool f8) {
   };
   int s = 1;
   while (wgs(s) < kTargetWgs && (k + 2 * s - 1) / (2 * s) >= kMinSplit && s < kMaxSplits) s *= 2;
+  while ((k + s - 1) / s > kMaxK && s < kMaxSplits) s *= 2;   // a split's row ids fit the LDS list
   return s;
 }
 
@@ -154,7 +164,8 @@ __device__ __forceinline__ void wait_counts() {
 
 template <int NW, int HT, bool SPLIT, bool F8>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
-    MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, int Q, int H, int splits,
+    MlaLayers layers, const int32_t* __restrict__ idx, int k, int idx_q_stride, MlaSecond sec, int Q, int H,
+    int splits,
     int split_len, float scale_log2, float out_scale, part_t* __restrict__ part_o_all,
     float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride, int64_t nrm_off, int n_hg,
     int n_units) {
@@ -213,9 +224,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   const int h0 = (hg * NW + wave) * 16 * HT;           // this wave's heads: tile ht = h0 + 16 ht ..
   constexpr int my_dma = kSegs;                        // loads this wave issues per step
 
+  // The split's tokens: positions tok_begin .. tok_end of the list, or of the two lists one after
+  // the other in a union launch (token t >= k is entry t - k of the second list).
   const int32_t* irow = idx + (int64_t)b * (idx_q_stride ? (int64_t)Q * k : k) + (int64_t)j * idx_q_stride;
+  const bool two = sec.k > 0;                          // launch-uniform
+  const int32_t* irow2 =
+      two ? sec.idx + (int64_t)b * (sec.idx_q_stride ? (int64_t)Q * sec.k : sec.k) + (int64_t)j * sec.idx_q_stride
+          : nullptr;
   const int tok_begin = split * split_len;
-  const int tok_end = min(k, tok_begin + split_len);
+  const int tok_end = min(k + sec.k, tok_begin + split_len);
   const int n_steps = tok_end > tok_begin ? (tok_end - tok_begin + kTok - 1) / kTok : 0;
 
   // Direct-to-LDS gather of step st: load d = (row group rg = d % 4, segment d / 4) lands rows
@@ -227,9 +244,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   // Steps past the last one load row 0 into a slot that is read no more: every step issues the
   // same loads, so the number of loads in flight is the same on every path.
   auto step_row = [&](int st) { return st < n_steps ? rowid[st * kTok + my_row] : -1; };
-  auto row_src = [&](int r) -> const uint8_t* {
-    return lat.base + (r >= 0 ? (int64_t)r * kRowBytes : 0) + 16 * ((lane & 7) ^ (my_row & 7));
+  // row ids: r >= 0 a row of the layer's cache, r <= -2 row -2 - r of the second list's cache,
+  // -1 a masked token (its loads read row 0, and its tile row is zeroed)
+  auto row_base = [&](int r, int64_t row_bytes) -> const uint8_t* {
+    if (r >= 0) return lat.base + (int64_t)r * row_bytes;
+    if (r <= -2) return sec.lat.base + (int64_t)(-2 - r) * row_bytes;
+    return lat.base;
   };
+  auto row_src = [&](int r) -> const uint8_t* { return row_base(r, kRowBytes) + 16 * ((lane & 7) ^ (my_row & 7)); };
   auto step_src = [&](int st) { return row_src(step_row(st)); };
   auto issue_seg = [&](const uint8_t* src, auto slot, int sg) {
     uint8_t* base = ring_of(slot) + wave * 1024;
@@ -250,16 +272,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   const int n_tok = n_steps * kTok;
   constexpr int kPerThread = kMaxK / (NW * 64);
   int pos_t[kPerThread], page_t[kPerThread] = {};
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int i = tid + e * NW * 64;
-    pos_t[e] = (i < n_tok && tok_begin + i < tok_end) ? irow[tok_begin + i] : -1;
-  }
   const int32_t* trow = lat.table ? lat.table + (int64_t)b * lat.max_pages : nullptr;
-  if (trow) {                                          // block-uniform
-    const uint32_t ps = (uint32_t)lat.page_size;
+  const int32_t* trow2 = two && sec.lat.table ? sec.lat.table + (int64_t)b * sec.lat.max_pages : nullptr;
+  if (!two) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) page_t[e] = trow[(uint32_t)max(pos_t[e], 0) / ps];
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = tid + e * NW * 64;
+      pos_t[e] = (i < n_tok && tok_begin + i < tok_end) ? irow[tok_begin + i] : -1;
+    }
+    if (trow) {                                        // block-uniform
+      const uint32_t ps = (uint32_t)lat.page_size;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) page_t[e] = trow[(uint32_t)max(pos_t[e], 0) / ps];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int t = tok_begin + tid + e * NW * 64;
+      const int32_t* src = t < k ? irow + t : irow2 + (t - k);
+      pos_t[e] = (tid + e * NW * 64 < n_tok && t < tok_end) ? *src : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const bool s2 = tok_begin + tid + e * NW * 64 >= k;
+      const int32_t* tr = s2 ? trow2 : trow;
+      const uint32_t ps = (uint32_t)(s2 ? sec.lat.page_size : lat.page_size);
+      if (tr) page_t[e] = tr[(uint32_t)max(pos_t[e], 0) / ps];
+    }
   }
 
   // query heads h0 + 16 ht + (l % 16) as the B operands of S^T = K . Q^T: 8 dims per lane per K step
@@ -276,8 +315,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   for (int e = 0; e < kPerThread; ++e) {
     const int i = tid + e * NW * 64;
     const int pos = pos_t[e];
-    if (i < n_tok)
-      rowid[i] = pos < 0 ? -1 : trow ? page_t[e] * lat.page_size + pos % lat.page_size : b * lat.L_max + pos;
+    if (i < n_tok) {
+      if (!two || tok_begin + i < k)
+        rowid[i] = pos < 0 ? -1 : trow ? page_t[e] * lat.page_size + pos % lat.page_size : b * lat.L_max + pos;
+      else
+        rowid[i] = pos < 0 ? -1
+                           : -2 - (trow2 ? page_t[e] * sec.lat.page_size + pos % sec.lat.page_size
+                                         : b * sec.lat.L_max + pos);
+    }
   }
   __syncthreads();
 
@@ -293,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const int i = d * 64 + ln;
     const int rl = i / 36, c = i - 36 * (i / 36);
     const int r = (i < kChunks8Wave && st < n_steps) ? rowid[st * kTok + 8 * wave + rl] : -1;
-    const uint8_t* src = lat.base + (r >= 0 ? (int64_t)r * kRowBytes8 + 16 * c : 0);
+    const uint8_t* src = row_base(r, kRowBytes8) + (r != -1 ? 16 * c : 0);
     __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + d * 1024),
                                      16, 0, 0);
   };
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         const int rl = i / 36, c = i - 36 * (i / 36);
         const int row = 8 * wave + rl;
         v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-        if (rowid[st * kTok + row] >= 0) {
+        if (rowid[st * kTok + row] != -1) {
           const v4i x = *(const v4i*)(sb + 16 * i);      // dims 16c .. 16c + 15
           lo = (v4i){(int)two(x[0], false), (int)two(x[0], true), (int)two(x[1], false), (int)two(x[1], true)};
           hi = (v4i){(int)two(x[2], false), (int)two(x[2], true), (int)two(x[3], false), (int)two(x[3], true)};
@@ -334,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 
   // masked rows this wave landed: overwrite the dummy bytes with zeros
   auto zero_masked = [&](int st, auto slot) {
-    if (rowid[st * kTok + my_row] >= 0) return;
+    if (rowid[st * kTok + my_row] != -1) return;
     uint8_t* base = ring_of(slot) + wave * 1024;
 #pragma unroll
     for (int sg = 0; sg < kSegs; ++sg) *(v4i*)(base + sg * (kTok * 128) + 16 * lane) = (v4i){0, 0, 0, 0};
@@ -390,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     // matrix cores run through those holds.
     auto compute = [&](int st, const uint8_t* tile, auto seg) {
       // one validity bit per token of the step (lanes 32..63 repeat lanes 0..31)
-      const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] >= 0);
+      const uint32_t valid = (uint32_t)__ballot(rowid[st * kTok + (lane & 31)] != -1);
 
       // LDS fragment reads go in batches of FBK, double-buffered: batch b + 1 is issued
       // right after an explicit wait for batch b and lands while batch b's products run. (While a
@@ -676,25 +721,45 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
 
 template <int NW, int HT, bool F8>
 static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L, const int32_t* idx, int k,
-                       int idx_q_stride, int Q, int H, int split_len, float sl2, float out_scale, part_t* part_o,
-                       float* part_lse, int64_t so, int64_t sl, int n_hg, int units) {
+                       int idx_q_stride, const MlaSecond& sec, int Q, int H, int split_len, float sl2,
+                       float out_scale, part_t* part_o, float* part_lse, int64_t so, int64_t sl, int n_hg,
+                       int units) {
   const dim3 block(NW * 64);
   const int64_t nrm_off = (int64_t)units * H;          // the factors follow the units' lse
   if (splits == 1)
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H, 1,
-                       split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, (int64_t)0, n_hg, units);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, sec, Q,
+                       H, 1, split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, (int64_t)0, n_hg,
+                       units);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, Q, H,
-                       splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, nrm_off, n_hg, units);
+    hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, sec, Q,
+                       H, splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, nrm_off, n_hg, units);
 }
+
+// The second list of a union launch (one layer), with its own cache of L_max rows per sequence.
+struct HostSecond {
+  HostCache latent;
+  const int32_t* idx;
+  int k, idx_q_stride, L_max;
+};
 
 // latent_scale > 0: FP8 latent rows (576 E4M3 codes, value = latent_scale x code); 0: bf16 rows
 static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, int H, const HostCache* latents,
                                 float latent_scale, const int32_t* idx, int k, int idx_q_stride, float scale,
-                                float* const* out, float* const* lse, int n_layers, void* ws, hipStream_t s) {
+                                float* const* out, float* const* lse, int n_layers, void* ws, hipStream_t s,
+                                const HostSecond* second = nullptr) {
   const int rows = bt.B * bt.Q;
   const bool f8 = latent_scale > 0.f;
   const float sl2 = scale * (f8 ? latent_scale : 1.f) * kLog2e;
+  MlaSecond sec{};
+  if (second) {
+    const HostCache& c = second->latent;
+    sec.lat = CacheView{(const uint8_t*)c.base, c.table, c.max_pages, c.page_size, f8 ? kRowBytes8 : kRowBytes,
+                        second->L_max};
+    sec.idx = second->idx;
+    sec.k = second->k;
+    sec.idx_q_stride = second->idx_q_stride;
+  }
+  const int k_all = k + sec.k;
   for (int l0 = 0; l0 < n_layers; l0 += kMlaMaxLayers) {
     const int nl = std::min(kMlaMaxLayers, n_layers - l0);
     MlaLayers L{};
@@ -706,8 +771,8 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
       L.out[i] = out[l0 + i];
       L.lse[i] = lse ? lse[l0 + i] : nullptr;
     }
-    const int splits = sparse_mla_splits(rows, H, k, nl, f8);
-    int split_len = (k + splits - 1) / splits;
+    const int splits = sparse_mla_splits(rows, H, k_all, nl, f8);
+    int split_len = (k_all + splits - 1) / splits;
     split_len = (split_len + kTok - 1) / kTok * kTok;
     part_t* part_o = nullptr;
     float* part_lse = nullptr;
@@ -727,16 +792,16 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
     const dim3 grid(n_hg == 1 ? (unsigned)units : (unsigned)((units + 7) / 8 * 8 * n_hg), (unsigned)nl);
     const float os = f8 ? latent_scale : 1.f;
     if (f8 && H == 128 && n_hg == 1)
-      launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o, part_lse,
-                             so, sl, 1, units);
+      launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
+                             part_lse, so, sl, 1, units);
     else if (f8)
-      launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o, part_lse,
-                             so, sl, n_hg, units);
+      launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
+                             part_lse, so, sl, n_hg, units);
     else if (H == 128 && n_hg == 1)
-      launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o,
+      launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
                               part_lse, so, sl, 1, units);
     else
-      launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, bt.Q, H, split_len, sl2, os, part_o,
+      launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
                               part_lse, so, sl, n_hg, units);
     if (splits > 1)
       hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)rows * (H / 4), (unsigned)nl), dim3(256), 0, s, L,
@@ -774,6 +839,16 @@ hipError_t launch_sparse_mla(const HostBatch& bt, const uint16_t* q, int H, cons
                              void* ws, hipStream_t s) {
   float* lse_arr[1] = {lse};
   return launch_layers(bt, &q, H, &latent, 0.f, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr, 1, ws, s);
+}
+
+hipError_t launch_sparse_mla_union(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
+                                   const int32_t* idx, int k, int idx_q_stride, const HostCache& latent2, int L_max2,
+                                   const int32_t* idx2, int k2, int idx2_q_stride, float scale, float* out, float* lse,
+                                   void* ws, hipStream_t s) {
+  float* lse_arr[1] = {lse};
+  const HostSecond second{latent2, idx2, k2, idx2_q_stride, L_max2};
+  return launch_layers(bt, &q, H, &latent, 0.f, idx, k, idx_q_stride, scale, &out, lse ? lse_arr : nullptr, 1, ws, s,
+                       k2 > 0 ? &second : nullptr);
 }
 
 hipError_t launch_sparse_mla_fp8(const HostBatch& bt, const uint16_t* q, int H, const HostCache& latent,
