@@ -161,6 +161,33 @@ def test_hca_keeps_every_entry_without_indexer_inputs():
         assert np_(idx)[b, 0].tolist() == list(range(n_c)) + [-1] * (wl.k - n_c)
 
 
+def test_csa_caches_of_different_layouts():
+    """The attention runs over two index lists on two caches, each with its own layout: compressed
+    caches stored contiguously and the raw cache in pages of 16 under another permutation give the
+    bits of the all-paged (64) call, since the same rows are gathered."""
+    wl = synth.small("csa_pro_decode_b32_128k", B=2, L=9000, L_max=9024, planted=4, seq_lens=(9000, 5000), k=300)
+    g = synth.generate(wl, seed=5, device=DEV)
+    idx, out, lse = run_gpu(g, wl)
+
+    def contiguous(pool, table, rows):
+        x = pool[table.long()].reshape(wl.B, -1, pool.shape[-1])
+        return x[:, :rows].contiguous()
+
+    keys_c = contiguous(g.keys, g.key_table, wl.rows)
+    lat_c = contiguous(g.latent[0], g.latent_table[0], wl.rows)
+    raw = g.window_latent[g.window_table.long()].reshape(wl.B, -1, 576)          # logical order
+    n16 = raw.shape[1] // 16
+    perm = torch.randperm(wl.B * n16, generator=torch.Generator().manual_seed(6)).to(DEV)
+    pool16 = torch.empty((wl.B * n16, 16, 576), dtype=raw.dtype, device=DEV)
+    pool16[perm] = raw.reshape(wl.B * n16, 16, 576)
+    table16 = perm.to(torch.int32).view(wl.B, n16).contiguous()
+    idx2, out2, lse2 = dsa.csa_forward(g.q_idx, g.w, dsa.Cache(keys_c, None, 0), dsa.Cache(lat_c, None, 0),
+                                       dsa.Cache(pool16, table16, 16), wl.ratio, wl.k, wl.window, g.q_mla[0],
+                                       wl.scale, g.seq_lens, wl.lmax)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_csa_rejects_before_hip():
     wl = synth.small("csa_pro_decode_b32_128k", B=1, L=4096, planted=0)
     g = synth.generate(wl, seed=0, device=DEV)
