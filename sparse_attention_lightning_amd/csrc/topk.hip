@@ -18,8 +18,8 @@
 //            candidates it contains the exact top-k (all scores >= tau, and tau is at most the
 //            k-th largest); holding them in registers, the workgroup radix-selects the k-th
 //            largest key T, breaks ties at T toward lower positions with a second radix select
-//            on the complemented position, and emits the k kept positions in order through LDS
-//            bitmaps of windows of positions. Otherwise (a sample that missed, or a flood of
+//            on the complemented position, and emits the k kept positions in order by a bucket
+//            sort in LDS. Otherwise (a sample that missed, or a flood of
 //            equal scores) it falls back to an exact scan of the whole row: histogram passes
 //            for T, then an ordered block-scan compaction.
 // Rows with p + 1 <= k keep every visible token. Results are deterministic: the kept set is
@@ -178,18 +178,31 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TkLds& L,
   __syncthreads();
 }
 
-// The need-th largest 32-bit key among key(i), i < n, and how many keys equal to it must be
-// taken. The radix digits are taken from key - min over only the significant bits of the
-// observed range (up to 11 bits per level), so even tightly clustered keys spread over the
+// f(key) for the key of every score srow[i], i < n: 8 per thread and pass, their loads issued
+// together (clamped into the row, masked after).
+template <int NT, typename F>
+__device__ __forceinline__ void for_each_key(const float* __restrict__ srow, int n, F f) {
+  for (int base = 0; base < n; base += NT * 8) {
+    const int i0 = base + 4 * (int)threadIdx.x, i1 = i0 + 4 * NT;
+    const float4 a = load4_clamped<false>(srow, i0, n), b = load4_clamped<false>(srow, i1, n);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((e < 4 ? i0 : i1) + (e & 3) < n) f(float_key(v[e]));
+  }
+}
+
+// The need-th largest key among those of srow[0..n) (n >= 1), and how many keys equal to it
+// must be taken. The radix digits are taken from key - min over only the significant bits of
+// the observed range (up to 11 bits per level), so even tightly clustered keys spread over the
 // histogram instead of piling onto one or two LDS counters; equal keys need no level at all.
-template <int NT = kTkThreads, typename KeyFn>
-__device__ void select_key(TkLds& L, int n, int need, KeyFn key, uint32_t& T, int& rem) {
+template <int NT = kTkThreads>
+__device__ void select_key(TkLds& L, const float* __restrict__ srow, int n, int need, uint32_t& T, int& rem) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t u = key(i);
+  for_each_key<NT>(srow, n, [&](uint32_t u) {
     lo = min(lo, u);
     hi = max(hi, u);
-  }
+  });
   block_minmax<NT>(lo, hi, L, lo, hi);
   const uint32_t span = hi - lo;
   int bits = span ? 32 - __clz((int)span) : 0;
@@ -198,10 +211,10 @@ __device__ void select_key(TkLds& L, int n, int need, KeyFn key, uint32_t& T, in
   while (bits > 0) {                      // block-uniform
     const int w = min(11, bits), shift = bits - w;
     zero_hist<NT>(L, 2048);
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t off = key(i) - lo;
+    for_each_key<NT>(srow, n, [&](uint32_t u) {
+      const uint32_t off = u - lo;
       if ((uint32_t)((uint64_t)off >> bits) == prefix) atomicAdd(&L.hist[(off >> shift) & ((1u << w) - 1)], 1u);
-    }
+    });
     __syncthreads();
     uint32_t b;
     int r;
@@ -299,22 +312,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
 }
 
 // ------------------------------------------------------------------------------------------ finish
-// Exact top-k of a whole row by one workgroup (the fallback): three histogram passes over the
-// row for T and the tie quota, then an ordered block-scan compaction in position order.
+// Exact top-k of a whole row of n > k scores by one workgroup (the fallback): histogram passes
+// over the row for T and the tie quota, then an ordered block-scan compaction in position order
+// that stops once all k outputs are placed (the keys above T number k - the tie quota), so a
+// row of ties ends after its first block.
 template <int NT = kTkThreads>
 __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, int32_t* __restrict__ out, TkLds& L) {
-  auto key_at = [&](int i) { return float_key(srow[i]); };
   uint32_t T;
   int rem;
-  select_key<NT>(L, n, k, key_at, T, rem);
+  select_key<NT>(L, srow, n, k, T, rem);
+  const int n_gt = k - rem;
   int gt_carry = 0, eq_carry = 0;
   for (int base = 0; base < n; base += NT * 4) {
     const int i0 = base + 4 * (int)threadIdx.x;
+    const float4 x = load4_clamped<false>(srow, i0, n);
+    const float v[4] = {x.x, x.y, x.z, x.w};
     uint32_t fgt = 0, feq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (i0 + e < n) {
-        const uint32_t u = key_at(i0 + e);
+        const uint32_t u = float_key(v[e]);
         fgt |= (uint32_t)(u > T) << e;
         feq |= (uint32_t)(u == T) << e;
       }
@@ -334,6 +351,7 @@ __device__ void finish_full_scan(const float* __restrict__ srow, int n, int k, i
     }
     gt_carry += (int)(tot & 0xFFFF);
     eq_carry += (int)(tot >> 16);
+    if (gt_carry >= n_gt && eq_carry >= rem) break;    // block-uniform
   }
 }
 
@@ -540,13 +558,21 @@ __device__ uint32_t sample_tau(Blk<NT>& B, const float* __restrict__ srow, int n
 // Exact top-k of the candidates held in registers (PER per thread; every score of the row that
 // can be among the k largest is a candidate, cnt >= k of them) written to out[0..k) in
 // ascending position order: the k-th largest key T, the ties at T by the lowest positions, then
-// an ordered emission through an LDS bitmap of WORDS words (32 positions each) at a time. Each
-// window costs two barriers and a block scan, so the caller lends the largest LDS region free
-// by then; its first use comes after the select's last barrier.
+// the k kept positions in order by a bucket sort in LDS. Bucket = position >> shift, with shift
+// the least that puts every position of the row below kEmitBuckets: count, prefix-sum the counts
+// into bucket offsets, scatter each position into its bucket, and give each position its rank
+// inside its bucket by counting the smaller ones there. A bucket spans 2^shift positions (64 at
+// 128K, 512 at 1M), so the rank loops are short, and nothing walks the n positions of the row.
+// The caller lends an LDS region of WORDS words free by then (its first use comes after the
+// select's last barrier).
+constexpr int kEmitBuckets = 2048;
+
 template <int NT, int PER, int WORDS>
 __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&cp)[PER], const bool (&cok)[PER], int n,
-                            int k, int32_t* __restrict__ out, uint32_t* __restrict__ bitmap) {
-  static_assert(WORDS % NT == 0, "whole bitmap words per thread");
+                            int k, int32_t* __restrict__ out, uint32_t* __restrict__ lds) {
+  constexpr int BPT = kEmitBuckets / NT;               // buckets per thread in the prefix sum
+  static_assert(BPT >= 1 && kEmitBuckets % NT == 0, "whole buckets per thread");
+  static_assert(WORDS >= 2 * kEmitBuckets + kMaxK, "counts, offsets and the scattered positions");
   const int tid = B.tid;
   int rem;
   const uint32_t T = B.select(ck, cok, k, true, &rem);
@@ -569,51 +595,53 @@ __device__ void select_emit(Blk<NT>& B, const uint32_t (&ck)[PER], const int (&c
 #pragma unroll
   for (int e = 0; e < PER; ++e)
     keep[e] = cok[e] && (ck[e] > T || (ck[e] == T && (0xFFFFFFu - (uint32_t)cp[e]) >= pos_cut));
-  int emitted = 0;
-  constexpr int kWindow = WORDS * 32;
-  constexpr int WPT = WORDS / NT + 1;                  // bitmap words per thread, at most
-  for (int wbase = 0; wbase < n; wbase += kWindow) {
-    // the window's words that hold positions below n, dealt evenly: thread t owns wd consecutive
-    // words, so the emission order is the position order. wd is odd, so that the lanes' reads,
-    // wd words apart, fall in distinct LDS banks (an even stride folds them onto a few banks).
-    const int nw = min(WORDS, (n - wbase + 31) >> 5);
-    const int wd = ((nw + NT - 1) / NT) | 1;
+  uint32_t* cnt = lds;                                 // [kEmitBuckets] counts, then cursors
+  uint32_t* off = lds + kEmitBuckets;                  // [kEmitBuckets] first slot of each bucket
+  int* srt = (int*)(lds + 2 * kEmitBuckets);           // [k] positions, grouped by bucket
+  int shift = 0;
+  while (((n - 1) >> shift) >= kEmitBuckets) ++shift;  // block-uniform
 #pragma unroll
-    for (int r = 0; r < WPT; ++r)
-      if (tid + r * NT < nw) bitmap[tid + r * NT] = 0u;
-    __syncthreads();
+  for (int b = 0; b < BPT; ++b) cnt[tid * BPT + b] = 0u;
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int q = cp[e] - wbase;
-      if (keep[e] && q >= 0 && q < kWindow) atomicOr(&bitmap[q >> 5], 1u << (q & 31));
+  for (int e = 0; e < PER; ++e)
+    if (keep[e]) atomicAdd(&cnt[cp[e] >> shift], 1u);
+  __syncthreads();
+  uint32_t c[BPT], mine = 0;
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    c[b] = cnt[tid * BPT + b];
+    mine += c[b];
+  }
+  uint32_t total;
+  uint32_t at = B.scan(mine, &total);                  // the scan's barrier orders the reads above
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    off[tid * BPT + b] = at;
+    at += c[b];
+    cnt[tid * BPT + b] = 0u;
+  }
+  __syncthreads();
+  int slot[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    slot[e] = -1;
+    if (keep[e]) {
+      const int bk = cp[e] >> shift;
+      slot[e] = (int)(off[bk] + atomicAdd(&cnt[bk], 1u));
+      srt[slot[e]] = cp[e];
     }
-    __syncthreads();
-    // the thread's words into registers in one burst: every read is issued (clamped into the
-    // bitmap) and the words it does not own are masked, so the reads do not wait one by one
-    const int w0 = tid * wd;
-    uint32_t wv[WPT];
-    uint32_t pc = 0;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int r = 0; r < WPT; ++r) {
-      const uint32_t x = bitmap[min(w0 + r, WORDS - 1)];
-      wv[r] = (r < wd && w0 + r < nw) ? x : 0u;
-      pc += (uint32_t)__builtin_popcount(wv[r]);
+  for (int e = 0; e < PER; ++e) {
+    if (slot[e] >= 0) {
+      const int bk = cp[e] >> shift;
+      const int b0 = (int)off[bk], b1 = b0 + (int)cnt[bk];
+      int r = b0;
+      for (int i = b0; i < b1; ++i) r += srt[i] < cp[e];
+      if (r < k) out[r] = cp[e];
     }
-    uint32_t tot;
-    int slot = emitted + (int)B.scan(pc, &tot);
-#pragma unroll
-    for (int r = 0; r < WPT; ++r) {
-      uint32_t m = wv[r];
-      const int pos0 = wbase + 32 * (w0 + r);
-      while (m) {
-        const int bit = __builtin_ctz(m);
-        m &= m - 1;
-        if (slot < k) out[slot] = pos0 + bit;
-        ++slot;
-      }
-    }
-    emitted += (int)tot;
-    __syncthreads();
   }
 }
 
@@ -713,7 +741,7 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
     cp[e] = cok[e] ? R.pos[i] : 0;
   }
   // the candidate arrays (key, then pos: 2 kRCap words) are free once read into registers: the
-  // emission bitmap takes them, 256K positions per window
+  // emission's bucket sort takes them
   static_assert(offsetof(RowLds, pos) == offsetof(RowLds, key) + kRCap * sizeof(uint32_t), "key, then pos");
   select_emit<kRT, kRCPer, 2 * kRCap>(B, ck, cp, cok, n, k, out, R.key);
 }
@@ -772,7 +800,7 @@ __global__ __launch_bounds__(kST) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int L_max, int k, TkWs ws, int32_t* __restrict__ idx) {
   constexpr int PER = kTkCap / kST;
-  constexpr int kEmitWords = 24 * kST;                 // 96 KB: 768K positions per emission window
+  constexpr int kEmitWords = 2 * rowsel::kEmitBuckets + kMaxK;   // the emission's bucket sort
   __shared__ rowsel::SelLds<kST> S;
   __shared__ uint32_t emit_bits[kEmitWords];
   const int row = blockIdx.x;
