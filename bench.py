@@ -291,7 +291,8 @@ def main():
                            share_first_query=bool(wl.share_first_query), outs=outs, lses=lses, idx=idx_fs, ws=ws_fs,
                            stream=stream, latent_scales=[1.0] * wl.n_layers if wl.latent_fp8 else None)
 
-    kCsaRepeat = 8                         # calls per timed group interval in the breakdown
+    kRepeat = 8      # back-to-back calls per timed interval of the group and CSA breakdowns, so that
+                     # the queue never drains inside an interval and the first launch's start-up is shared
 
     def csa_call(pr, g):
         dsa.csa_forward(g.q_idx, g.w, pr["keys"], pr["lats"][0], pr["win"], wl.ratio, wl.k, wl.window, g.q_mla[0],
@@ -308,15 +309,15 @@ def main():
             if record == "all":
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
                 e[0].record(stream)
-                if scan_runs(wl):
+                for _ in range(kRepeat if scan_runs(wl) else 0):
                     dsa.index_score(g.q_idx, g.w, pr["keys"], g.seq_lens, wl.rows, q_pos=q_pos, scores=scores,
                                     stream=stream)
                 e[1].record(stream)
-                if scan_runs(wl):
+                for _ in range(kRepeat if scan_runs(wl) else 0):
                     dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
                 e[2].record(stream)
                 e[4].record(stream)
-                for _ in range(kCsaRepeat):        # back to back, so that the queue never drains
+                for _ in range(kRepeat):
                     csa_call(pr, g)
                 e[5].record(stream)
                 if scan_runs(wl):                  # HCA: no scan or top-k to time
@@ -332,13 +333,16 @@ def main():
                 # launches are the group call minus those two stages
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
                 e[0].record(stream)
-                dsa.index_score(pr["qi"], pr["wi"], pr["keys"], g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores,
-                                stream=stream)
+                for _ in range(kRepeat):
+                    dsa.index_score(pr["qi"], pr["wi"], pr["keys"], g.seq_lens, wl.lmax, q_pos=q_pos, scores=scores,
+                                    stream=stream)
                 e[1].record(stream)
-                dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
+                for _ in range(kRepeat):
+                    dsa.topk(scores, g.seq_lens, wl.k, q_pos=q_pos, idx=idx, ws=ws_topk, stream=stream)
                 e[2].record(stream)
                 e[3].record(stream)
-                group_call(pr, g)
+                for _ in range(kRepeat):
+                    group_call(pr, g)
                 e[4].record(stream)
                 ev["index"].append((e[0], e[1]))
                 ev["topk"].append((e[1], e[2]))
@@ -390,8 +394,11 @@ def main():
         step(args.warmup + args.steps + i, "all")
     torch.cuda.synchronize()
     avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in ev.items() if v}   # microseconds
+    if wl.ratio or group:
+        for key in ("index", "topk", "group"):
+            if key in avg:
+                avg[key] /= kRepeat
     if wl.ratio:
-        avg["group"] /= kCsaRepeat
         # the attention over the union of the two lists is what the one call spends beyond the stages
         avg.setdefault("index", 0.0)
         avg.setdefault("topk", 0.0)
@@ -438,13 +445,15 @@ def main():
                    "planted": wl.planted, "compression_ratio": wl.ratio, "window": wl.window},
         "roofline": roof,
         "kernels_us": {"index_score": avg["index"], "topk": avg["topk"], "sparse_mla": avg["mla"],
-                       "note": ("one dsa_csa_forward call per timed step; index_score and topk from separate "
-                                "calls in 3 steps after the timed region; sparse_mla (one launch over the selected "
-                                "compressed rows and the window rows): the call (8 back to back between two events) "
-                                "minus those two" if wl.ratio else
+                       "note": ("one dsa_csa_forward call per timed step; breakdown in 3 steps after the timed "
+                                "region, each stage timed over %d back-to-back calls between two events: "
+                                "index_score and topk as separate calls; sparse_mla (one launch over the selected "
+                                "compressed rows and the window rows): the whole call minus those two" % kRepeat
+                                if wl.ratio else
                                 "one dsa_forward_shared call per timed step (all layers' MLA launched together); "
-                                "index_score and topk: events around separate calls in 3 steps after the timed "
-                                "region; sparse_mla: the group call minus those two" if group else
+                                "breakdown in 3 steps after the timed region, each stage timed over %d back-to-back "
+                                "calls between two events: index_score and topk as separate calls; sparse_mla: the "
+                                "group call minus those two" % kRepeat if group else
                                 "index_score: HIP events around the scan in every fourth timed step; topk and sparse_mla: "
                                 "events around each stage in 3 steps after the timed region")},
         "step_hbm_GBps_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
