@@ -225,6 +225,27 @@ def test_topk_odd_row_length(form):
 
 
 @pytest.mark.parametrize("form", FORMS)
+def test_topk_emission_bucket_edges(form):
+    # The ordered emission buckets the kept positions by position >> shift, with shift the least
+    # that puts a row's positions below 2048 buckets. Visible lengths on both sides of each shift
+    # change; scores rising with position put the whole selection in the last buckets, filled to
+    # their width, and a random permutation spreads it.
+    rng = np.random.default_rng(11)
+    lens = [2048, 2049, 4096, 4097, 131072, 131073, 262144, 262145]
+    L = 262160
+    rising = np.tile(np.arange(L, dtype=np.float32), (len(lens), 1))
+    spread = np.stack([rng.permutation(L).astype(np.float32) for _ in lens])
+    middle = rng.normal(size=(len(lens), L)).astype(np.float32)
+    for b, n in enumerate(lens):                     # a run of high scores in the middle of the row
+        middle[b, max(0, n // 2 - 1500): n // 2 + 1500] += 100.0
+    for s in (rising, spread, middle):
+        s3 = s[:, None, :]
+        for k in (2048, 2047):
+            got = run_topk(s3, lens, k, form=form)
+            assert np.array_equal(got, oracle_topk(s3, lens, k)), k
+
+
+@pytest.mark.parametrize("form", FORMS)
 def test_topk_deterministic(form):
     rng = np.random.default_rng(9)
     s = rng.integers(0, 1000, size=(4, 1, 70000)).astype(np.float32)
@@ -362,6 +383,45 @@ def test_decode_tiny_end_to_end():
     ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), o_idx, wl.scale)
     check_mla(np_(out)[0, 0], np_(lse)[0, 0], ref_o[0, 0], ref_l[0, 0])
     print(f"decode_tiny_8k: {swaps} near-threshold swaps")
+
+
+def random_shape(seed):
+    """A seeded random small shape: cache layout, query count, head counts, k and ragged lengths."""
+    r = np.random.default_rng(1000 + seed)
+    ps = int(r.choice([0, 0, 16, 48, 64, 128]))
+    Q = int(r.choice([1, 2, 5, 8]))
+    B = int(r.integers(1, 5))
+    L_max = int(r.integers(64, 16000))
+    lens = tuple(int(x) for x in r.integers(Q, L_max + 1, B))
+    return synth.small("verify_b64_q8_32k", B=B, Q=Q, L=max(lens), L_max=L_max, page_size=ps, seq_lens=lens,
+                       Hi=int(r.choice([32, 64])), H=int(r.choice([64, 128])), k=int(r.choice([1, 777, 2048, 2048])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_end_to_end(seed):
+    """Scan, top-k and attention on a random small shape, each stage against the oracle: scores
+    within the tolerance, sets up to near-threshold swaps, attention over the GPU's own set."""
+    wl = random_shape(seed)
+    print(f"seed {seed}: B={wl.B} Q={wl.Q} L_max={wl.lmax} page={wl.page_size} Hi={wl.Hi} H={wl.H} k={wl.k} "
+          f"lens={wl.lens}", flush=True)
+    cpu, g = gpu_batch(wl, seed=seed)
+    scores = dsa.index_score(g.q_idx, g.w, keys_arg(g), g.seq_lens, wl.lmax)
+    idx = dsa.topk(scores, g.seq_lens, wl.k)
+    out, lse = dsa.sparse_mla_fwd(g.q_mla[0], lat_arg(g), idx, wl.k, wl.scale, g.seq_lens, wl.lmax)
+    o_idx, exact = oracle_idx(cpu, wl)
+    kc = key_cache(cpu)
+    sc, gi = np_(scores), np_(idx)
+    for b in range(wl.B):
+        for j, p in enumerate(positions(wl)[b]):
+            if j in (0, wl.Q - 1):                  # the tolerance costs host time per key: two queries
+                tol = score_tolerance(np_(cpu.q_idx[b, j]), np_(cpu.w[b, j]), kc.rows(b, np.arange(wl.lmax)))
+                check_scores(sc[b, j], exact[b, j], tol, p)
+            check_topk_sets(gi[b, j], o_idx[b, j], exact[b, j], wl.k)
+    ref_o, ref_l = oracle.sparse_mla_batch(bits(cpu.q_mla[0]), latent_cache(cpu), gi, wl.scale)
+    out, lse = np_(out), np_(lse)
+    for b in range(wl.B):
+        for j in range(wl.Q):
+            check_mla(out[b, j], lse[b, j], ref_o[b, j], ref_l[b, j])
 
 
 @pytest.mark.parametrize("share_first", [False, True])
