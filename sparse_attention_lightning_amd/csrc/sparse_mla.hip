@@ -670,14 +670,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 
 // Merge split partials: one workgroup per (query token, 4 heads), 64 threads x 8 dims per head
 // (two 16-byte loads per split and thread); every split's lse and partial are loaded before the
-// merge, so the loads overlap. The split count is a template argument: registers for exactly
-// that many partials, so that every workgroup of a launch fits on the chip at once.
+// merge, so the loads overlap. S > 0 fixes the split count at S: registers for exactly that many
+// partials, so that every workgroup of a decode-sized launch fits on the chip at once (at 4
+// splits: 55 VGPRs and 8 waves per SIMD, against 175 VGPRs for the general form). S = 0 takes
+// any count up to kMaxSplits from `splits_rt`; it serves 16 splits, where the fixed form's
+// compiler schedule consumed each partial before loading the next and measured slower.
 template <int S>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
-                                                          const float* __restrict__ part_lse_all, int H,
+                                                          const float* __restrict__ part_lse_all, int H, int splits_rt,
                                                           int64_t part_o_stride, int64_t part_lse_stride,
                                                           int64_t nrm_off) {
-  constexpr int splits = S;
+  constexpr int N = S > 0 ? S : kMaxSplits;
+  const int splits = S > 0 ? S : splits_rt;
   typedef part_t p8 __attribute__((ext_vector_type(8)));
   const int layer = blockIdx.y;
   const part_t* __restrict__ part_o = part_o_all + layer * part_o_stride;
@@ -687,28 +691,31 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
   const int hl = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int bq = blockIdx.x / (H / 4);
   const int h = (blockIdx.x - bq * (H / 4)) * 4 + hl;
-  float ls[S], nr[S];
-  p8 po[S];
+  float ls[N], nr[N];
+  p8 po[N];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < N; ++s) {
+    const bool in = S > 0 || s < splits;
     const int64_t ps = (int64_t)bq * splits + s;
-    ls[s] = part_lse[ps * H + h];
-    nr[s] = part_lse[nrm_off + ps * H + h];
-    po[s] = *(const p8*)(part_o + (ps * H + h) * kDv + 8 * t);
+    ls[s] = in ? part_lse[ps * H + h] : -INFINITY;
+    nr[s] = in ? part_lse[nrm_off + ps * H + h] : 0.f;
+    if (in) po[s] = *(const p8*)(part_o + (ps * H + h) * kDv + 8 * t);
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, ls[s]);
+  for (int s = 0; s < N; ++s) mx = fmaxf(mx, ls[s]);
   v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float den = 0.f;
   if (mx != -INFINITY) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const float wgt = expf(ls[s] - mx);
-      den += wgt;
-      const float c = wgt * nr[s];
+    for (int s = 0; s < N; ++s) {
+      if (S > 0 || s < splits) {
+        const float wgt = expf(ls[s] - mx);
+        den += wgt;
+        const float c = wgt * nr[s];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e >> 2][e & 3] += c * (float)po[s][e];
+        for (int e = 0; e < 8; ++e) acc[e >> 2][e & 3] += c * (float)po[s][e];
+      }
     }
     const float inv = 1.f / den;
     acc[0] *= inv;
@@ -807,13 +814,18 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
     if (splits > 1) {
       const dim3 cgrid((unsigned)rows * (H / 4), (unsigned)nl), cblock(256);
       const int64_t nrm = (int64_t)units * H;
-      static_assert(kMaxSplits == 16, "a combine instance per power-of-two split count");
-      switch (splits) {                                // a power of two (sparse_mla_splits doubles)
-        case 2: hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, s, L, part_o, part_lse, H, so, sl, nrm); break;
-        case 4: hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, s, L, part_o, part_lse, H, so, sl, nrm); break;
-        case 8: hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, s, L, part_o, part_lse, H, so, sl, nrm); break;
-        case 16: hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, cblock, 0, s, L, part_o, part_lse, H, so, sl, nrm); break;
-        default: return hipErrorInvalidValue;
+      switch (splits) {
+        case 2:
+          hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 2, so, sl, nrm);
+          break;
+        case 4:
+          hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 4, so, sl, nrm);
+          break;
+        case 8:
+          hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 8, so, sl, nrm);
+          break;
+        default:
+          hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, cblock, 0, s, L, part_o, part_lse, H, splits, so, sl, nrm);
       }
     }
     hipError_t e = hipGetLastError();
