@@ -63,7 +63,10 @@ typedef struct {
 
 /* A batch of B sequences with Q query tokens each. Query token j of sequence b sits at
  * position q_pos[b*Q + j], or at seq_lens[b] - Q + j when q_pos is NULL (the Q newest
- * cache entries). Causality is inclusive: the query at position p sees tokens 0..p. */
+ * cache entries). Causality is inclusive: the query at position p sees tokens 0..p.
+ * Limits (DSA_ERR_UNSUPPORTED beyond them): B*Q <= 2^24 and L_max <= 2^24; a call that
+ * writes or reads a score matrix (dsa_index_score, dsa_topk, dsa_forward_shared*,
+ * dsa_csa_forward) also needs B*Q*L_max <= 2^36, i.e. at most 256 GiB of fp32 scores. */
 typedef struct {
   int32_t B, Q, L_max;         /* (host) sizes; L_max is the row stride of scores and caches  */
   const int32_t* seq_lens;     /* device [B]                                                  */

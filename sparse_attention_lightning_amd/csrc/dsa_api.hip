@@ -54,6 +54,15 @@ dsa_status check_batch(const dsa_batch_t* bt, const char* who) {
   return DSA_OK;
 }
 
+// Calls with a score matrix [B*Q][L_max]: at most 2^36 entries, which also keeps every grid of
+// the scan and top-k kernels (one workgroup per 2048 or 4096 scores) within int range.
+dsa_status check_score_matrix(const dsa_batch_t* bt, const char* who) {
+  if ((int64_t)bt->B * bt->Q * bt->L_max > (int64_t(1) << 36))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*Q*L_max=%lld scores above 2^36", who,
+                (long long)bt->B * bt->Q * bt->L_max);
+  return DSA_OK;
+}
+
 dsa_status check_cache(const dsa_cache_t* c, int L_max, const char* who, const char* name) {
   if (!c) return fail(DSA_ERR_INVALID_ARG, "%s: %s cache is NULL", who, name);
   if (!c->base || !aligned(c->base, 16)) return fail(DSA_ERR_INVALID_ARG, "%s: %s base is NULL or not 16-byte aligned", who, name);
@@ -171,6 +180,7 @@ dsa_status dsa_index_score(const dsa_batch_t* batch, const uint8_t* q, const flo
                            const dsa_cache_t* keys, float* scores, void* stream) {
   const char* who = "dsa_index_score";
   TRY(check_batch(batch, who));
+  TRY(check_score_matrix(batch, who));
   if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
   TRY(check_ptr(q, 16, who, "q"));
   TRY(check_ptr(w, 4, who, "w"));
@@ -184,6 +194,7 @@ dsa_status dsa_topk(const dsa_batch_t* batch, const float* scores, int k, int32_
                     void* stream) {
   const char* who = "dsa_topk";
   TRY(check_batch(batch, who));
+  TRY(check_score_matrix(batch, who));
   if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
   TRY(check_ptr(scores, 4, who, "scores"));
   TRY(check_ptr(idx, 4, who, "idx"));
@@ -252,6 +263,7 @@ dsa_status check_forward_shared(const dsa_batch_t* batch, const uint8_t* q_e4m3,
                                 float softmax_scale, float* const* out, float* const* lse, int32_t* idx_out,
                                 const char* who) {
   TRY(check_batch(batch, who));
+  TRY(check_score_matrix(batch, who));
   if (Hi != 32 && Hi != 64) return fail(DSA_ERR_UNSUPPORTED, "%s: Hi=%d (supported: 32, 64)", who, Hi);
   if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
   if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, %d]", who, k, kMaxTopK);
@@ -383,6 +395,7 @@ dsa_status dsa_csa_forward(const dsa_batch_t* batch, const uint8_t* q_e4m3, cons
                            float* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   const char* who = "dsa_csa_forward";
   TRY(check_batch(batch, who));
+  TRY(check_score_matrix(batch, who));
   if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: H=%d (supported: 64, 128)", who, H);
   if (ratio < 1 || ratio > batch->L_max) return fail(DSA_ERR_INVALID_ARG, "%s: ratio=%d outside [1, L_max]", who, ratio);
   if (k < 0 || k > kMaxTopK) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [0, %d]", who, k, kMaxTopK);

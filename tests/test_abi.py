@@ -67,6 +67,9 @@ def call_index(bt, q=A, w=A, Hi=64, kc=None, scores=A):
     (dict(bt=batch(), kc=cache(table=A, max_pages=64, page=24)), UNSUPPORTED),
     (dict(bt=batch(), kc=cache(table=A, max_pages=64, page=0)), UNSUPPORTED),
     (dict(bt=batch(L=4096), kc=cache(table=A, max_pages=63, page=64)), INVALID),
+    (dict(bt=batch(B=(1 << 24) + 1, L=4096)), UNSUPPORTED),  # B*Q above 2^24
+    (dict(bt=batch(L=(1 << 24) + 16)), UNSUPPORTED),         # L_max above 2^24
+    (dict(bt=batch(B=1 << 13, L=1 << 24)), UNSUPPORTED),     # B*Q*L_max = 2^37 scores
 ])
 def test_index_score_rejects(case, expect):
     assert call_index(**case) == expect
@@ -85,6 +88,10 @@ def test_topk_rejects():
     assert lib.dsa_topk(C.byref(bt), A, 2048, A, A, need - 1, None) == WORKSPACE
     assert lib.dsa_topk(C.byref(bt), A + 1, 2048, A, A, need, None) == INVALID
     assert lib.dsa_topk(C.byref(bt), A, 2048, None, A, need, None) == INVALID
+    big = batch(B=1 << 12, L=1 << 24)                        # B*Q*L_max = 2^36 scores: accepted shape
+    assert lib.dsa_topk(C.byref(big), A, 2048, A, None, 0, None) == WORKSPACE
+    big = batch(B=(1 << 12) + 1, L=1 << 24)                  # one row more
+    assert lib.dsa_topk(C.byref(big), A, 2048, A, None, 0, None) == UNSUPPORTED
 
 
 def test_sparse_mla_rejects():
