@@ -6,7 +6,9 @@
 //   mark   one thread per selected position: the page's clock is set to this step; a page
 //          that is resident refreshes its slot's clock (so it cannot be evicted this step).
 //   plan   one 1024-thread workgroup per sequence: the missing pages in ascending page order
-//          (an ordered block compaction over the page clocks); the same number of victims,
+//          (with one index set per sequence in dsa_topk's order, an ordered compaction of the
+//          first position of each page run in the set; otherwise an ordered block compaction
+//          over the page clocks); the same number of victims,
 //          the least recently used of the slots this step does not use, ties to the lower
 //          slot (a 4-pass radix select of the threshold clock, then an ordered compaction
 //          with a quota for the slots at that clock), listed in ascending slot order; then
@@ -74,7 +76,9 @@ __global__ __launch_bounds__(256) void hs_mark_kernel(const int32_t* __restrict_
   if (phys >= 0 && s >= 0 && s < n_slots) slot_clock[(int64_t)b * n_slots + s] = step;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int32_t* __restrict__ block_table,
+__global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(const int32_t* __restrict__ idx, int n_sets, int k,
+                                                               int page_size, int32_t step,
+                                                               int32_t* __restrict__ block_table,
                                                                int32_t* __restrict__ slot_page,
                                                                int32_t* __restrict__ slot_clock,
                                                                const int32_t* __restrict__ page_clock, int max_pages,
@@ -91,11 +95,50 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
   int32_t* vs = victim + (int64_t)b * cap;
   int parity = 0;
 
-  // ---- missing pages (selected this step, not resident), ascending: kPlanPages consecutive
-  // pages per thread and pass. Loads are clamped into the sequence's pages (and masked) rather
-  // than branched, and the next pass's go out before this pass's scan, so that the passes do
-  // not wait for memory one after another.
+  // ---- missing pages (selected this step, not resident), ascending.
   uint32_t n_miss = 0;
+  bool listed = false;
+  // One index set whose valid positions ascend, -1 only after them (as dsa_topk writes it):
+  // pages ascend too and repeat only in runs, so the first position of each run names its page
+  // once, in order. Positions i and i + kPlanThreads per thread (k <= 2 kPlanThreads).
+  if (n_sets == 1) {
+    const int32_t* ip = idx + (int64_t)b * k;
+    int cur[2], prv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = tid + e * kPlanThreads;
+      cur[e] = i < k ? ip[i] : -1;
+      prv[e] = (i > 0 && i < k) ? ip[i - 1] : -1;
+    }
+    int bad = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (cur[e] >= 0 && tid + e * kPlanThreads > 0 && (prv[e] < 0 || prv[e] > cur[e])) bad = 1;
+    if (!__syncthreads_or(bad)) {                        // workgroup-uniform
+      int page[2], res[2];
+      bool cand[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        page[e] = cur[e] >= 0 ? cur[e] / page_size : -1;
+        const int pp = prv[e] >= 0 ? prv[e] / page_size : -1;
+        cand[e] = cur[e] >= 0 && page[e] < max_pages && page[e] != pp;
+        res[e] = bt[cand[e] ? page[e] : 0];              // both loads go out together
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {                      // positions [0, 1024), then [1024, 2048)
+        const uint32_t flag = cand[e] && res[e] < 0;
+        uint32_t tot;
+        const uint32_t at = n_miss + block_scan(L, parity, flag, &tot);
+        parity ^= 1;
+        if (flag && at < (uint32_t)cap) mp[at] = page[e];
+        n_miss += tot;
+      }
+      listed = true;
+    }
+  }
+  // Otherwise every page clock: kPlanPages consecutive pages per thread and pass. Loads are
+  // clamped into the sequence's pages (and masked) rather than branched, and the next pass's go
+  // out before this pass's scan, so that the passes do not wait for memory one after another.
   int pc_cur[kPlanPages], bt_cur[kPlanPages], pc_nxt[kPlanPages], bt_nxt[kPlanPages];
   auto load_pages = [&](int base, int (&c)[kPlanPages], int (&t)[kPlanPages]) {
 #pragma unroll
@@ -105,8 +148,8 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(int32_t step, int
       t[e] = bt[p];
     }
   };
-  load_pages(0, pc_cur, bt_cur);
-  for (int base = 0; base < max_pages; base += kPlanPages * kPlanThreads) {
+  if (!listed) load_pages(0, pc_cur, bt_cur);
+  for (int base = 0; !listed && base < max_pages; base += kPlanPages * kPlanThreads) {
     load_pages(base + kPlanPages * kPlanThreads, pc_nxt, bt_nxt);
     uint32_t flags = 0;
 #pragma unroll
@@ -279,7 +322,9 @@ hipError_t launch_hisparse_swap_in(int B, const int32_t* idx, int n_sets, int k,
   const int chunks = (k + 255) / 256;
   hipLaunchKernelGGL(hs::hs_mark_kernel, dim3((unsigned)(B * n_sets * chunks)), dim3(256), 0, s, idx, n_sets, k, chunks,
                      step, hb.block_table, hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, hb.page_size);
-  hipLaunchKernelGGL(hs::hs_plan_kernel, dim3(B), dim3(hs::kPlanThreads), 0, s, step, hb.block_table, hb.slot_page,
+  static_assert(2 * hs::kPlanThreads >= 2048, "the one-set miss list reads two positions per thread");
+  hipLaunchKernelGGL(hs::hs_plan_kernel, dim3(B), dim3(hs::kPlanThreads), 0, s, idx, n_sets, k, hb.page_size, step,
+                     hb.block_table, hb.slot_page,
                      hb.slot_clock, hb.page_clock, hb.max_pages, hb.n_slots, cap, miss_page, victim, n_copy, copied);
   hipLaunchKernelGGL(hs::hs_copy_kernel, dim3((unsigned)(B * cap)), dim3(hs::kCopyThreads), 0, s,
                      (const uint8_t*)host_pool, (uint8_t*)device_pool, cap, miss_page, victim, n_copy, hb.max_pages,
