@@ -190,6 +190,12 @@ __global__ __launch_bounds__(kPlanThreads) void hs_plan_kernel(const int32_t* __
   int need = (int)n_miss;
   if (tid == 0) L.res[0] = L.res[1] = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
+    // every eligible key is at most `step`: levels above its top bit are all zero (bin 0 holds
+    // every key, so the prefix gains a zero byte and `need` stays)
+    if (shift > 0 && (step >> shift) == 0) {             // workgroup-uniform
+      prefix <<= 8;
+      continue;
+    }
     for (int i = tid; i < 256; i += kPlanThreads) L.hist[i] = 0u;
     __syncthreads();
     for (int s0 = 0; s0 < n_slots; s0 += 4 * kPlanThreads) {

@@ -88,6 +88,26 @@ def test_swap_in_matches_oracle(B, n_sets, k, ps, max_pages, n_slots, steps, kee
         assert copied.cpu().tolist() == [sum(1 for c in copies if c[0] == b) for b in range(B)], step
 
 
+def test_step_clocks_across_every_radix_level():
+    """The victim select is a radix select over slot clocks + 1, 8 bits per level from the top;
+    levels above the step's top bit hold nothing and are skipped. Step numbers that grow through
+    every byte exercise each level, with slot clocks spread over them (ties broken by slot)."""
+    B, n_sets, k, ps, max_pages, n_slots = 2, 1, 40, 16, 64, 48
+    host, hb, st, dev_np = make(B, max_pages, n_slots, ps, seed=21)
+    host_np = host.numpy()
+    rng = np.random.default_rng(22)
+    L = max_pages * ps
+    prev = None
+    steps = [0, 1, 255, 256, 257, 65535, 65536, 70000, (1 << 24) - 1, 1 << 24, (1 << 24) + 3, (1 << 30) + 7]
+    for step in steps:
+        n_valid = rng.integers(k // 2, k + 1, size=B)
+        idx = random_sets(rng, B, n_sets, k, L, n_valid, prev, 0.5)
+        prev = idx
+        dsa.hisparse_swap_in(torch.from_numpy(idx).to(DEV), step, hb, host)
+        oracle.swap_in(st, idx, step, ps, host_np, dev_np)
+        compare(hb, st, dev_np, step)
+
+
 def test_repeated_positions_and_empty_sets():
     B, ps, max_pages, n_slots, k = 2, 16, 20, 32, 16
     host, hb, st, dev_np = make(B, max_pages, n_slots, ps, seed=5)
