@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     int splits,
     int split_len, float scale_log2, float out_scale, part_t* __restrict__ part_o_all,
     float* __restrict__ part_lse_all, int64_t part_o_stride, int64_t part_lse_stride, int64_t nrm_off, int n_hg,
-    int n_units) {
+    int n_units, bool tok_xcd) {
   // layer blockIdx.y of the launch: its query, latent cache, outputs and partials
   const int layer = blockIdx.y;
   const uint16_t* __restrict__ q = layers.q[layer];
@@ -208,18 +208,31 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  // unit = (query token, split); with n_hg head groups, the groups of one unit are 8 workgroups
-  // apart, which puts them on one XCD (workgroups are dealt to the 8 XCDs in turn), so that the
-  // second group's gathers of the same rows hit that XCD's L2
-  int unit = blockIdx.x, hg = 0;
-  if (n_hg > 1) {
-    const int grp = blockIdx.x / (8 * n_hg), r = blockIdx.x - grp * 8 * n_hg;
-    hg = r >> 3;
-    unit = grp * 8 + (r & 7);
+  // Workgroups are dealt to the 8 XCDs in turn, so workgroup ids 8 apart share an XCD and its
+  // L2. With at least 8 query tokens (tok_xcd), every workgroup of token bq (its splits x n_hg
+  // head groups) gets an id congruent to bq mod 8: the head groups of a split gather the same
+  // rows, and every split reads the token's query, from that one L2. With fewer tokens the
+  // splits spread over the XCDs and only the head groups of a split share one (ids 8 apart).
+  int bq, split, hg = 0;
+  if (tok_xcd) {
+    const int per_tok = splits * n_hg;
+    const int r8 = blockIdx.x >> 3;
+    bq = (r8 / per_tok) * 8 + (blockIdx.x & 7);
+    const int w_tok = r8 - (r8 / per_tok) * per_tok;
+    split = w_tok / n_hg;
+    hg = w_tok - split * n_hg;
+    if (bq * splits >= n_units) return;                // the grid is padded to whole groups of 8 tokens
+  } else {
+    int unit = blockIdx.x;
+    if (n_hg > 1) {
+      const int grp = blockIdx.x / (8 * n_hg), r = blockIdx.x - grp * 8 * n_hg;
+      hg = r >> 3;
+      unit = grp * 8 + (r & 7);
+    }
+    if (unit >= n_units) return;                       // the grid is padded to whole groups of 8
+    split = unit % splits;
+    bq = unit / splits;
   }
-  if (unit >= n_units) return;                         // the grid is padded to whole groups of 8
-  const int split = unit % splits;
-  const int bq = unit / splits;
   const int b = bq / Q, j = bq - b * Q;
   const int h0 = (hg * NW + wave) * 16 * HT;           // this wave's heads: tile ht = h0 + 16 ht ..
   constexpr int my_dma = kSegs;                        // loads this wave issues per step
@@ -677,7 +690,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 // compiler schedule consumed each partial before loading the next and measured slower.
 template <int S>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, const part_t* __restrict__ part_o_all,
-                                                          const float* __restrict__ part_lse_all, int H, int splits_rt,
+                                                          const float* __restrict__ part_lse_all, int H, int n_rows,
+                                                          int splits_rt,
                                                           int64_t part_o_stride, int64_t part_lse_stride,
                                                           int64_t nrm_off) {
   constexpr int N = S > 0 ? S : kMaxSplits;
@@ -689,8 +703,18 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaLayers layers, cons
   float* __restrict__ out = layers.out[layer];
   float* __restrict__ lse_out = layers.lse[layer];
   const int hl = threadIdx.x >> 6, t = threadIdx.x & 63;
-  const int bq = blockIdx.x / (H / 4);
-  const int h = (blockIdx.x - bq * (H / 4)) * 4 + hl;
+  // with at least 8 query tokens, the workgroups of token bq get ids congruent to bq mod 8, like
+  // the attention's that wrote its partials: one XCD
+  int bq, h;
+  if (n_rows >= 8) {
+    const int r8 = blockIdx.x >> 3, per_tok = H / 4;
+    bq = (r8 / per_tok) * 8 + (blockIdx.x & 7);
+    if (bq >= n_rows) return;                          // the grid is padded to whole groups of 8 tokens
+    h = (r8 - (r8 / per_tok) * per_tok) * 4 + hl;
+  } else {
+    bq = blockIdx.x / (H / 4);
+    h = (blockIdx.x - bq * (H / 4)) * 4 + hl;
+  }
   float ls[N], nr[N];
   p8 po[N];
 #pragma unroll
@@ -731,16 +755,16 @@ template <int NW, int HT, bool F8>
 static void launch_mla(int splits, dim3 grid, hipStream_t s, const MlaLayers& L, const int32_t* idx, int k,
                        int idx_q_stride, const MlaSecond& sec, int Q, int H, int split_len, float sl2,
                        float out_scale, part_t* part_o, float* part_lse, int64_t so, int64_t sl, int n_hg,
-                       int units) {
+                       int units, bool tok_xcd) {
   const dim3 block(NW * 64);
   const int64_t nrm_off = (int64_t)units * H;          // the factors follow the units' lse
   if (splits == 1)
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, false, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, sec, Q,
                        H, 1, split_len, sl2, out_scale, nullptr, nullptr, (int64_t)0, (int64_t)0, (int64_t)0, n_hg,
-                       units);
+                       units, tok_xcd);
   else
     hipLaunchKernelGGL((sparse_mla_kernel<NW, HT, true, F8>), grid, block, 0, s, L, idx, k, idx_q_stride, sec, Q,
-                       H, splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, nrm_off, n_hg, units);
+                       H, splits, split_len, sl2, out_scale, part_o, part_lse, so, sl, nrm_off, n_hg, units, tok_xcd);
 }
 
 // The second list of a union launch (one layer), with its own cache of L_max rows per sequence.
@@ -797,35 +821,38 @@ static hipError_t launch_layers(const HostBatch& bt, const uint16_t* const* q, i
     // 128 heads are dealt to two workgroups of 4 x 16 heads instead (same splits, same results).
     const int units = rows * splits;
     const int n_hg = (H == 128 && 2 * units * nl <= kTargetWgs) ? 2 : 1;
-    const dim3 grid(n_hg == 1 ? (unsigned)units : (unsigned)((units + 7) / 8 * 8 * n_hg), (unsigned)nl);
+    const bool tok_xcd = rows >= 8;
+    const dim3 grid(tok_xcd ? (unsigned)((rows + 7) / 8 * 8 * splits * n_hg)
+                            : (n_hg == 1 ? (unsigned)units : (unsigned)((units + 7) / 8 * 8 * n_hg)),
+                    (unsigned)nl);
     const float os = f8 ? latent_scale : 1.f;
     if (f8 && H == 128 && n_hg == 1)
       launch_mla<4, 2, true>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
-                             part_lse, so, sl, 1, units);
+                             part_lse, so, sl, 1, units, tok_xcd);
     else if (f8)
       launch_mla<4, 1, true>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
-                             part_lse, so, sl, n_hg, units);
+                             part_lse, so, sl, n_hg, units, tok_xcd);
     else if (H == 128 && n_hg == 1)
       launch_mla<4, 2, false>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
-                              part_lse, so, sl, 1, units);
+                              part_lse, so, sl, 1, units, tok_xcd);
     else
       launch_mla<4, 1, false>(splits, grid, s, L, idx, k, idx_q_stride, sec, bt.Q, H, split_len, sl2, os, part_o,
-                              part_lse, so, sl, n_hg, units);
+                              part_lse, so, sl, n_hg, units, tok_xcd);
     if (splits > 1) {
-      const dim3 cgrid((unsigned)rows * (H / 4), (unsigned)nl), cblock(256);
+      const dim3 cgrid((unsigned)(rows >= 8 ? (rows + 7) / 8 * 8 : rows) * (H / 4), (unsigned)nl), cblock(256);
       const int64_t nrm = (int64_t)units * H;
       switch (splits) {
         case 2:
-          hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 2, so, sl, nrm);
+          hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, cblock, 0, s, L, part_o, part_lse, H, rows, 2, so, sl, nrm);
           break;
         case 4:
-          hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 4, so, sl, nrm);
+          hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, cblock, 0, s, L, part_o, part_lse, H, rows, 4, so, sl, nrm);
           break;
         case 8:
-          hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, s, L, part_o, part_lse, H, 8, so, sl, nrm);
+          hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, cblock, 0, s, L, part_o, part_lse, H, rows, 8, so, sl, nrm);
           break;
         default:
-          hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, cblock, 0, s, L, part_o, part_lse, H, splits, so, sl, nrm);
+          hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, cblock, 0, s, L, part_o, part_lse, H, rows, splits, so, sl, nrm);
       }
     }
     hipError_t e = hipGetLastError();
