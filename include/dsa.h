@@ -260,7 +260,8 @@ dsa_status dsa_hisparse_swap_in(int32_t B, const int32_t* idx, int32_t n_sets, i
                                 const dsa_hot_buffer_t* hb, const void* host_pool, void* device_pool,
                                 int32_t* copied, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace sizes, from host fields of `batch` only (B, Q, L_max). */
+/* Workspace sizes, from host fields of `batch` only (B, Q, L_max); 0 for a shape outside the
+ * batch limits above (which every entry point rejects). */
 enum { DSA_OP_INDEX_SCORE = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD_SHARED = 3,
        DSA_OP_HISPARSE_SWAP_IN = 4 };
 size_t dsa_workspace_size(int op, const dsa_batch_t* batch, int Hi, int H, int k, int n_layers);

@@ -160,6 +160,7 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 size_t dsa_workspace_size(int op, const dsa_batch_t* bt, int Hi, int H, int k, int n_layers) {
   (void)Hi;
   if (!bt || bt->B < 1 || bt->Q < 1 || bt->L_max < 1 || k < 1) return 0;
+  if ((int64_t)bt->B * bt->Q > (1 << 24) || bt->L_max > (1 << 24)) return 0;   // shapes every entry point rejects
   const int rows = bt->B * bt->Q;
   switch (op) {
     case DSA_OP_INDEX_SCORE: return 0;
