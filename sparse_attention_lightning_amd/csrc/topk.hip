@@ -227,24 +227,6 @@ __device__ void select_key(TkLds& L, const float* __restrict__ srow, int n, int 
   rem = nd;
 }
 
-// The need-th largest 24-bit value v(i) among the i with use(i): two 12-bit levels.
-template <int NT = kTkThreads, typename ValFn, typename UseFn>
-__device__ uint32_t select_24(TkLds& L, int n, int need, ValFn v, UseFn use) {
-  uint32_t b1, b2;
-  int r1, r2;
-  zero_hist<NT>(L, 4096);
-  for (int i = threadIdx.x; i < n; i += NT)
-    if (use(i)) atomicAdd(&L.hist[v(i) >> 12], 1u);
-  __syncthreads();
-  find_bin<4096, NT>(L, need, b1, r1);
-  zero_hist<NT>(L, 4096);
-  for (int i = threadIdx.x; i < n; i += NT)
-    if (use(i) && (v(i) >> 12) == b1) atomicAdd(&L.hist[v(i) & 0xFFF], 1u);
-  __syncthreads();
-  find_bin<4096, NT>(L, r1, b2, r2);
-  return (b1 << 12) | b2;
-}
-
 // ------------------------------------------------------------------------------------------ gather
 // One workgroup per chunk of kGatherChunk scores. Its score loads go out first, all at once and
 // clamped into the row, so that their latency overlaps that of the row's length and tau. A
