@@ -246,6 +246,28 @@ def test_topk_emission_bucket_edges(form):
 
 
 @pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("L", [8192, 8191, 4100])
+def test_topk_short_rows(form, L):
+    # rows of at most 8192 scores (the tiny decode's length), where the row form's sample is
+    # short or skipped (rows up to 4096 keep every score as a candidate): aligned (L % 4 == 0)
+    # and unaligned rows, ties, -inf runs, all-equal rows and lengths on both sides of k
+    rng = np.random.default_rng(12 + L)
+    rows = [
+        rng.normal(size=L).astype(np.float32),
+        rng.integers(0, 40, L).astype(np.float32),
+        np.full(L, -2.5, np.float32),
+        np.concatenate([rng.normal(size=L // 2), np.full(L - L // 2, -np.inf)]).astype(np.float32),
+        (rng.integers(-3, 3, L) * 1e-30).astype(np.float32),
+        rng.normal(size=L).astype(np.float32),
+    ]
+    s = np.stack(rows)[:, None, :]
+    lens = [L, L - 1, L, L, 2049, 2048]
+    for k in (2048, 2047, 100, 1):
+        got = run_topk(s, lens, k, form=form)
+        assert np.array_equal(got, oracle_topk(s, lens, k)), k
+
+
+@pytest.mark.parametrize("form", FORMS)
 def test_topk_deterministic(form):
     rng = np.random.default_rng(9)
     s = rng.integers(0, 1000, size=(4, 1, 70000)).astype(np.float32)
