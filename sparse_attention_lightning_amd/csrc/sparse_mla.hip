@@ -361,8 +361,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
   };
   // this wave's 8 FP8 rows of step st, from staging buffer p into the bf16 tile of `slot`
   // (masked tokens become zero rows). E4M3 values are exact in bf16, and gfx950 converts two
-  // codes to two packed bf16 in one instruction (scale 1; checked on the box against the fp32
-  // route, whose upper half is the bf16 pattern, on every non-NaN code).
+  // codes to two packed bf16 in one instruction (scale 1: the same bits as the fp32 route,
+  // whose upper half is the bf16 pattern, on every non-NaN code).
   auto convert8 = [&](int st, auto p, auto slot) {
     const uint8_t* sb = stg_of(p) + wave * kWaveStage8;
     uint8_t* tile = ring_of(slot);

@@ -576,6 +576,27 @@ def test_sparse_mla_fp8_latent_equals_bf16_cache_of_its_values(H):
     assert torch.equal(o8, ob) and torch.equal(l8, lb)
 
 
+def test_sparse_mla_fp8_every_code():
+    """Latent rows that hold every E4M3FN code but the two NaNs: the FP8 path converts each
+    code on the device and gives the bits of the bf16 path over the decoded values."""
+    gen = torch.Generator().manual_seed(13)
+    B, L, k, H = 2, 2048, 2048, 128
+    codes = (torch.arange(B * L * 576, dtype=torch.int64) * 37 % 256).to(torch.uint8).view(B, L, 576)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    assert torch.unique(codes).numel() == 254
+    q = (torch.randn((B, 1, H, 576), generator=gen) * 0.05).to(torch.bfloat16)
+    idx = torch.arange(k, dtype=torch.int32).repeat(B, 1, 1)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    scale, ls = 1.0 / 576 ** 0.5, 2.0 ** -6
+    o8, l8 = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(codes.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L,
+                                latent_scale=ls)
+    vals = (codes.view(torch.float8_e4m3fn).to(torch.float32) * ls).to(torch.bfloat16)
+    ob, lb = dsa.sparse_mla_fwd(q.to(DEV), dsa.Cache(vals.to(DEV), None, 0), idx.to(DEV), k, scale, seq_lens, L)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o8).all()
+    assert torch.equal(o8, ob) and torch.equal(l8, lb)
+
+
 def e4m3_codes(x):
     """E4M3FN codes (uint8) of float values (torch's round-to-nearest-even cast)."""
     return x.to(torch.float8_e4m3fn).view(torch.uint8)
