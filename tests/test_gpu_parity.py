@@ -423,7 +423,22 @@ def random_shape(seed):
 def test_random_shapes_end_to_end(seed):
     """Scan, top-k and attention on a random small shape, each stage against the oracle: scores
     within the tolerance, sets up to near-threshold swaps, attention over the GPU's own set."""
-    wl = random_shape(seed)
+    check_end_to_end(random_shape(seed), seed)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("one token each", dict(B=3, Q=1, L=1, L_max=1, page_size=0, seq_lens=(1, 1, 1))),
+    ("one and seventeen tokens, pages of 16", dict(B=2, Q=1, L=17, L_max=17, page_size=16, seq_lens=(1, 17))),
+    ("two queries at positions 0 and 1", dict(B=2, Q=2, L=2, L_max=2, page_size=0, seq_lens=(2, 2))),
+    ("k = 1 over pages of 16", dict(B=2, Q=3, L=40, L_max=48, page_size=16, seq_lens=(40, 3), k=1)),
+])
+def test_degenerate_lengths_end_to_end(name, kw):
+    """Sequences of one or a few tokens, rows shorter than every tile, k = 1: the path still
+    matches the oracle (one visible token: its score, the set {0}, the output its value row)."""
+    check_end_to_end(synth.small("verify_b64_q8_32k", **kw), 0)
+
+
+def check_end_to_end(wl, seed):
     print(f"seed {seed}: B={wl.B} Q={wl.Q} L_max={wl.lmax} page={wl.page_size} Hi={wl.Hi} H={wl.H} k={wl.k} "
           f"lens={wl.lens}", flush=True)
     cpu, g = gpu_batch(wl, seed=seed)
