@@ -20,7 +20,9 @@
 
 namespace dsa {
 
-constexpr int kScoreChunk = 2048;              // keys per workgroup of the decode form
+constexpr int kScoreChunk = 2048;              // keys per workgroup of the decode form ...
+constexpr int kScoreChunkSmall = 256;          // ... and in a launch that would not fill the chip
+constexpr int kChipCUs = 256;                   // compute units of the part
 constexpr int kDecWaves = 4;                    // waves per workgroup
 
 // XCD-aware work index: consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
@@ -286,13 +288,13 @@ __device__ __forceinline__ void dec_wait() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int HI, int ROWS>
+template <int HI, int ROWS, int CHUNK>
 __global__ __launch_bounds__(kDecWaves * 64) void index_score_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, CacheView keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_pos,
     int Q, int in_Q, int n_chunks, int n_items, float* __restrict__ scores) {
   constexpr int MT = HI / 16;
-  constexpr int kWaveKeys = kScoreChunk / kDecWaves;
+  constexpr int kWaveKeys = CHUNK / kDecWaves;
   static_assert(kWaveKeys / 16 + 1 <= 64, "a wave's pages fit in one register across lanes");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kDecWaves][kDecStages][kDecTile * kDi];
   const int lane = threadIdx.x & 63;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void index_score_decode_kernel(
   const int bqi = b * in_Q + j;
   const int L_max = keys.L_max;
   const int p = __builtin_amdgcn_readfirstlane(min(query_pos(seq_lens, q_pos, in_Q, b, j), L_max - 1));
-  const int t_begin = chunk * kScoreChunk + wave * kWaveKeys;
+  const int t_begin = chunk * CHUNK + wave * kWaveKeys;
   const int t_end = min(t_begin + kWaveKeys, L_max);
   float* srow = scores + (int64_t)bq * L_max;
   if (t_begin >= t_end) return;
@@ -416,23 +418,34 @@ hipError_t launch_index_score(const HostBatch& bt, const uint8_t* q, const float
     else launch_multi_rows<32>(bt, q, w, kv, scores, s);
     return hipGetLastError();
   }
-  const int n_chunks = (bt.L_max + kScoreChunk - 1) / kScoreChunk;
-  const int n_items = bt.B * bt.Q * n_chunks;
-  const dim3 grid(n_items), block(kDecWaves * 64);
-  auto dec = [&](auto hi) {
+  // Each wave streams its keys one tile after another, so a launch with fewer workgroups than
+  // CUs (one short sequence) takes workgroups of 256 keys, one tile per wave: the scan is then
+  // one memory round trip per wave instead of eight.
+  const bool small = (int64_t)bt.B * bt.Q * ((bt.L_max + kScoreChunk - 1) / kScoreChunk) < kChipCUs;
+  auto dec = [&](auto hi, auto chunk_c) {
     constexpr int HI = decltype(hi)::value;
+    constexpr int CH = decltype(chunk_c)::value;
+    const int n_chunks = (bt.L_max + CH - 1) / CH;
+    const int n_items = bt.B * bt.Q * n_chunks;
+    const dim3 grid(n_items), block(kDecWaves * 64);
     if (kv.table != nullptr)
-      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsPaged>), grid, block, 0, s, q, w, kv, bt.seq_lens,
+      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsPaged, CH>), grid, block, 0, s, q, w, kv, bt.seq_lens,
                          bt.q_pos, bt.Q, bt.in_Q, n_chunks, n_items, scores);
     else if (bt.L_max % 8 == 0)
-      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsContiguous>), grid, block, 0, s, q, w, kv, bt.seq_lens,
-                         bt.q_pos, bt.Q, bt.in_Q, n_chunks, n_items, scores);
+      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsContiguous, CH>), grid, block, 0, s, q, w, kv,
+                         bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, n_chunks, n_items, scores);
     else
-      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsPerLane>), grid, block, 0, s, q, w, kv, bt.seq_lens,
-                         bt.q_pos, bt.Q, bt.in_Q, n_chunks, n_items, scores);
+      hipLaunchKernelGGL((index_score_decode_kernel<HI, kRowsPerLane, CH>), grid, block, 0, s, q, w, kv,
+                         bt.seq_lens, bt.q_pos, bt.Q, bt.in_Q, n_chunks, n_items, scores);
   };
-  if (Hi == 64) dec(std::integral_constant<int, 64>{});
-  else dec(std::integral_constant<int, 32>{});
+  using Big = std::integral_constant<int, kScoreChunk>;
+  using Small = std::integral_constant<int, kScoreChunkSmall>;
+  auto by_chunk = [&](auto hi) {
+    if (small) dec(hi, Small{});
+    else dec(hi, Big{});
+  };
+  if (Hi == 64) by_chunk(std::integral_constant<int, 64>{});
+  else by_chunk(std::integral_constant<int, 32>{});
   return hipGetLastError();
 }
 
