@@ -88,8 +88,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void index_score_multi_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  // work item = (b, chunk, query group), query group fastest: groups sharing keys run together
-  const int item = blockIdx.x;
+  // work item = (b, chunk, query group), query group fastest: groups sharing keys run together,
+  // and on one XCD (each XCD walks a contiguous range of items), so they share its L2
+  const int item = xcd_remap(blockIdx.x, (int)gridDim.x);
   const int qg = item % n_qgroups;
   const int rest = item / n_qgroups;
   const int chunk = rest % n_chunks;
