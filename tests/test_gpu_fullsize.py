@@ -55,6 +55,16 @@ def check_rows_wellformed(idx, wl, share_first=False):
             assert np.all(np.diff(row[:m]) > 0) and row[0] >= 0 and row[m - 1] <= p
 
 
+def check_topk_exact(scores, idx, wl, rows, share_first=False):
+    """The selection of each (b, j) in rows, bit for bit against the oracle's on the GPU's own fp32
+    scores (the top-k is exact given its scores; only the scores carry rounding)."""
+    s = scores.cpu().numpy()
+    got = idx.cpu().numpy()
+    for b, j in rows:
+        p = wl.lens[b] - wl.Q + j
+        assert np.array_equal(got[b, 0 if share_first else j], oracle.select_topk(s[b, 0 if share_first else j], p, wl.k)), (b, j)
+
+
 def oracle_check_query(g, wl, b, j, scores_gpu, idx_gpu, outs, lses, share_first=False, layers=None,
                        q_mla=None, latent_scale=None):
     """Oracle for one query token (b, j) of a full-size batch. q_mla: the MLA query of each entry
@@ -119,7 +129,8 @@ def test_decode_b32_128k_paged():
         assert set(g.planted_pos[b].tolist()) <= set(sets[b, 0].tolist())
     s2, i2, o2, l2 = run_path(g, wl)                        # bitwise reproducible
     assert torch.equal(scores, s2) and torch.equal(idx, i2) and torch.equal(outs[0], o2[0])
-    for b in (0, 17, 31):
+    check_topk_exact(scores, idx, wl, [(b, 0) for b in range(wl.B)])
+    for b in (0, 5, 9, 13, 17, 22, 27, 31):
         oracle_check_query(g, wl, b, 0, scores, idx, outs, lses)
 
 
@@ -132,7 +143,8 @@ def test_decode_b32_128k_paged_fp8kv():
     check_rows_wellformed(idx, wl)
     s2, i2, o2, l2 = run_path(g, wl, latent_scale=1.0)
     assert torch.equal(idx, i2) and torch.equal(outs[0], o2[0]) and torch.equal(lses[0], l2[0])
-    for b in (0, 31):
+    check_topk_exact(scores, idx, wl, [(b, 0) for b in range(wl.B)])
+    for b in (0, 11, 31):
         oracle_check_query(g, wl, b, 0, scores, idx, outs, lses, latent_scale=1.0)
 
 
@@ -154,7 +166,8 @@ def test_prefill_4096_at_128k():
     g = synth.generate(wl, seed=0, device=DEV)
     scores, idx, outs, lses = run_path(g, wl)
     check_rows_wellformed(idx, wl)
-    for j in (0, 1234, 4095):
+    check_topk_exact(scores, idx, wl, [(0, j) for j in range(0, wl.Q, 32)] + [(0, wl.Q - 1)])
+    for j in (0, 1234, 2047, 3001, 4095):
         oracle_check_query(g, wl, 0, j, scores, idx, outs, lses)
 
 
@@ -169,6 +182,7 @@ def test_indexshare_b8_1m_4layers():
     # the group selects what separate stage calls select; its four layers match the oracle
     scores = dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax)
     assert torch.equal(idx, dsa.topk(scores, g.seq_lens, wl.k))
+    check_topk_exact(scores, idx, wl, [(b, 0) for b in range(wl.B)])
     oracle_check_query(g, wl, 3, 0, scores, idx, [o for o, _ in res], [l for _, l in res])
 
 
@@ -228,6 +242,8 @@ def test_verify_b64_q8_32k(name):
     g = synth.generate(wl, seed=0, device=DEV)
     scores, idx, outs, lses = run_path(g, wl, share_first=share)
     check_rows_wellformed(idx, wl, share_first=share)
+    check_topk_exact(scores, idx, wl, [(b, j) for b in range(wl.B) for j in range(1 if share else wl.Q)],
+                     share_first=share)
     if share:
         oracle_check_query(g, wl, 5, 0, scores, idx, outs, lses, share_first=True)
     else:
