@@ -91,8 +91,14 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 // into the row instead of guarded by a branch: a branch around each load makes the compiler wait
 // at the join for every load before it, while clamped loads issue back to back. Entries at or
 // past lim hold some in-row value; the caller masks them.
-template <bool VEC>
+// NT: a nontemporal load (for passes that read each score once).
+template <bool VEC, bool NT = false>
 __device__ __forceinline__ float4 load4_clamped(const float* __restrict__ row, int i0, int lim) {
+  if (VEC && NT) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 v = __builtin_nontemporal_load((const f4*)(row + min(i0, (lim - 1) & ~3)));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
   if (VEC) return *(const float4*)(row + min(i0, (lim - 1) & ~3));
   float4 x;
   x.x = row[min(i0 + 0, lim - 1)];

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_gather_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float4 x[NV];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) x[v] = load4_clamped<VEC>(srow, lo + 4 * tid + 4 * kTkThreads * v, L_max);
+  for (int v = 0; v < NV; ++v) x[v] = load4_clamped<VEC, true>(srow, lo + 4 * tid + 4 * kTkThreads * v, L_max);
   const TkRowInfo ri = tk_row(seq_lens, q_pos, Q, in_Q, L_max, k, row);
   if (ri.m == ri.n) return;
   const int hi = min(lo + kGatherChunk, ri.n);
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(
   auto load = [&](float4 (&d)[kRUnroll], int base) {
 #pragma unroll
     for (int u = 0; u < kRUnroll; ++u) {
-      d[u] = load4_clamped<VEC>(srow, base + 4 * (tid + u * kRT), n);   // past n: masked below
+      d[u] = load4_clamped<VEC, true>(srow, base + 4 * (tid + u * kRT), n);   // past n: masked below
     }
   };
   load(cur, 0);
