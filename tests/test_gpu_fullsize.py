@@ -305,3 +305,29 @@ def test_hisparse_b8_1m_decode(name):
         pool = hb.device_pool.view(bits)
         for b, p, s in copies[:: max(1, len(copies) // 64)]:     # a sample of this step's copies
             assert np.array_equal(pool[b * wl.n_slots + s].cpu().numpy(), host_np[b, p]), (step, b, p)
+
+
+@pytest.mark.parametrize("B,Q,L,lens,page_size", [
+    (2, 1024, 200003, (200003, 150001), 0),       # contiguous rows, L_max % 8 != 0: each lane finds its row
+    (8, 512, 65536, (65536, 60001, 65000, 33333, 65536, 40000, 65536, 512), 64),   # paged
+])
+def test_multi_query_scan_in_long_chunks(B, Q, L, lens, page_size):
+    """Launches of the multi-query scan that hold 16 or more workgroups per CU at 8192 keys take
+    8192-key chunks: scores of sampled query tokens against the oracle (ragged lengths, chunk
+    edges inside a row), every score after the query -inf, and the selection of sampled rows bit
+    for bit against the oracle's on the GPU's scores."""
+    wl = synth.Workload("mq_long", B=B, Q=Q, L=L, L_max=L, seq_lens=lens, page_size=page_size, k=2048)
+    g = synth.generate(wl, seed=3, device=DEV, with_mla=False)
+    keys = dsa.Cache(g.keys, g.key_table, wl.page_size)
+    scores = dsa.index_score(g.q_idx, g.w, keys, g.seq_lens, wl.lmax)
+    idx = dsa.topk(scores, g.seq_lens, wl.k)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (0, Q // 2), (0, Q - 1), (1, 7), (B - 1, Q - 1)]
+    check_topk_exact(scores, idx, wl, rows + [(b, j) for b in range(B) for j in (0, Q - 1)])
+    for b, j in rows:
+        p = wl.lens[b] - wl.Q + j
+        kc = seq_cache(g.keys, g.key_table, b)
+        qi, wi = g.q_idx[b, j].cpu().numpy(), g.w[b, j].cpu().numpy()
+        exact = oracle.index_scores(qi, wi, kc, 0, p, wl.lmax)
+        tol = score_tolerance(qi, wi, kc.rows(0, np.arange(wl.lmax)))
+        check_scores(scores[b, j].cpu().numpy(), exact, tol, p)
